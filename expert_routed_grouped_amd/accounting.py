@@ -1,0 +1,101 @@
+"""Host-side accounting for one MoE layer call: FLOPs, bytes, padding, skew.
+
+These are the quantities the AI-infra book (ch. 9) uses to reason about the
+expert layer, written as functions so the benchmark can report them and the
+tests can pin them to the book's worked numbers:
+
+* expert size P_e = 3*h*I parameters (section 9.3.2: 3 x 4096 x 1536);
+* useful expert FLOPs F_e(m) = 2*m*P_e (section 9.3.2 equations);
+* expected number of distinct active experts E[U] = E*(1-(1-K/E)^M)
+  (section 9.3.3; the second "E" of the printed formula is the expert count);
+* rows a grouped GEMM executes when every expert is padded to a tile
+  (section 9.4.3, local counts [32,16,8,4,2,1,1,0]);
+* expert skew s = max_j m_j / (n*k/R) (section 9.4.2 equations);
+* rows on the card that holds a hot expert (section 9.4.1).
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Sequence
+
+import numpy as np
+
+
+def expert_params(H: int, I: int) -> int:
+    """Parameters of one SwiGLU expert: gate [I,H], up [I,H], down [H,I]."""
+    return 3 * H * I
+
+
+def expert_bytes(H: int, I: int, bytes_per_weight: float, with_channel_scales: bool = False) -> int:
+    """Weight bytes of one expert; fp8 experts add one fp32 scale per output channel (2I + H)."""
+    b = int(expert_params(H, I) * bytes_per_weight)
+    if with_channel_scales:
+        b += 4 * (2 * I + H)
+    return b
+
+
+def useful_flops(assignments: int, H: int, I: int) -> int:
+    """2 * m * P_e summed over assignments (no padding)."""
+    return 2 * assignments * expert_params(H, I)
+
+
+def router_flops(T: int, H: int, E: int) -> int:
+    return 2 * T * H * E
+
+
+def expected_active_experts(E: int, K: int, M: int) -> float:
+    """E[U] = E * (1 - (1 - K/E)^M) for M tokens each picking K of E experts uniformly."""
+    return E * (1.0 - (1.0 - K / E) ** M)
+
+
+def padded_rows(counts: Sequence[int], tile: int) -> int:
+    """Rows executed when each non-empty expert is padded up to a multiple of ``tile``."""
+    return int(sum(-(-int(c) // tile) * tile for c in counts if c > 0))
+
+
+def padded_rows_to_max(counts: Sequence[int]) -> int:
+    """Rows executed when every expert (empty ones included) is padded to the largest count."""
+    return int(len(counts) * max(int(c) for c in counts))
+
+
+def skew(counts: Sequence[int], n: int, k: int, groups: int) -> float:
+    """s_expert = max_j m_j / (n*k/R) for R groups (cards) with loads m_j."""
+    return max(counts) / (n * k / groups)
+
+
+def group_loads(expert_loads: Sequence[float], groups: int) -> np.ndarray:
+    """Loads of ``groups`` cards when experts are split into equal contiguous id ranges."""
+    a = np.asarray(expert_loads, dtype=np.float64)
+    return a.reshape(groups, -1).sum(axis=1)
+
+
+def hot_expert_card_rows(n: int, k: int, E: int, hot_rows: float, groups: int) -> float:
+    """Rows on the card holding one hot expert with ``hot_rows`` rows when the other
+    n*k - hot_rows rows spread evenly over the remaining E - 1 experts."""
+    rest = (n * k - hot_rows) / (E - 1)
+    per_card = E // groups
+    return hot_rows + (per_card - 1) * rest
+
+
+def layer_hbm_bytes(counts: Iterable[int], T: int, H: int, I: int, E: int, act_bytes: int,
+                    w_bytes_per_expert: int, router_w_bytes: int, y_bytes: int = 4) -> int:
+    """Algorithmic HBM bytes of one layer call: the weights of every active expert
+    once, the router weight, x read once, y written once (index arrays are ignored)."""
+    active = sum(1 for c in counts if c > 0)
+    return active * w_bytes_per_expert + router_w_bytes + T * H * act_bytes + T * H * y_bytes
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def gib(nbytes: float) -> float:
+    return nbytes / float(1 << 30)
+
+
+def mib(nbytes: float) -> float:
+    return nbytes / float(1 << 20)
+
+
+def isclose(a: float, b: float, rel: float) -> bool:
+    return math.isclose(a, b, rel_tol=rel)

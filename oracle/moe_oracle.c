@@ -1,0 +1,300 @@
+/*
+ * CPU oracle for the Mixture-of-Experts FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * definition that the GPU path is checked against.  Only the test suite, the
+ * package smoke check and the benchmark's CPU-baseline leg may load it; the
+ * GPU library never links, calls or includes anything from here, and this
+ * file includes nothing from the GPU library.
+ *
+ * What it computes (sources are the three pages the method is taken from):
+ *   - "AI-infra book, ch. 9", section 9.3.4 (Fig. 9-16): a router picks k
+ *     experts per token, rows are grouped by expert, every expert runs its
+ *     FFN on its rows, and the token's output is the routing-weighted sum of
+ *     its k expert outputs.
+ *   - "PagedAttention, speculative decoding, MoE and Blackwell", MoE bullet
+ *     list: a learned gating network sends each token to its top-K experts.
+ *   - "Hosting Qwen on Blackwell", section "MoE Dispatch - Combine": dispatch
+ *     groups the tokens of each expert into GEMM input buffers; combine is a
+ *     weighted accumulation; with replicated inputs (section "Expert
+ *     parallelism") a rank keeps only the tokens routed to its own experts.
+ *   - Book, section 9.3.2: the Qwen3-235B-A22B expert is three matrices of
+ *     4096 x 1536 (gate, up, down); the FFN form is SwiGLU.
+ *
+ * Readings where the pages are silent (each is data, not an optimisation):
+ *   R1 router logit = fp32 fused-multiply-add chain over h = 0..H-1 in
+ *      ascending order, starting at +0, then one fp32 add of the bias;
+ *   R2 top-k order = logit descending, ties (IEEE equality, so -0 == +0) to
+ *      the lower expert index;
+ *   R3 gates = softmax over the k selected logits (fp64), which equals a full
+ *      softmax renormalised over the selected experts;
+ *   R4 a rank that owns experts [e_begin, e_end) drops the other assignments
+ *      from its combine and does not renormalise the remaining gates;
+ *   R5 expert FFN: G = Wg x, U = Wu x, h = silu(G) * U, o = Wd h; for bf16
+ *      models h is rounded fp64 -> fp32 -> bf16 (RNE) before the down
+ *      projection (the precision the GPU feeds to it), for fp32 models only
+ *      fp64 -> fp32; fp8 weights are exact e4m3 values times a fp32 scale of
+ *      their output channel;
+ *   R6 output y[t] = sum over kept j of gate_j * o_j, accumulated in fp64 and
+ *      stored fp32;
+ *   R7 permuted rows are ordered by (expert ascending, token ascending).
+ *
+ * Everything else accumulates in fp64 over the exact stored input values.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ODT_F32 = 0, ODT_BF16 = 1, ODT_E4M3 = 2 };
+
+/* ---- storage decoding ---------------------------------------------------- */
+
+static float bf16_bits_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* OCP 8-bit E4M3 ("fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; no
+ * infinities; exponent 0 is subnormal (m/8 * 2^-6); 0x7F and 0xFF are NaN. */
+double oracle_e4m3_value(uint8_t code)
+{
+    int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* float -> bf16, round to nearest, ties to even (finite inputs). */
+uint16_t oracle_bf16_round(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+static double elem(const void *p, int dt, size_t i)
+{
+    switch (dt) {
+    case ODT_F32: return (double)((const float *)p)[i];
+    case ODT_BF16: return (double)bf16_bits_to_float(((const uint16_t *)p)[i]);
+    default: return oracle_e4m3_value(((const uint8_t *)p)[i]);
+    }
+}
+
+static float elem_f32(const void *p, int dt, size_t i)
+{
+    return dt == ODT_F32 ? ((const float *)p)[i] : bf16_bits_to_float(((const uint16_t *)p)[i]);
+}
+
+/* ---- routing ------------------------------------------------------------- */
+
+/* R1: logits[t,e] for all t, e (x [T,H], w [E,H], bias [E] or NULL). */
+void oracle_router_logits(const void *x, int x_dt, const void *w, int w_dt, const float *bias,
+                          int T, int H, int E, float *logits)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int t = 0; t < T; t++) {
+        for (int e = 0; e < E; e++) {
+            float acc = 0.0f;
+            for (int h = 0; h < H; h++)
+                acc = fmaf(elem_f32(x, x_dt, (size_t)t * H + h), elem_f32(w, w_dt, (size_t)e * H + h), acc);
+            if (bias)
+                acc = acc + bias[e];
+            logits[(size_t)t * E + e] = acc;
+        }
+    }
+}
+
+/* R2 + R3 for one token: pick k experts by (logit desc, index asc), then the
+ * gates.  ``taken`` is scratch of E bytes. */
+static void topk_one(const float *l, int E, int k, int32_t *ids, float *gates, unsigned char *taken)
+{
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; j++) {
+        int best = -1;
+        for (int e = 0; e < E; e++) {
+            if (taken[e])
+                continue;
+            /* strictly greater wins; equal logits keep the lower index found first */
+            if (best < 0 || l[e] > l[best])
+                best = e;
+        }
+        taken[best] = 1;
+        ids[j] = best;
+    }
+    double m = (double)l[ids[0]], sum = 0.0, u[64];
+    for (int j = 0; j < k; j++) {
+        u[j] = exp((double)l[ids[j]] - m);
+        sum += u[j];
+    }
+    for (int j = 0; j < k; j++)
+        gates[j] = (float)(u[j] / sum);
+}
+
+/* Top-k and gates from given logits [T,E]; k <= 64. */
+int oracle_topk(const float *logits, int T, int E, int k, int32_t *topk_ids, float *topk_w)
+{
+    if (k < 1 || k > 64 || k > E)
+        return -1;
+#pragma omp parallel
+    {
+        unsigned char *taken = (unsigned char *)malloc((size_t)E);
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; t++)
+            topk_one(logits + (size_t)t * E, E, k, topk_ids + (size_t)t * k, topk_w + (size_t)t * k, taken);
+        free(taken);
+    }
+    return 0;
+}
+
+/* Router + top-k + gates.  ``logits`` [T,E] is an output (may not be NULL). */
+int oracle_route(const void *x, int x_dt, const void *w, int w_dt, const float *bias,
+                 int T, int H, int E, int k, int32_t *topk_ids, float *topk_w, float *logits)
+{
+    oracle_router_logits(x, x_dt, w, w_dt, bias, T, H, E, logits);
+    return oracle_topk(logits, T, E, k, topk_ids, topk_w);
+}
+
+/* ---- dispatch (permutation) ---------------------------------------------- */
+
+/* R7: stable counting sort of the local assignments by expert.
+ * counts [e_end-e_begin], offsets [e_end-e_begin+1], row_token/row_w [R],
+ * token_row [T,k] (-1 for assignments to non-local experts).  Returns R. */
+int oracle_permute(const int32_t *topk_ids, const float *topk_w, int T, int k, int e_begin, int e_end,
+                   int32_t *counts, int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row)
+{
+    int El = e_end - e_begin;
+    for (int i = 0; i < El; i++)
+        counts[i] = 0;
+    for (size_t a = 0; a < (size_t)T * k; a++) {
+        int e = topk_ids[a];
+        if (e >= e_begin && e < e_end)
+            counts[e - e_begin]++;
+    }
+    offsets[0] = 0;
+    for (int i = 0; i < El; i++)
+        offsets[i + 1] = offsets[i] + counts[i];
+    int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)(El > 0 ? El : 1));
+    for (int i = 0; i < El; i++)
+        cursor[i] = offsets[i];
+    for (int t = 0; t < T; t++) {
+        for (int j = 0; j < k; j++) {
+            size_t a = (size_t)t * k + j;
+            int e = topk_ids[a];
+            if (e >= e_begin && e < e_end) {
+                int r = cursor[e - e_begin]++;
+                row_token[r] = t;
+                row_w[r] = topk_w[a];
+                token_row[a] = r;
+            } else {
+                token_row[a] = -1;
+            }
+        }
+    }
+    free(cursor);
+    return offsets[El];
+}
+
+/* ---- expert FFN and combine ---------------------------------------------- */
+
+/* R5 + R6, token-major: y for the listed tokens only (y_out [n_tok, H]).
+ * w_gate_up [E_loc, 2I, H] (rows 0..I-1 gate, I..2I-1 up), w_down [E_loc, H, I];
+ * s_gate_up [E_loc, 2I], s_down [E_loc, H] are per-output-channel scales used
+ * only when w_dt is e4m3.  round_h: 1 = h goes fp64 -> fp32 -> bf16, 0 = fp64 -> fp32. */
+void oracle_layer_tokens(const int32_t *tokens, int n_tok, const void *x, int x_dt,
+                         const int32_t *topk_ids, const float *topk_w, int T, int H, int k,
+                         int e_begin, int e_end, int I, const void *w_gate_up, const void *w_down, int w_dt,
+                         const float *s_gate_up, const float *s_down, int round_h, float *y_out)
+{
+    (void)T;
+#pragma omp parallel
+    {
+        double *yacc = (double *)malloc(sizeof(double) * (size_t)H);
+        double *xt = (double *)malloc(sizeof(double) * (size_t)H);
+        double *hb = (double *)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 1)
+        for (int q = 0; q < n_tok; q++) {
+            int t = tokens[q];
+            for (int n = 0; n < H; n++) {
+                yacc[n] = 0.0;
+                xt[n] = elem(x, x_dt, (size_t)t * H + n);
+            }
+            for (int j = 0; j < k; j++) {
+                int e = topk_ids[(size_t)t * k + j];
+                if (e < e_begin || e >= e_end)
+                    continue; /* R4 */
+                size_t le = (size_t)(e - e_begin);
+                double g = (double)topk_w[(size_t)t * k + j];
+                for (int i = 0; i < I; i++) {
+                    double G = 0.0, U = 0.0;
+                    size_t rg = (le * 2 * I + i) * (size_t)H, ru = (le * 2 * I + I + i) * (size_t)H;
+                    for (int h = 0; h < H; h++) {
+                        G += xt[h] * elem(w_gate_up, w_dt, rg + h);
+                        U += xt[h] * elem(w_gate_up, w_dt, ru + h);
+                    }
+                    if (w_dt == ODT_E4M3) {
+                        G *= (double)s_gate_up[le * 2 * I + i];
+                        U *= (double)s_gate_up[le * 2 * I + I + i];
+                    }
+                    double hv = G / (1.0 + exp(-G)) * U;
+                    float hf = (float)hv;
+                    hb[i] = round_h ? (double)bf16_bits_to_float(oracle_bf16_round(hf)) : (double)hf;
+                }
+                for (int n = 0; n < H; n++) {
+                    double o = 0.0;
+                    size_t rd = (le * H + n) * (size_t)I;
+                    for (int i = 0; i < I; i++)
+                        o += hb[i] * elem(w_down, w_dt, rd + i);
+                    if (w_dt == ODT_E4M3)
+                        o *= (double)s_down[le * H + n];
+                    yacc[n] += g * o;
+                }
+            }
+            for (int n = 0; n < H; n++)
+                y_out[(size_t)q * H + n] = (float)yacc[n];
+        }
+        free(yacc);
+        free(xt);
+        free(hb);
+    }
+}
+
+/* Combine of unweighted per-row expert outputs y_perm [R, H]:
+ * y[t] = sum_{j : token_row[t,j] >= 0} topk_w[t,j] * y_perm[token_row[t,j]] (fp64, stored fp32). */
+void oracle_combine(const float *y_perm, const int32_t *token_row, const float *topk_w, int T, int k, int H, float *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; t++) {
+        for (int n = 0; n < H; n++) {
+            double acc = 0.0;
+            for (int j = 0; j < k; j++) {
+                int r = token_row[(size_t)t * k + j];
+                if (r >= 0)
+                    acc += (double)topk_w[(size_t)t * k + j] * (double)y_perm[(size_t)r * H + n];
+            }
+            y[(size_t)t * H + n] = (float)acc;
+        }
+    }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,428 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix,
+never against the oracle's own formulas retyped.
+
+Each test names the mistake it is there to catch.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from expert_routed_grouped_amd import synth
+from expert_routed_grouped_amd.synth import LayerConfig, bf16_bits_to_f32, f32_to_bf16_bits
+
+# the mutant check (test_oracle_mutants.py) points this module at a planted-mistake build
+if os.environ.get("MOE_ORACLE_LIBRARY"):
+    O.use_library(os.environ["MOE_ORACLE_LIBRARY"])
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")))
+
+
+def torch_bf16_bits(a):
+    """bf16 bits by torch's own float32 -> bfloat16 conversion (RNE), a library routine."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def e4m3_values_torch(codes):
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+# ----------------------------------------------------------------------------
+# storage decoding
+# ----------------------------------------------------------------------------
+def test_e4m3_decode_all_codes_match_torch_and_closed_forms():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = np.array([O.e4m3_value(c) for c in codes])
+    ref = e4m3_values_torch(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert set(np.nonzero(nan)[0]) == {0x7F, 0xFF}
+    # OCP E4M3 closed forms: largest finite, smallest subnormal, smallest normal, one
+    assert O.e4m3_value(0x7E) == 448.0 and O.e4m3_value(0xFE) == -448.0
+    assert O.e4m3_value(0x01) == 2.0 ** -9
+    assert O.e4m3_value(0x08) == 2.0 ** -6
+    assert O.e4m3_value(0x38) == 1.0
+
+
+def test_bf16_round_matches_torch_including_ties():
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal(2000).astype(np.float32) * np.float32(3.0)
+    # exact ties: bf16 value + half an ulp, with even and odd kept mantissas
+    base = f32_to_bf16_bits(rng.standard_normal(200).astype(np.float32))
+    ties = ((base.astype(np.uint32) << 16) | np.uint32(0x8000)).view(np.float32)
+    vals = np.concatenate([v, ties, np.float32([0.0, -0.0, 1.0, 65504.0, 1e-30, -3.3e38])])
+    assert np.array_equal(O.bf16_round(vals), torch_bf16_bits(vals))
+
+
+def test_generator_bf16_and_e4m3_encoders_agree_with_torch():
+    """The generator's storage rounding (data preparation) matches torch's casts."""
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal(5000).astype(np.float32)
+    assert np.array_equal(f32_to_bf16_bits(v), torch_bf16_bits(v))
+    w = rng.standard_normal((16, 64)).astype(np.float32)
+    codes, scale = synth.quantize_e4m3_per_row(w)
+    q = w.astype(np.float64) / scale[:, None].astype(np.float64)
+    ref = torch.from_numpy(q.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # torch rounds from the fp32 value; they agree except where fp64->fp32 lands on a tie
+    assert (codes == ref).mean() > 0.999
+    assert np.all(np.abs(e4m3_values_torch(codes)) <= 448)
+
+
+# ----------------------------------------------------------------------------
+# router logits
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_router_logits_exact_on_integer_inputs(dt):
+    """Small-integer inputs make every product and partial sum exact, so the logits
+    must equal the integer matrix product x @ Wr^T (+ bias) exactly: catches a
+    transposed operand, a wrong stride or a dropped term."""
+    rng = np.random.default_rng(11)
+    T, H, E = 9, 40, 7
+    xi = rng.integers(-8, 9, size=(T, H))
+    wi = rng.integers(-8, 9, size=(E, H))
+    bi = rng.integers(-50, 51, size=E)
+    store = (lambda a: a.astype(np.float32)) if dt == "f32" else (lambda a: f32_to_bf16_bits(a.astype(np.float32)))
+    lg = O.router_logits(store(xi), store(wi), bi.astype(np.float32))
+    assert np.array_equal(lg, (xi @ wi.T + bi).astype(np.float32))
+
+
+def test_router_is_ascending_fp32_chain():
+    """Order pin: [2^24, 1, -2^24] summed left to right in fp32 gives 0 (2^24 + 1
+    rounds back to 2^24); any other order of the same terms gives 1."""
+    x = np.array([[2.0 ** 24, 1.0, -(2.0 ** 24), 0.0]], dtype=np.float32)
+    w = np.ones((1, 4), dtype=np.float32)
+    assert O.router_logits(x, w)[0, 0] == 0.0
+    x2 = x[:, [2, 1, 0, 3]].copy()
+    assert O.router_logits(x2, w)[0, 0] == 1.0
+
+
+def test_router_uses_fused_multiply_add():
+    """(1+2^-12)^2 - 1 is 2^-11 + 2^-24 when fused, 2^-11 when the product is rounded first."""
+    a = np.float32(1.0 + 2.0 ** -12)
+    x = np.array([[-1.0, a]], dtype=np.float32)
+    w = np.array([[1.0, a]], dtype=np.float32)
+    assert O.router_logits(x, w)[0, 0] == np.float32(2.0 ** -11 + 2.0 ** -24)
+
+
+def test_router_bias_added_once_after_the_chain():
+    x = np.array([[1.0, 2.0 ** -24]], dtype=np.float32)
+    w = np.ones((1, 2), dtype=np.float32)
+    # chain: 1, then 1 + 2^-24 -> 1 (tie to even); + bias 2^-24 -> 1 again
+    assert O.router_logits(x, w, np.float32([2.0 ** -24]))[0, 0] == 1.0
+
+
+def test_router_within_recursive_summation_bound():
+    """|fl(sum) - sum| <= gamma_H * sum|x w| with gamma_n = n u / (1 - n u), u = 2^-24."""
+    cfg = LayerConfig("t", T=32, H=4096, E=16, k=4, I=64, seed=99)
+    x = synth.gen_x(cfg)
+    w = synth.gen_router(cfg)
+    lg = O.router_logits(x, w).astype(np.float64)
+    xf = bf16_bits_to_f32(x).astype(np.float64)
+    wf = bf16_bits_to_f32(w).astype(np.float64)
+    exact = xf @ wf.T
+    u = 2.0 ** -24
+    gamma = cfg.H * u / (1 - cfg.H * u)
+    bound = gamma * (np.abs(xf) @ np.abs(wf).T)
+    assert np.all(np.abs(lg - exact) <= bound)
+    assert np.abs(lg - exact).max() > 0  # really fp32
+
+
+# ----------------------------------------------------------------------------
+# top-k and gates
+# ----------------------------------------------------------------------------
+def brute_topk(lg, k):
+    T, E = lg.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        keyed = sorted(range(E), key=lambda e: (-float(lg[t, e]), e))
+        ids[t] = keyed[:k]
+    return ids
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (16, 8), (13, 13), (5, 1)])
+def test_topk_matches_brute_force_sort(E, k):
+    rng = np.random.default_rng(E * 31 + k)
+    lg = rng.standard_normal((40, E)).astype(np.float32)
+    lg[::3] = rng.integers(-2, 3, size=lg[::3].shape).astype(np.float32)  # many exact ties
+    ids, _ = O.topk(lg, k)
+    assert np.array_equal(ids, brute_topk(lg, k))
+
+
+def test_topk_signed_zero_tie_goes_to_lower_index():
+    lg = np.array([[-1.0, 0.0, -0.0, -2.0], [-1.0, -0.0, 0.0, -2.0]], dtype=np.float32)
+    ids, w = O.topk(lg, 2)
+    assert ids.tolist() == [[1, 2], [1, 2]]
+    assert np.all(w == np.float32(0.5))
+
+
+def test_zero_router_picks_first_k_with_equal_gates():
+    cfg = LayerConfig("t", T=5, H=64, E=16, k=8, I=64, seed=1)
+    x = synth.gen_x(cfg)
+    ids, w, lg = O.route(x, np.zeros((16, 64), dtype=np.uint16), None, 8)
+    assert np.all(lg == 0)
+    assert np.all(ids == np.arange(8))
+    assert np.all(w == np.float32(0.125))
+
+
+def test_duplicate_router_rows_tie_to_lower_index():
+    cfg = LayerConfig("t", T=20, H=64, E=6, k=3, I=64, seed=2)
+    x = synth.gen_x(cfg)
+    w = synth.gen_router(cfg)
+    w[4] = w[1]  # experts 1 and 4 always tie
+    ids, _, lg = O.route(x, w, None, 3)
+    assert np.array_equal(lg[:, 1], lg[:, 4])
+    for t in range(cfg.T):
+        row = list(ids[t])
+        if 4 in row:
+            assert 1 in row and row.index(1) < row.index(4)
+
+
+def test_k_equals_E_is_full_descending_order_and_full_softmax():
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal((10, 7)).astype(np.float32)
+    ids, w = O.topk(lg, 7)
+    assert np.array_equal(ids, np.argsort(-lg, axis=1, kind="stable"))
+    l64 = lg.astype(np.float64)
+    sm = np.exp(l64 - l64.max(1, keepdims=True))
+    sm /= sm.sum(1, keepdims=True)
+    assert np.allclose(np.take_along_axis(sm, ids, 1), w, rtol=1e-6, atol=0)
+
+
+def test_gates_equal_renormalised_full_softmax():
+    """Gates = full softmax over E renormalised over the selected experts (fp64 reference)."""
+    rng = np.random.default_rng(6)
+    lg = (rng.standard_normal((64, 128)) * 3).astype(np.float32)
+    ids, w = O.topk(lg, 8)
+    l64 = lg.astype(np.float64)
+    p = np.exp(l64 - l64.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    sel = np.take_along_axis(p, ids, 1)
+    ref = sel / sel.sum(1, keepdims=True)
+    assert np.max(np.abs(ref - w)) <= 1e-7
+    assert np.max(np.abs(w.astype(np.float64).sum(1) - 1)) <= 1e-6
+    ids1, w1 = O.topk(lg, 1)
+    assert np.all(w1 == 1.0)
+    assert np.array_equal(ids1[:, 0], np.argmax(lg, axis=1))
+
+
+# ----------------------------------------------------------------------------
+# permutation and counts
+# ----------------------------------------------------------------------------
+def random_routing(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    return ids, w
+
+
+@pytest.mark.parametrize("T,E,k,lo,hi", [(50, 8, 2, 0, 8), (300, 32, 8, 0, 32), (300, 32, 8, 8, 16), (7, 4, 4, 0, 4),
+                                         (40, 16, 3, 15, 16), (40, 16, 3, 3, 3)])
+def test_permutation_is_the_stable_sort_by_expert(T, E, k, lo, hi):
+    ids, w = random_routing(T, E, k, T + E + k + lo)
+    p = O.permute(ids, w, lo, hi)
+    flat = ids.ravel()
+    local = np.nonzero((flat >= lo) & (flat < hi))[0]
+    order = local[np.argsort(flat[local], kind="stable")]  # textbook stable sort
+    assert p["R"] == len(local)
+    assert np.array_equal(p["row_token"], order // k)
+    assert np.array_equal(p["row_w"], w.ravel()[order])
+    tr = np.full(T * k, -1, dtype=np.int64)
+    tr[order] = np.arange(len(order))
+    assert np.array_equal(p["token_row"].ravel(), tr)
+    cnt = np.bincount(flat[local] - lo, minlength=hi - lo) if hi > lo else np.zeros(0, dtype=np.int64)
+    assert np.array_equal(p["counts"], cnt)
+    assert np.array_equal(p["offsets"], np.concatenate([[0], np.cumsum(cnt)]))
+
+
+def test_counts_sum_and_mean_load_page_example():
+    """Counts sum to T*k and the mean load is T*k/E = 6000*8/128 = 375."""
+    g = GOLD["prefill_rows_per_expert"]
+    ids, w = random_routing(g["T"], g["E"], g["k"], 1)
+    p = O.permute(ids, w, 0, g["E"])
+    assert p["counts"].sum() == g["T"] * g["k"]
+    assert p["counts"].mean() == g["value"]
+    # every token got k distinct experts
+    assert all(len(set(r)) == g["k"] for r in ids.tolist())
+
+
+# ----------------------------------------------------------------------------
+# expert FFN and combine
+# ----------------------------------------------------------------------------
+def decode_w(w, wdt):
+    if wdt == "f32":
+        return w.astype(np.float64)
+    if wdt == "bf16":
+        return bf16_bits_to_f32(w).astype(np.float64)
+    return e4m3_values_torch(w)
+
+
+def dense_reference(inp, ids, gates, round_h):
+    """Independent dense formulation: every expert runs on every token (numpy
+    matmuls), then y = sum_e mask[t,e] * gate[t,e] * FFN_e(x_t)."""
+    cfg = inp["cfg"]
+    x = decode_w(inp["x"], cfg.act) if cfg.act == "bf16" else inp["x"].astype(np.float64)
+    T = cfg.T
+    y = np.zeros((T, cfg.H))
+    for e in range(cfg.lo, cfg.hi):
+        j = e - cfg.lo
+        wgu = decode_w(inp["w_gate_up"][j], cfg.wdt)
+        wd = decode_w(inp["w_down"][j], cfg.wdt)
+        if cfg.wdt == "fp8":
+            wgu = wgu * inp["s_gate_up"][j][:, None].astype(np.float64)
+            wd = wd * inp["s_down"][j][:, None].astype(np.float64)
+        gu = x @ wgu.T
+        h = (silu(gu[:, :cfg.I]) * gu[:, cfg.I:]).astype(np.float32)
+        if round_h:
+            h = bf16_bits_to_f32(torch_bf16_bits(h))
+        o = h.astype(np.float64) @ wd.T
+        g = np.where(ids == e, gates, 0).sum(1).astype(np.float64)
+        y += g[:, None] * o
+    return y
+
+
+SMALL = [
+    LayerConfig("s1", T=24, H=64, E=6, k=2, I=32, act="f32", wdt="f32", init="fan_in", seed=21),
+    LayerConfig("s2", T=20, H=64, E=8, k=3, I=32, act="bf16", wdt="bf16", seed=22, x_std=1.0, w_std=0.1),
+    LayerConfig("s3", T=20, H=64, E=8, k=4, I=32, act="bf16", wdt="fp8", e_begin=2, e_end=6, seed=23, w_std=0.1),
+    LayerConfig("s4", T=16, H=64, E=5, k=5, I=32, act="bf16", wdt="bf16", bias="zipf", seed=24, w_std=0.1),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_layer_matches_dense_formulation(cfg):
+    inp = synth.make_inputs(cfg)
+    r = O.layer(inp)
+    ref = dense_reference(inp, r["topk_ids"], r["topk_w"], round_h=cfg.act != "f32")
+    rms = np.sqrt((ref ** 2).mean())
+    assert rms > 0
+    # fp64 accumulation on both sides; the only differences are fp32 storage of y
+    # and rare h values whose fp32 rounding tips a bf16 tie the other way
+    err = np.abs(r["y"] - ref)
+    assert np.max(err) <= 1e-5 * np.max(np.abs(ref)) + 1e-3 * rms
+
+
+def test_single_expert_top1_is_a_dense_swiglu_ffn():
+    cfg = LayerConfig("d", T=12, H=64, E=1, k=1, I=48, act="f32", wdt="f32", init="fan_in", seed=31)
+    inp = synth.make_inputs(cfg)
+    r = O.layer(inp)
+    assert np.all(r["topk_ids"] == 0) and np.all(r["topk_w"] == 1.0)
+    x = inp["x"].astype(np.float64)
+    gu = x @ inp["w_gate_up"][0].astype(np.float64).T
+    h = (silu(gu[:, :48]) * gu[:, 48:]).astype(np.float32).astype(np.float64)
+    y = h @ inp["w_down"][0].astype(np.float64).T
+    assert np.allclose(r["y"], y, rtol=1e-6, atol=1e-7 * np.abs(y).max())
+
+
+def test_token_permutation_equivariance_bit_exact():
+    cfg = SMALL[1]
+    inp = synth.make_inputs(cfg)
+    r = O.layer(inp)
+    perm = np.random.default_rng(0).permutation(cfg.T)
+    inp2 = dict(inp, x=inp["x"][perm].copy())
+    r2 = O.layer(inp2)
+    assert np.array_equal(r2["topk_ids"], r["topk_ids"][perm])
+    assert np.array_equal(r2["y"], r["y"][perm])
+
+
+def test_linear_in_down_weights():
+    cfg = SMALL[1]
+    inp = synth.make_inputs(cfg)
+    r = O.layer(inp)
+    wd2 = f32_to_bf16_bits(bf16_bits_to_f32(inp["w_down"]) * np.float32(2.0))
+    r2 = O.layer(dict(inp, w_down=wd2))
+    assert np.array_equal(r2["y"], r["y"] * np.float32(2.0))
+
+
+def test_expert_parallel_shares_sum_to_full_layer():
+    """Ranks owning disjoint expert ranges produce partial outputs whose sum is the
+    full output (what the EP all-reduce completes); non-local gates are not
+    renormalised."""
+    cfg = LayerConfig("ep", T=30, H=64, E=8, k=4, I=32, act="bf16", wdt="bf16", seed=41, w_std=0.1)
+    inp = synth.make_inputs(cfg)
+    full = O.layer(inp)["y"].astype(np.float64)
+    parts = 0
+    for lo in range(0, 8, 2):
+        c = cfg.replace(e_begin=lo, e_end=lo + 2)
+        sub = dict(inp, cfg=c, w_gate_up=inp["w_gate_up"][lo:lo + 2], w_down=inp["w_down"][lo:lo + 2])
+        parts = parts + O.layer(sub)["y"].astype(np.float64)
+    assert np.max(np.abs(parts - full)) <= 4e-7 * np.abs(full).max()
+
+
+def test_token_with_no_local_expert_outputs_zero():
+    cfg = LayerConfig("z", T=40, H=64, E=8, k=2, I=32, act="bf16", wdt="bf16", e_begin=0, e_end=2, seed=43)
+    inp = synth.make_inputs(cfg)
+    r = O.layer(inp)
+    none_local = ~np.any(r["topk_ids"] < 2, axis=1)
+    assert none_local.any()
+    assert np.all(r["y"][none_local] == 0)
+    assert np.all(r["token_row"][r["topk_ids"] >= 2] == -1)
+
+
+def test_combine_is_gate_weighted_gather_sum():
+    rng = np.random.default_rng(9)
+    ids, w = random_routing(30, 8, 3, 9)
+    p = O.permute(ids, w, 2, 7)
+    yp = rng.standard_normal((p["R"], 16)).astype(np.float32)
+    y = O.combine(yp, p["token_row"], w)
+    ref = np.zeros((30, 16))
+    for t in range(30):
+        for j in range(3):
+            r = p["token_row"][t, j]
+            if r >= 0:
+                ref[t] += float(w[t, j]) * yp[r].astype(np.float64)
+    assert np.allclose(y, ref, rtol=1e-6, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------
+# page numbers
+# ----------------------------------------------------------------------------
+def test_accounting_matches_page_numbers():
+    from expert_routed_grouped_amd import accounting as A
+    g = GOLD["expert_params"]
+    assert A.expert_params(g["H"], g["I"]) == g["value"]
+    assert A.mib(A.expert_bytes(g["H"], g["I"], 2)) == g["bf16_mib"]
+    assert A.gib(128 * A.expert_bytes(4096, 1536, 2)) == GOLD["layer_bytes_bf16"]["gib"]
+    d = GOLD["decode_batch"]
+    assert d["T"] * d["k"] == d["assignments"] and d["assignments"] // 128 == d["uniform_rows"]
+    assert round(A.useful_flops(d["assignments"], 4096, 1536) / 1e9, 1) == d["gflop"]
+    assert A.mib(8 * A.expert_bytes(4096, 1536, 2)) == d["weights_mib_concentrated"]
+    u = GOLD["expected_active_experts"]
+    eu = A.expected_active_experts(u["E"], u["K"], u["M"])
+    assert round(eu) == u["value"]
+    assert round(A.gib(eu * A.expert_bytes(4096, 1536, 2)), 2) == u["weights_gib"]
+    m = GOLD["rows_per_expert_mean"]
+    assert m["n"] * m["k"] / m["E"] == m["value"]
+    h = GOLD["hot_expert_card_rows"]
+    got = [round(A.hot_expert_card_rows(h["n"], h["k"], h["E"], h["hot_rows"], g_)) for g_ in h["groups"]]
+    assert got == h["values"]
+    s = GOLD["skew"]
+    assert A.skew(s["loads"], s["n"], s["k"], s["R"]) == s["value"]
+    assert GOLD["flops_per_assignment"]["value"] == A.useful_flops(1, 4096, 1536)
+    p = GOLD["grouped_gemm_padding"]
+    assert sum(p["counts"]) == p["useful"]
+    assert A.padded_rows(p["counts"], 32) == p["pad_to_32"]
+    assert A.padded_rows_to_max(p["counts"]) == p["pad_to_max"]
+    assert [A.padded_rows(p["counts"], 32) / 64, A.padded_rows_to_max(p["counts"]) / 64] == p["ratios"]
+
+
+def test_decode_routing_touches_about_E_U_experts():
+    """The synthetic decode workload routes near-uniformly: the number of distinct
+    experts its 64 tokens use is close to E[U] = 126 (section 9.3.3)."""
+    cfg = synth.CONFIGS["decode"]
+    inp = synth.make_inputs(cfg, with_weights=False)
+    ids, _, _ = O.route(inp["x"], inp["w_router"], None, cfg.k)
+    U = len(np.unique(ids))
+    assert 120 <= U <= 128
+    p = O.permute(ids, np.ones_like(ids, dtype=np.float32), 0, cfg.E)
+    assert p["counts"].sum() == 512
