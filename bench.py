@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Benchmark of one MoE FFN layer step on one MI355X.
+
+A step is the whole hot path on one batch already resident in HBM:
+moe_route -> moe_permute -> moe_grouped_ffn (gate/up half, down half with the
+combine) [-> moe_combine for large batches].  Default workload: the decode
+layer (T=64 tokens, top-8 of 128 experts, H=4096, I=1536, bf16), which is
+weight-load bound; ``--config prefill`` times the 6000-token prefill layer
+(matrix-core bound).
+
+Prints ONE JSON line.  ``roofline`` covers the dominant kernel (the gate/up
+grouped GEMM): its algorithmic bytes (decode) or FLOPs (prefill) per launch
+over its average duration, measured with HIP events on the stream the library
+launches on.  ``cpu_baseline`` is the CPU oracle timed on this host on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec + % bf16 MFMA peak (prefill) / % HBM BW (decode)"
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
+WORKLOADS = {
+    "decode": "decode MoE layer: T=64 tokens x top-8 of E=128 experts (512 assignments), H=4096, SwiGLU I=1536, bf16",
+    "prefill": "prefill MoE layer: T=6000 tokens x top-8 of E=128 experts, H=4096, SwiGLU I=1536, bf16",
+    "skew": "skewed prefill MoE layer: T=6000, top-8 of 128, logit bias 2*ln Zipf(1.2), H=4096, I=1536, bf16",
+    "ep_share": "EP=4 share: T=8192 routed over 128 experts, local experts 0-31, fp8 e4m3 weights, H=4096, I=1536",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-sample", type=int, default=16, help="tokens of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, cfg, n_tok):
+    """The oracle as it stands, on the first n_tok tokens: route, permute, token-major FFN + combine."""
+    from oracle import oracle as O
+    n = min(n_tok, cfg.T)
+    x = np.ascontiguousarray(inp["x"][:n])
+    t0 = time.perf_counter()
+    ids, w, _ = O.route(x, inp["w_router"], inp["bias"], cfg.k)
+    O.permute(ids, w, cfg.lo, cfg.hi)
+    O.layer_tokens(np.arange(n), x, ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"], inp["s_gate_up"],
+                   inp["s_down"], round_h=cfg.act != "f32")
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens of the same workload, whole layer (route, permute, "
+                      f"token-major SwiGLU FFN + combine), {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "see DESIGN.md for how the layer would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from expert_routed_grouped_amd import accounting as A
+    from expert_routed_grouped_amd import layer as L
+    from expert_routed_grouped_amd import moe, synth
+
+    cfg = synth.CONFIGS[args.config]
+    print(f"[bench] generating {args.config} inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(cfg)
+    dev = L.to_device(inp)
+    bufs = L.LayerBuffers(cfg)
+    stream = torch.cuda.current_stream()
+    p = bufs.perm
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=stream)
+        moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=p, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        common = dict(workspace=bufs.workspace, gather=True, stream=stream)
+        outs = dict(y=bufs.y, zero_y=True) if bufs.fused else dict(y_perm=bufs.y_perm, zero_y=False)
+        moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap, dev["w_gate_up"],
+                            dev["w_down"], dev["s_gate_up"], dev["s_down"], phase="gate_up", **outs, **common)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap, dev["w_gate_up"],
+                            dev["w_down"], dev["s_gate_up"], dev["s_down"], phase="down", **outs, **common)
+        if not bufs.fused:
+            moe.moe_combine(bufs.y_perm, p["token_row"], bufs.topk_w, y=bufs.y, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    layer_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    route_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    gu_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    down_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    counts = p["counts"].cpu().numpy().astype(np.int64)
+    R = int(counts.sum())
+    U = int((counts > 0).sum())
+    H, I, T = cfg.H, cfg.I, cfg.T
+    wbytes = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.wdt]
+    abytes = 4 if cfg.act == "f32" else 2
+    scale_gu = 4 * 2 * I if cfg.wdt == "fp8" else 0
+    # gate/up half, algorithmic: each active expert's gate/up weights once, x read once, h written once
+    gu_bytes = U * (2 * I * H * wbytes + scale_gu) + T * H * abytes + R * I * abytes
+    gu_flops = 4 * R * H * I
+    layer_flops = A.useful_flops(R, H, I) + A.router_flops(T, H, cfg.E)
+    layer_bytes = A.layer_hbm_bytes(counts, T, H, I, cfg.E, abytes,
+                                    A.expert_bytes(H, I, wbytes, cfg.wdt == "fp8"), cfg.E * H * abytes)
+    gu_s = float(np.mean(gu_ms)) * 1e-3
+    if args.config == "decode":
+        achieved = gu_bytes / gu_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        achieved = gu_flops / gu_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof.update({"kernel": "ffn_tile_kernel<gate_up> (+ its schedule kernel)", "avg_ms": round(float(np.mean(gu_ms)), 4),
+                 "algorithmic_per_launch": gu_bytes if args.config == "decode" else gu_flops})
+    layer_s = ms_per_step * 1e-3
+    res = {
+        "metric": METRIC,
+        "value": round(T / layer_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.wdt == "bf16" else ("fp8-weights/bf16" if cfg.wdt == "fp8" else "f32"),
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "T": T, "H": H, "E": cfg.E, "k": cfg.k, "I": I,
+                   "local_experts": [cfg.lo, cfg.hi], "parallelism": "none (one GPU)",
+                   "combine": "fused atomic epilogue" if bufs.fused else "per-row outputs + moe_combine"},
+        "roofline": roof,
+        "layer": {"ms_p50": round(float(np.median(layer_ms)), 4), "ms_p10": round(float(np.percentile(layer_ms, 10)), 4),
+                  "ms_p90": round(float(np.percentile(layer_ms, 90)), 4),
+                  "route_permute_ms": round(float(np.mean(route_ms)), 4), "gate_up_ms": round(float(np.mean(gu_ms)), 4),
+                  "down_combine_ms": round(float(np.mean(down_ms)), 4),
+                  "hbm_bytes": int(layer_bytes), "hbm_frac": round(layer_bytes / layer_s / 1e9 / PEAK_HBM_GBS, 4),
+                  "flops": int(layer_flops), "mfma_frac": round(layer_flops / layer_s / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "routing": {"assignments": R, "active_experts": U, "max_rows": int(counts.max()),
+                    "padded_rows_bm128": A.padded_rows(counts, 128),
+                    "skew": round(float(counts.max() / (R / max(len(counts), 1))), 3) if R else None},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_sample)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

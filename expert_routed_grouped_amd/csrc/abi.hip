@@ -1,0 +1,140 @@
+// C ABI of the MoE layer library: argument checks on the host, then launches.
+// Every check runs before anything is enqueued, so an error return means the
+// stream is untouched.  No call allocates, frees or synchronises.
+#include "../../include/moe.h"
+#include "common.h"
+
+#define MOE_VERSION_NUMBER 100  // 0.1.0
+
+namespace {
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return MOE_VERSION_NUMBER; }
+
+const char *moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of the supported range";
+    case MOE_ERR_DTYPE: return "unsupported element type or type combination";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "a kernel launch failed";
+    case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const void *x, int x_dtype, const void *w_router, int w_dtype, const float *bias, int T, int H, int E,
+              int k, int32_t *topk_ids, float *topk_w, void *stream) {
+  if (T < 0 || H < 1 || E < 1 || E > 512 || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
+  if ((long long)T * k >= (1LL << 31) || (long long)T * H >= (1LL << 40)) return MOE_ERR_SHAPE;
+  if ((x_dtype != MOE_F32 && x_dtype != MOE_BF16) || (w_dtype != MOE_F32 && w_dtype != MOE_BF16)) return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_NULL;
+  return hip_status(launch_route(x, x_dtype == MOE_BF16, w_router, w_dtype == MOE_BF16, bias, T, H, E, k, topk_ids,
+                                 topk_w, (hipStream_t)stream));
+}
+
+int moe_permute(const int32_t *topk_ids, const float *topk_w, int T, int k, int E, int e_begin, int e_end,
+                int32_t *counts, int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
+                const void *x, int x_dtype, int H, void *x_perm, void *stream) {
+  if (T < 0 || E < 1 || E > 512 || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
+  if (e_begin < 0 || e_end <= e_begin || e_end > E) return MOE_ERR_SHAPE;
+  if ((long long)T * k >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_ids || !topk_w || !row_token || !row_w || !token_row)) return MOE_ERR_NULL;
+  const bool gather = x != nullptr || x_perm != nullptr;
+  if (gather) {
+    if (!x || !x_perm) return MOE_ERR_NULL;
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_ALIGN;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const int El = e_end - e_begin;
+  hipError_t err = launch_permute(topk_ids, topk_w, T, k, e_begin, El, counts, offsets, row_token, row_w, token_row, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  if (gather && T > 0) {
+    const int R_cap = T * (k < El ? k : El);
+    err = launch_gather_rows(x, x_dtype == MOE_BF16 ? 2 : 4, H, offsets, El, row_token, R_cap, x_perm, s);
+  }
+  return hip_status(err);
+}
+
+size_t moe_ffn_workspace_size(int R_cap, int E_loc, int H, int I, int a_dtype) {
+  (void)H;
+  if (R_cap < 0 || E_loc < 1 || I < 1) return 0;
+  const size_t esz = a_dtype == MOE_F32 ? 4 : 2;
+  return ffn_sched_bytes(E_loc) + align_up((size_t)R_cap * (size_t)I * esz, 256);
+}
+
+int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const int32_t *row_token, const float *row_w,
+                    int E_loc, int T, int R_cap, int H, int I, const void *w_gate_up, const void *w_down, int w_dtype,
+                    const float *s_gate_up, const float *s_down, float *y, float *y_perm, void *workspace,
+                    size_t workspace_bytes, unsigned flags, void *stream) {
+  if (T < 0 || R_cap < 0 || E_loc < 1 || E_loc > 512 || H < 64 || I < 64 || H % 64 != 0 || I % 64 != 0)
+    return MOE_ERR_SHAPE;
+  if ((long long)R_cap > (long long)T * E_loc || (long long)R_cap * (H > I ? H : I) >= (1LL << 40)) return MOE_ERR_SHAPE;
+  const bool bf16_path = a_dtype == MOE_BF16 && (w_dtype == MOE_BF16 || w_dtype == MOE_FP8_E4M3);
+  const bool f32_path = a_dtype == MOE_F32 && w_dtype == MOE_F32;
+  if (!bf16_path && !f32_path) return MOE_ERR_DTYPE;
+  if ((y == nullptr) == (y_perm == nullptr)) return MOE_ERR_NULL;
+  const bool gather = (flags & MOE_FFN_GATHER) != 0;
+  if (!a || !offsets || !w_gate_up || !w_down) return MOE_ERR_NULL;
+  if ((gather || y) && !row_token) return MOE_ERR_NULL;
+  if (y && !row_w) return MOE_ERR_NULL;
+  if (w_dtype == MOE_FP8_E4M3 && (!s_gate_up || !s_down)) return MOE_ERR_NULL;
+  if (!workspace) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < moe_ffn_workspace_size(R_cap, E_loc, H, I, a_dtype)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(a) || !aligned16(w_gate_up) || !aligned16(w_down) || (y && !aligned16(y)) ||
+      (y_perm && !aligned16(y_perm)) || ((uintptr_t)workspace & 255u) != 0)
+    return MOE_ERR_ALIGN;
+  const unsigned only = flags & (MOE_FFN_ONLY_GATE_UP | MOE_FFN_ONLY_DOWN);
+  if (only == (MOE_FFN_ONLY_GATE_UP | MOE_FFN_ONLY_DOWN)) return MOE_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (y && (flags & MOE_FFN_ZERO_Y) && only != MOE_FFN_ONLY_GATE_UP) {
+    hipError_t err = launch_zero_f32(y, (size_t)T * H, s);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+  }
+  FfnArgs fa{};
+  fa.a = a;
+  fa.a_bf16 = a_dtype == MOE_BF16;
+  fa.gather = gather;
+  fa.offsets = offsets;
+  fa.row_token = row_token;
+  fa.row_w = row_w;
+  fa.El = E_loc;
+  fa.T = T;
+  fa.R_cap = R_cap;
+  fa.H = H;
+  fa.I = I;
+  fa.w_gu = w_gate_up;
+  fa.w_d = w_down;
+  fa.w_dt = w_dtype == MOE_F32 ? 0 : (w_dtype == MOE_BF16 ? 1 : 2);
+  fa.s_gu = s_gate_up;
+  fa.s_d = s_down;
+  fa.y = y;
+  fa.y_perm = y_perm;
+  fa.sched = (int32_t *)workspace;
+  fa.h = (char *)workspace + ffn_sched_bytes(E_loc);
+  fa.phase = only == MOE_FFN_ONLY_GATE_UP ? 1 : (only == MOE_FFN_ONLY_DOWN ? 2 : 3);
+  return hip_status(launch_ffn(fa, s));
+}
+
+int moe_combine(const float *y_perm, const int32_t *token_row, const float *topk_w, int T, int k, int H, float *y,
+                void *stream) {
+  if (T < 0 || k < 1 || k > 32 || H < 4 || H % 4 != 0) return MOE_ERR_SHAPE;
+  if ((long long)T * k >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !token_row || !topk_w || !y) return MOE_ERR_NULL;
+  if (!aligned16(y_perm) || !aligned16(y)) return MOE_ERR_ALIGN;
+  return hip_status(launch_combine(y_perm, token_row, topk_w, T, k, H, y, (hipStream_t)stream));
+}
+
+}  // extern "C"

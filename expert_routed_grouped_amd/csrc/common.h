@@ -1,0 +1,82 @@
+// Shared device helpers and internal launcher declarations of the gfx950 MoE library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MOE_WAVE 64
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 bit patterns held two per 32-bit word: element 0 in the low half.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 with round-to-nearest-even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Pack two fp32 into two bf16 (lo = a, hi = b), RNE.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Four e4m3 codes (one 32-bit word) -> four bf16 values (two words), exact.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
+  auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+static inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// Internal launchers (host side).  Arguments are validated by the ABI layer.
+// ---------------------------------------------------------------------------
+hipError_t launch_route(const void *x, int x_bf16, const void *w, int w_bf16, const float *bias, int T, int H, int E,
+                        int k, int32_t *ids, float *gates, hipStream_t s);
+
+hipError_t launch_permute(const int32_t *ids, const float *w, int T, int k, int lo, int El, int32_t *counts,
+                          int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row, hipStream_t s);
+
+hipError_t launch_gather_rows(const void *x, int esz, int H, const int32_t *offsets, int El, const int32_t *row_token,
+                              int R_cap, void *x_perm, hipStream_t s);
+
+hipError_t launch_combine(const float *y_perm, const int32_t *token_row, const float *w, int T, int k, int H, float *y,
+                          hipStream_t s);
+
+hipError_t launch_zero_f32(float *p, size_t n, hipStream_t s);
+
+// Grouped FFN.  ``sched`` is device scratch of at least ffn_sched_bytes(El) bytes,
+// ``h`` is the intermediate [R_cap, I] (bf16 or fp32 by path).
+struct FfnArgs {
+  const void *a;          // x [T,H] (gather) or x_perm [R_cap,H]
+  int a_bf16;             // 1: bf16 activations, 0: fp32
+  int gather;             // 1: row r reads a[row_token[r]]
+  const int32_t *offsets; // [El+1]
+  const int32_t *row_token;
+  const float *row_w;
+  int El, T, R_cap, H, I;
+  const void *w_gu;       // [El, 2I, H]
+  const void *w_d;        // [El, H, I]
+  int w_dt;               // 0 f32, 1 bf16, 2 e4m3
+  const float *s_gu, *s_d;
+  float *y;               // fused combine target (atomic) or NULL
+  float *y_perm;          // per-row outputs when y == NULL
+  void *h;                // intermediate
+  int32_t *sched;         // scheduling scratch
+  int phase;              // bit 0: gate/up half, bit 1: down half
+};
+
+size_t ffn_sched_bytes(int El);
+hipError_t launch_ffn(const FfnArgs &a, hipStream_t s);

@@ -1,0 +1,180 @@
+"""Thin ctypes binding of ``libmoe.so`` (declared in ``include/moe.h``).
+
+Argument marshalling only: torch tensors in, raw device pointers and sizes to
+the C ABI, every step runs in the library's HIP kernels on the tensor's
+current stream.  There is no fallback: without the built library every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_FFN_GATHER, MOE_FFN_ZERO_Y, MOE_FFN_ONLY_GATE_UP, MOE_FFN_ONLY_DOWN = 1, 2, 4, 8
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE", -4: "MOE_ERR_WORKSPACE",
+          -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIGN"}
+
+# Every symbol moe.h declares (checked by the CPU test suite).
+EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_ffn_workspace_size",
+           "moe_grouped_ffn", "moe_combine")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m expert_routed_grouped_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.moe_version.restype = I
+        L.moe_version.argtypes = []
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_status_str.argtypes = [I]
+        L.moe_route.restype = I
+        L.moe_route.argtypes = [P, I, P, I, P, I, I, I, I, P, P, P]
+        L.moe_permute.restype = I
+        L.moe_permute.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, I, I, P, P]
+        L.moe_ffn_workspace_size.restype = Z
+        L.moe_ffn_workspace_size.argtypes = [I, I, I, I, I]
+        L.moe_grouped_ffn.restype = I
+        L.moe_grouped_ffn.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, P, Z, ctypes.c_uint, P]
+        L.moe_combine.restype = I
+        L.moe_combine.argtypes = [P, P, P, I, I, I, P, P]
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoEError(fn, status, lib().moe_status_str(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MOE_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def moe_version() -> int:
+    return lib().moe_version()
+
+
+def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+              topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None, stream=None):
+    """Router logits (canonical fp32 FMA chain), top-k, renormalised gates -> (topk_ids, topk_w)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _check("moe_route", lib().moe_route(_ptr(x), _dtype(x), _ptr(w_router), _dtype(w_router), _ptr(bias), T, H, E, k,
+                                        _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+    return topk_ids, topk_w
+
+
+def moe_permute(topk_ids: torch.Tensor, topk_w: torch.Tensor, E: int, e_begin: int, e_end: int,
+                x: Optional[torch.Tensor] = None, x_perm: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                stream=None) -> dict:
+    """Counts, offsets and the stable by-expert grouping of the local assignments.
+
+    Returns dict(counts, offsets, row_token, row_w, token_row[, x_perm]); row
+    buffers have R_cap = T*min(k, E_loc) entries, the first offsets[-1] are valid."""
+    T, k = topk_ids.shape
+    El = e_end - e_begin
+    R_cap = T * min(k, El)
+    dev = topk_ids.device
+    o = dict(out) if out else {}
+    o.setdefault("counts", torch.empty(El, dtype=torch.int32, device=dev))
+    o.setdefault("offsets", torch.empty(El + 1, dtype=torch.int32, device=dev))
+    o.setdefault("row_token", torch.empty(max(R_cap, 1), dtype=torch.int32, device=dev))
+    o.setdefault("row_w", torch.empty(max(R_cap, 1), dtype=torch.float32, device=dev))
+    o.setdefault("token_row", torch.empty((T, k), dtype=torch.int32, device=dev))
+    H = 0
+    xdt = MOE_BF16
+    if x is not None:
+        H = x.shape[1]
+        xdt = _dtype(x)
+        if x_perm is None:
+            x_perm = torch.empty((max(R_cap, 1), H), dtype=x.dtype, device=dev)
+        o["x_perm"] = x_perm
+    _check("moe_permute", lib().moe_permute(_ptr(topk_ids), _ptr(topk_w), T, k, E, e_begin, e_end,
+                                            _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["row_token"]),
+                                            _ptr(o["row_w"]), _ptr(o["token_row"]), _ptr(x), xdt, H,
+                                            _ptr(x_perm), _stream(stream)))
+    o["R_cap"] = R_cap
+    return o
+
+
+def moe_ffn_workspace_size(R_cap: int, E_loc: int, H: int, I: int, a_dtype: int) -> int:
+    return int(lib().moe_ffn_workspace_size(R_cap, E_loc, H, I, a_dtype))
+
+
+def moe_grouped_ffn(a: torch.Tensor, offsets: torch.Tensor, row_token: torch.Tensor, row_w: torch.Tensor, T: int,
+                    R_cap: int, w_gate_up: torch.Tensor, w_down: torch.Tensor,
+                    s_gate_up: Optional[torch.Tensor] = None, s_down: Optional[torch.Tensor] = None,
+                    y: Optional[torch.Tensor] = None, y_perm: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, gather: bool = True, zero_y: bool = True,
+                    phase: str = "both", stream=None):
+    """SwiGLU expert FFN over the grouped rows.  With ``y`` the gate-weighted combine is
+    fused (y accumulates; zeroed first when ``zero_y``); otherwise writes ``y_perm``.
+    ``phase``: "both", "gate_up" or "down" (the two halves, same arguments and workspace)."""
+    El, twoI, H = w_gate_up.shape
+    I = twoI // 2
+    adt = _dtype(a)
+    need = moe_ffn_workspace_size(R_cap, El, H, I, adt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    flags = (MOE_FFN_GATHER if gather else 0) | (MOE_FFN_ZERO_Y if zero_y else 0)
+    flags |= {"both": 0, "gate_up": MOE_FFN_ONLY_GATE_UP, "down": MOE_FFN_ONLY_DOWN}[phase]
+    _check("moe_grouped_ffn", lib().moe_grouped_ffn(
+        _ptr(a), adt, _ptr(offsets), _ptr(row_token), _ptr(row_w), El, T, R_cap, H, I, _ptr(w_gate_up),
+        _ptr(w_down), _dtype(w_gate_up), _ptr(s_gate_up), _ptr(s_down), _ptr(y), _ptr(y_perm), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), flags, _stream(stream)))
+    return y if y is not None else y_perm
+
+
+def moe_combine(y_perm: torch.Tensor, token_row: torch.Tensor, topk_w: torch.Tensor, y: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    T, k = token_row.shape
+    H = y_perm.shape[1]
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=y_perm.device)
+    _check("moe_combine", lib().moe_combine(_ptr(y_perm), _ptr(token_row), _ptr(topk_w), T, k, H, _ptr(y),
+                                            _stream(stream)))
+    return y

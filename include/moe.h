@@ -1,0 +1,209 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) Mixture-of-Experts FFN layer library.
+ *
+ * One MoE FFN layer, as one GPU's share of the work, is four calls:
+ *
+ *   moe_route        router GEMM, top-k of E experts, renormalised gates
+ *   moe_permute      per-expert counts and offsets, rows grouped by expert
+ *   moe_grouped_ffn  SwiGLU expert FFN as grouped GEMMs over the expert rows,
+ *                    with the gate-weighted combine fused into the
+ *                    down-projection epilogue (or per-row outputs for moe_combine)
+ *   moe_combine      gate-weighted gather-sum of per-row outputs to token order
+ *
+ * The method follows three pages: "AI-infra book, ch. 9 Distributed inference"
+ * (section 9.3.4, Fig. 9-16: route, group rows by expert, expert GEMMs, weighted
+ * combine; section 9.3.2: the expert is three 4096 x 1536 matrices), "Hosting
+ * Qwen on Blackwell" (section "MoE Dispatch - Combine": dispatch groups each
+ * expert's tokens into GEMM input buffers and combine is a weighted
+ * accumulation; section "Expert parallelism": with replicated inputs a rank only
+ * selects the tokens of its local experts) and "PagedAttention, speculative
+ * decoding, MoE and Blackwell" (MoE list: a gating network sends each token to
+ * its top-K experts).  The library never drops an assignment of a local expert
+ * and never changes k (book, section 9.4.2: changing top-k changes the model).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every array argument is a DEVICE pointer to row-major memory owned by the
+ *    caller.  The library allocates nothing, frees nothing and keeps no mutable
+ *    global state; calls on different streams may run concurrently as long as
+ *    they do not share output buffers.
+ *  - ``stream`` is a hipStream_t passed as ``void*`` (NULL = the null stream).
+ *    All work is enqueued on it; the calls return without waiting for the GPU.
+ *    There is no device-to-host copy anywhere inside the calls.
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code.  Argument errors are
+ *    detected on the host before anything is enqueued (then nothing ran).
+ *    MOE_ERR_HIP means a launch failed (hipGetLastError after the launch).
+ *    Faults inside kernels surface, as usual for HIP, at the next
+ *    synchronisation of the stream.  NaN/Inf input values are not checked.
+ *  - Element types: MOE_F32 (float), MOE_BF16 (bfloat16 bit patterns, uint16),
+ *    MOE_FP8_E4M3 (OCP E4M3 codes, uint8; only for expert weights, always with
+ *    fp32 per-output-channel scales).
+ *  - Sizes: T >= 0 tokens, hidden H, E experts with 1 <= k <= min(E, 32),
+ *    E <= 512, intermediate I.  Local experts are [e_begin, e_end) with
+ *    E_loc = e_end - e_begin >= 1; R_cap = T * min(k, E_loc) bounds the number
+ *    of local assignments, so every row buffer is sized without knowing the
+ *    routing on the host.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define MOE_F32 0
+#define MOE_BF16 1
+#define MOE_FP8_E4M3 2
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)      /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)     /* a size is out of the supported range */
+#define MOE_ERR_DTYPE (-3)     /* unsupported element type or type combination */
+#define MOE_ERR_WORKSPACE (-4) /* workspace missing or too small */
+#define MOE_ERR_HIP (-5)       /* a kernel launch failed */
+#define MOE_ERR_ALIGN (-6)     /* a pointer is not 16-byte aligned */
+
+/* moe_grouped_ffn flags */
+#define MOE_FFN_GATHER 1u /* ``a`` is x [T,H]; row r reads x[row_token[r]] (no x_perm needed) */
+#define MOE_FFN_ZERO_Y 2u /* zero y [T,H] on the stream before the fused combine accumulates */
+#define MOE_FFN_ONLY_GATE_UP 4u /* run only the first half: gate/up + SwiGLU into the workspace's h */
+#define MOE_FFN_ONLY_DOWN 8u    /* run only the second half: down + combine from the workspace's h, which a
+                                   preceding MOE_FFN_ONLY_GATE_UP call with the same arguments filled */
+
+/* Library version (major*10000 + minor*100 + patch). */
+int moe_version(void);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char *moe_status_str(int status);
+
+/*
+ * moe_route - router GEMM, top-k selection and renormalised gates.
+ *
+ * Defined by: PagedAttention/MoE page, MoE list (a gating network picks the
+ * top-K experts of each token); AI-infra book section 9.3.4 (the router picks 8
+ * experts per token, the combine is the routing-weighted sum).
+ *
+ *   logit[t,e] = fp32 fused-multiply-add chain over h = 0..H-1 (ascending,
+ *                starting at +0) of x[t,h] * w_router[e,h], then + bias[e]
+ *                (one fp32 add) when bias != NULL.  This order is part of the
+ *                contract: it makes the selected experts reproducible bit for bit.
+ *   topk_ids[t,0..k-1] = the k experts with the largest logits, largest first;
+ *                equal logits (IEEE equality, -0 == +0) go to the lower index.
+ *   topk_w[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected
+ *                logits (= softmax over all E renormalised over the k selected).
+ *
+ * x [T,H] and w_router [E,H]: MOE_F32 or MOE_BF16 each; bias [E] fp32 or NULL.
+ * Outputs topk_ids [T,k] int32 and topk_w [T,k] fp32 are overwritten.
+ * Errors: MOE_ERR_NULL (x, w_router, topk_ids or topk_w NULL with T > 0),
+ * MOE_ERR_SHAPE (T < 0, H < 1, E < 1 or E > 512, k < 1, k > min(E, 32)),
+ * MOE_ERR_DTYPE, MOE_ERR_HIP.  T == 0 enqueues nothing.
+ */
+int moe_route(const void *x, int x_dtype, const void *w_router, int w_dtype, const float *bias,
+              int T, int H, int E, int k, int32_t *topk_ids, float *topk_w, void *stream);
+
+/*
+ * moe_permute - local dispatch: group the assignments of local experts by expert.
+ *
+ * Defined by: "Hosting Qwen on Blackwell", section "MoE Dispatch - Combine"
+ * (dispatch moves and groups tokens for the MoE GEMM) and section "Expert
+ * parallelism" (inputs replicated on all ranks, so dispatch only selects the
+ * tokens routed to local experts and prepares the GEMM input buffers);
+ * AI-infra book section 9.3.4 (rows are permuted by expert before the expert
+ * GEMMs); book section 9.4.2 (m_j, the rows each expert receives).
+ *
+ *   counts[i]  = number of assignments (t, j) with topk_ids[t,j] == e_begin + i
+ *   offsets    = exclusive prefix sum of counts, offsets[E_loc] = R
+ *   rows r in [offsets[i], offsets[i+1]) are the assignments of expert
+ *   e_begin + i in increasing token order (the unique stable order), and
+ *   row_token[r] = t, row_w[r] = topk_w[t,j], token_row[t,j] = r;
+ *   token_row[t,j] = -1 when topk_ids[t,j] is not local.
+ *   x_perm[r,:] = x[row_token[r],:] bit for bit when x and x_perm are not NULL.
+ *
+ * Sizes: counts [E_loc], offsets [E_loc+1] int32; row_token [R_cap] int32,
+ * row_w [R_cap] fp32 (only the first R entries are written); token_row [T,k]
+ * int32; x [T,H] and x_perm [R_cap,H] of element type x_dtype (MOE_F32 or
+ * MOE_BF16), 16-byte aligned, H a multiple of 8.  topk_ids must hold distinct
+ * experts per token in [0, E) (as moe_route writes them).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (0 <= e_begin < e_end <= E, E <= 512,
+ * 1 <= k <= min(E,32), T*k < 2^31), MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_permute(const int32_t *topk_ids, const float *topk_w, int T, int k, int E, int e_begin, int e_end,
+                int32_t *counts, int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
+                const void *x, int x_dtype, int H, void *x_perm, void *stream);
+
+/*
+ * Bytes of workspace moe_grouped_ffn needs (the intermediate h [R_cap, I] plus
+ * scheduling scratch), for activations of type a_dtype.
+ */
+size_t moe_ffn_workspace_size(int R_cap, int E_loc, int H, int I, int a_dtype);
+
+/*
+ * moe_grouped_ffn - SwiGLU expert FFN over the grouped rows, with the combine.
+ *
+ * Defined by: AI-infra book section 9.3.2 (expert = gate, up and down matrices
+ * of 4096 x 1536; expert FLOPs 2*m*P_e) and section 9.4.3 (grouped GEMM over the
+ * experts' variable row counts); "Hosting Qwen on Blackwell", section "MoE
+ * GEMM" and section "MoE Dispatch - Combine" (combine = weighted accumulation;
+ * with expert parallelism a local accumulation over the local experts).
+ *
+ * For each local expert i and each of its rows r in [offsets[i], offsets[i+1]):
+ *   a_r   = MOE_FFN_GATHER ? a[row_token[r],:] : a[r,:]            (length H)
+ *   G     = w_gate_up[i, 0..I-1, :]  . a_r   (x s_gate_up[i, 0..I-1] for fp8)
+ *   U     = w_gate_up[i, I..2I-1, :] . a_r   (x s_gate_up[i, I..2I-1] for fp8)
+ *   h_r   = silu(G) * U  (silu(z) = z / (1 + exp(-z))), fp32, then rounded to
+ *           bf16 (round-to-nearest-even) when a_dtype is MOE_BF16
+ *   o_r   = w_down[i] . h_r              (x s_down[i, :] for fp8), length H
+ *   y != NULL:  y[row_token[r],:] += row_w[r] * o_r   (fp32 atomic adds, so the
+ *               order of the k additions to a token is not fixed; with
+ *               MOE_FFN_ZERO_Y y is zeroed first on the stream)
+ *   y == NULL:  y_perm[r,:] = o_r                     (then call moe_combine)
+ * Products accumulate in fp32 (bf16 matrix cores for bf16 and fp8 weights;
+ * e4m3 values are exact in bf16).
+ *
+ * a: [R_cap,H] (or [T,H] with MOE_FFN_GATHER), MOE_BF16 with MOE_BF16 or
+ * MOE_FP8_E4M3 weights, or MOE_F32 with MOE_F32 weights.  w_gate_up
+ * [E_loc,2I,H] (rows 0..I-1 gate, I..2I-1 up), w_down [E_loc,H,I]; s_gate_up
+ * [E_loc,2I] and s_down [E_loc,H] fp32, required for fp8 and ignored otherwise.
+ * y [T,H] fp32 or y_perm [R_cap,H] fp32 (exactly one of them non-NULL).
+ * workspace: at least moe_ffn_workspace_size(...) bytes, 256-byte aligned.
+ * H and I must be multiples of 64; every pointer 16-byte aligned.
+ * MOE_FFN_ONLY_GATE_UP / MOE_FFN_ONLY_DOWN split the call into its two halves
+ * (same arguments, same workspace, same stream, in that order), e.g. to place
+ * other work between them; setting both is MOE_ERR_SHAPE.  MOE_FFN_ZERO_Y is
+ * honoured by the call that runs the down half.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE,
+ * MOE_ERR_ALIGN, MOE_ERR_HIP.  R_cap == 0 or T == 0 only zeroes y (if asked).
+ */
+int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const int32_t *row_token,
+                    const float *row_w, int E_loc, int T, int R_cap, int H, int I,
+                    const void *w_gate_up, const void *w_down, int w_dtype,
+                    const float *s_gate_up, const float *s_down, float *y, float *y_perm,
+                    void *workspace, size_t workspace_bytes, unsigned flags, void *stream);
+
+/*
+ * moe_combine - gate-weighted gather-sum of per-row outputs back to token order.
+ *
+ * Defined by: "Hosting Qwen on Blackwell", section "MoE Dispatch - Combine"
+ * (combine = weighted accumulation); AI-infra book section 9.3.4 (the token's
+ * output is the routing-weighted sum of its expert results).
+ *
+ *   y[t,:] = sum over j = 0..k-1 with token_row[t,j] >= 0 of
+ *            topk_w[t,j] * y_perm[token_row[t,j],:]
+ * accumulated in fp32 in increasing j (deterministic); y [T,H] is overwritten
+ * (rows of tokens without local experts become 0).  y_perm [R_cap,H] fp32,
+ * token_row [T,k] int32, topk_w [T,k] fp32.  H a multiple of 4, pointers
+ * 16-byte aligned.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_combine(const float *y_perm, const int32_t *token_row, const float *topk_w, int T, int k, int H,
+                float *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

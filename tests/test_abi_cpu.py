@@ -1,0 +1,116 @@
+"""CPU checks of the C ABI: the library loads without a GPU, exports every symbol
+the header declares, and rejects bad arguments on the host before any HIP call
+(nothing here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from expert_routed_grouped_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = moe.lib()
+    names = header_functions()
+    assert set(names) == set(moe.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert moe.moe_version() == 100
+
+
+def test_status_strings():
+    L = moe.lib()
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert L.moe_status_str(code)
+    assert L.moe_status_str(-99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)  # never dereferenced: every call below fails validation first
+FAKE_ODD = P(0x1004)
+
+
+def route(**kw):
+    a = dict(x=FAKE, xd=1, w=FAKE, wd=1, b=None, T=4, H=64, E=8, k=2, ids=FAKE, gw=FAKE)
+    a.update(kw)
+    return moe.lib().moe_route(a["x"], a["xd"], a["w"], a["wd"], a["b"], a["T"], a["H"], a["E"], a["k"], a["ids"],
+                               a["gw"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), -2), (dict(k=9), -2), (dict(E=513, k=2), -2), (dict(E=64, k=33), -2), (dict(T=-1), -2),
+    (dict(H=0), -2), (dict(xd=2), -3), (dict(wd=7), -3), (dict(x=None), -1), (dict(ids=None), -1),
+    (dict(gw=None), -1), (dict(T=0), 0),
+])
+def test_route_validation(kw, code):
+    assert route(**kw) == code
+
+
+def permute(**kw):
+    a = dict(ids=FAKE, w=FAKE, T=4, k=2, E=8, lo=0, hi=8, c=FAKE, o=FAKE, rt=FAKE, rw=FAKE, tr=FAKE, x=None, xd=1,
+             H=0, xp=None)
+    a.update(kw)
+    return moe.lib().moe_permute(a["ids"], a["w"], a["T"], a["k"], a["E"], a["lo"], a["hi"], a["c"], a["o"], a["rt"],
+                                 a["rw"], a["tr"], a["x"], a["xd"], a["H"], a["xp"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lo=3, hi=3), -2), (dict(lo=-1), -2), (dict(hi=9), -2), (dict(k=9), -2), (dict(E=600, hi=600), -2),
+    (dict(c=None), -1), (dict(rt=None), -1), (dict(x=FAKE), -1), (dict(xp=FAKE), -1),
+    (dict(x=FAKE, xp=FAKE, H=12), -2), (dict(x=FAKE, xp=FAKE, H=64, xd=2), -3),
+    (dict(x=FAKE_ODD, xp=FAKE, H=64), -6),
+])
+def test_permute_validation(kw, code):
+    assert permute(**kw) == code
+
+
+def ffn(**kw):
+    a = dict(a=FAKE, ad=1, off=FAKE, rt=FAKE, rw=FAKE, El=8, T=16, R=32, H=128, I=64, wgu=FAKE, wd=FAKE, wdt=1,
+             sgu=None, sd=None, y=FAKE, yp=None, ws=FAKE, wsb=1 << 30, flags=3)
+    a.update(kw)
+    return moe.lib().moe_grouped_ffn(a["a"], a["ad"], a["off"], a["rt"], a["rw"], a["El"], a["T"], a["R"], a["H"],
+                                     a["I"], a["wgu"], a["wd"], a["wdt"], a["sgu"], a["sd"], a["y"], a["yp"], a["ws"],
+                                     a["wsb"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=100), -2), (dict(I=96), -2), (dict(El=0), -2), (dict(R=16 * 8 + 1), -2), (dict(T=-1), -2),
+    (dict(ad=0), -3), (dict(wdt=0), -3), (dict(ad=2, wdt=2), -3),
+    (dict(y=None), -1), (dict(yp=FAKE), -1), (dict(wdt=2), -1), (dict(rt=None), -1), (dict(rw=None), -1),
+    (dict(ws=None), -4), (dict(wsb=10), -4), (dict(a=FAKE_ODD), -6), (dict(ws=P(0x1010)), -6),
+])
+def test_ffn_validation(kw, code):
+    assert ffn(**kw) == code
+
+
+def test_workspace_size():
+    L = moe.lib()
+    # h [R_cap, I] bf16 plus an aligned schedule prefix
+    ws = L.moe_ffn_workspace_size(48000, 128, 4096, 1536, 1)
+    assert ws >= 48000 * 1536 * 2 and ws % 256 == 0
+    assert L.moe_ffn_workspace_size(100, 4, 64, 64, 0) >= 100 * 64 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=6), -2), (dict(k=0), -2), (dict(y=None), -1), (dict(yp=FAKE_ODD), -6), (dict(T=0), 0),
+])
+def test_combine_validation(kw, code):
+    a = dict(yp=FAKE, tr=FAKE, w=FAKE, T=4, k=2, H=64, y=FAKE)
+    a.update(kw)
+    assert moe.lib().moe_combine(a["yp"], a["tr"], a["w"], a["T"], a["k"], a["H"], a["y"], None) == code
+
+
+def test_python_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.lib()

@@ -1,0 +1,338 @@
+"""GPU parity: every entry point of the HIP library against the CPU oracle.
+
+Routing ids, counts, offsets, the permutation and x_perm must match bit for
+bit; gates within 1e-6; layer outputs within max|err| <= 1e-2 * RMS(oracle).
+Small shapes are compared element by element on every token; the full
+workload shapes (decode, prefill, skewed prefill, EP share) run in the launch
+configuration the benchmark times and are compared on sampled tokens, whose
+oracle rows are computed one token at a time.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from expert_routed_grouped_amd import layer as L
+from expert_routed_grouped_amd import moe, synth
+from expert_routed_grouped_amd.synth import CONFIGS, LayerConfig
+
+pytestmark = pytest.mark.gpu
+
+GATE_TOL = 1e-6
+Y_TOL = 1e-2
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@functools.lru_cache(maxsize=None)
+def host_inputs(cfg: LayerConfig):
+    return synth.make_inputs(cfg)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_routing(cfg: LayerConfig):
+    inp = host_inputs(cfg)
+    ids, w, _ = O.route(inp["x"], inp["w_router"], inp["bias"], cfg.k)
+    return ids, w
+
+
+def check_y(y_gpu, y_ref, what=""):
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(y_ref ** 2))
+    err = np.max(np.abs(y_gpu - y_ref)) if y_ref.size else 0.0
+    say(f"  {what} max|err| = {err:.3e}, RMS = {rms:.3e}, ratio = {err / max(rms, 1e-30):.2e}")
+    assert rms > 0
+    assert err <= Y_TOL * rms
+
+
+def gpu_route(dev, cfg):
+    ids, w = moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+def to_dev_routing(ids, w):
+    return torch.from_numpy(np.ascontiguousarray(ids)).cuda(), torch.from_numpy(np.ascontiguousarray(w)).cuda()
+
+
+def gpu_layer(dev, cfg, ids_d, w_d, fused: bool, gather: bool = True):
+    """The four calls on the given routing; returns (y, perm dict)."""
+    x = dev["x"]
+    p = moe.moe_permute(ids_d, w_d, cfg.E, cfg.lo, cfg.hi, x=None if gather else x)
+    R_cap = p["R_cap"]
+    a = x if gather else p["x_perm"]
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+    if fused:
+        y.fill_(float("nan"))  # MOE_FFN_ZERO_Y must clear it
+        moe.moe_grouped_ffn(a, p["offsets"], p["row_token"], p["row_w"], cfg.T, R_cap, dev["w_gate_up"],
+                            dev["w_down"], dev["s_gate_up"], dev["s_down"], y=y, gather=gather, zero_y=True)
+    else:
+        yp = torch.empty((max(R_cap, 1), cfg.H), dtype=torch.float32, device="cuda")
+        moe.moe_grouped_ffn(a, p["offsets"], p["row_token"], p["row_w"], cfg.T, R_cap, dev["w_gate_up"],
+                            dev["w_down"], dev["s_gate_up"], dev["s_down"], y_perm=yp, gather=gather)
+        moe.moe_combine(yp, p["token_row"], w_d, y=y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), p
+
+
+# ----------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------
+ROUTE_CASES = [
+    CONFIGS["tiny"], CONFIGS["decode"], CONFIGS["prefill"], CONFIGS["skew"], CONFIGS["ep_share"],
+    LayerConfig("r_f32_oddH", T=37, H=203, E=5, k=3, I=64, act="f32", wdt="f32", init="fan_in", seed=101),
+    LayerConfig("r_E200", T=600, H=512, E=200, k=8, I=64, seed=102),
+    LayerConfig("r_E512_k32", T=70, H=256, E=512, k=32, I=64, seed=103, w_std=0.05),
+    LayerConfig("r_kE", T=64, H=128, E=16, k=16, I=64, seed=104),
+    LayerConfig("r_k1", T=513, H=64, E=64, k=1, I=64, seed=105),
+]
+
+
+@pytest.mark.parametrize("cfg", ROUTE_CASES, ids=lambda c: c.name)
+def test_route_matches_oracle(cfg):
+    inp = synth.make_inputs(cfg, with_weights=False)
+    dev = L.to_device(inp)
+    say(f"route {cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k}")
+    ids, w = gpu_route(dev, cfg)
+    ids_o, w_o, _ = O.route(inp["x"], inp["w_router"], inp["bias"], cfg.k)
+    assert np.array_equal(ids, ids_o)
+    assert np.max(np.abs(w - w_o)) <= GATE_TOL
+    # deterministic: a second run gives the same bits
+    ids2, w2 = gpu_route(dev, cfg)
+    assert np.array_equal(ids2, ids) and np.array_equal(w2.view(np.uint32), w.view(np.uint32))
+
+
+def test_route_ties_and_zero_router():
+    cfg = LayerConfig("ties", T=300, H=256, E=128, k=8, I=64, seed=106)
+    inp = synth.make_inputs(cfg, with_weights=False)
+    wr = inp["w_router"].copy()
+    wr[7] = wr[3]
+    wr[100] = wr[3]
+    wr[64] = wr[0]
+    for w_router in (wr, np.zeros_like(wr)):
+        dev = L.to_device(dict(inp, w_router=w_router))
+        ids, w = gpu_route(dev, cfg)
+        ids_o, w_o, _ = O.route(inp["x"], w_router, None, cfg.k)
+        assert np.array_equal(ids, ids_o)
+        assert np.max(np.abs(w - w_o)) <= GATE_TOL
+    assert np.all(ids == np.arange(8)) and np.all(w == np.float32(0.125))
+
+
+def test_route_empty_batch():
+    cfg = LayerConfig("empty", T=0, H=64, E=8, k=2, I=64, seed=107)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    wr = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    ids, w = moe.moe_route(x, wr, None, 2)
+    assert ids.shape == (0, 2)
+
+
+# ----------------------------------------------------------------------------
+# permutation
+# ----------------------------------------------------------------------------
+def check_permutation(p_gpu, p_or, T, k, x=None, same_gates=True):
+    """Integer outputs bit for bit.  row_w is a copy of the gates given to moe_permute:
+    bit for bit when those were the oracle's, else within the gate tolerance."""
+    R = p_or["R"]
+    assert np.array_equal(p_gpu["counts"].cpu().numpy(), p_or["counts"])
+    assert np.array_equal(p_gpu["offsets"].cpu().numpy(), p_or["offsets"])
+    assert np.array_equal(p_gpu["row_token"][:R].cpu().numpy(), p_or["row_token"])
+    rw = p_gpu["row_w"][:R].cpu().numpy()
+    if same_gates:
+        assert np.array_equal(rw.view(np.uint32), p_or["row_w"].view(np.uint32))
+    else:
+        assert np.max(np.abs(rw - p_or["row_w"]), initial=0.0) <= GATE_TOL
+    assert np.array_equal(p_gpu["token_row"].cpu().numpy(), p_or["token_row"])
+    if x is not None:
+        xp = p_gpu["x_perm"][:R].cpu()
+        ref = x[p_or["row_token"]]
+        assert np.array_equal(xp.view(torch.int16).numpy().view(np.uint16) if xp.dtype == torch.bfloat16 else xp.numpy(),
+                              ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "ep_share"])
+def test_permute_matches_oracle(name):
+    cfg = CONFIGS[name]
+    ids, w = oracle_routing(cfg)
+    inp = host_inputs(cfg)
+    say(f"permute {name}: T={cfg.T} k={cfg.k} local=[{cfg.lo},{cfg.hi})")
+    ids_d, w_d = to_dev_routing(ids, w)
+    xd = L.to_device({"cfg": cfg, "x": inp["x"], "w_router": inp["w_router"]})["x"]
+    p = moe.moe_permute(ids_d, w_d, cfg.E, cfg.lo, cfg.hi, x=xd)
+    torch.cuda.synchronize()
+    check_permutation(p, O.permute(ids, w, cfg.lo, cfg.hi), cfg.T, cfg.k, x=inp["x"])
+    counts = p["counts"].cpu().numpy()
+    if cfg.E_loc == cfg.E:
+        assert counts.sum() == cfg.T * cfg.k
+    if name == "prefill":
+        assert counts.mean() == 375  # 6000 * 8 / 128
+
+
+def routing_case(kind):
+    rng = np.random.default_rng(sum(map(ord, kind)))
+    if kind == "one_hot_experts":      # every token picks experts 0..k-1
+        T, E, k = 1000, 64, 4
+        ids = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    elif kind == "k_equals_E":
+        T, E, k = 300, 8, 8
+        ids = np.argsort(rng.random((T, E)), axis=1).astype(np.int32)
+    elif kind == "max_experts":
+        T, E, k = 2000, 512, 8
+        ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    elif kind == "ragged":
+        T, E, k = 333, 128, 7
+        ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    elif kind == "many_tokens":
+        T, E, k = 20000, 128, 8
+        ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    else:
+        raise ValueError(kind)
+    w = rng.random(ids.shape).astype(np.float32)
+    return ids, w, E
+
+
+@pytest.mark.parametrize("kind,lo,hi", [("one_hot_experts", 0, 64), ("one_hot_experts", 2, 3), ("k_equals_E", 0, 8),
+                                        ("k_equals_E", 5, 8), ("max_experts", 0, 512), ("max_experts", 100, 356),
+                                        ("ragged", 0, 128), ("ragged", 127, 128), ("many_tokens", 0, 128),
+                                        ("many_tokens", 32, 64)])
+def test_permute_edge_cases(kind, lo, hi):
+    ids, w, E = routing_case(kind)
+    ids_d, w_d = to_dev_routing(ids, w)
+    p = moe.moe_permute(ids_d, w_d, E, lo, hi)
+    torch.cuda.synchronize()
+    check_permutation(p, O.permute(ids, w, lo, hi), *ids.shape)
+
+
+def test_permute_empty_batch():
+    ids_d = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    w_d = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    p = moe.moe_permute(ids_d, w_d, 8, 0, 8)
+    torch.cuda.synchronize()
+    assert p["counts"].cpu().tolist() == [0] * 8 and p["offsets"].cpu().tolist() == [0] * 9
+
+
+# ----------------------------------------------------------------------------
+# expert FFN + combine, every token against the oracle
+# ----------------------------------------------------------------------------
+FFN_CASES = [
+    # several 128-row tiles per expert with ragged tails; 64-col ragged N tail in the down projection
+    LayerConfig("ffn_bf16", T=700, H=320, E=4, k=2, I=192, seed=201, w_std=0.05),
+    LayerConfig("ffn_fp8_local", T=700, H=320, E=6, k=3, I=192, wdt="fp8", e_begin=1, e_end=4, seed=202, w_std=0.05),
+    LayerConfig("ffn_skew_empty", T=500, H=256, E=32, k=4, I=128, bias="zipf", seed=203, w_std=0.05),
+    LayerConfig("ffn_k_eq_E", T=130, H=128, E=4, k=4, I=64, seed=204, w_std=0.05),
+    LayerConfig("ffn_single_expert", T=257, H=192, E=1, k=1, I=128, seed=205, w_std=0.05),
+    CONFIGS["tiny"],
+    LayerConfig("ffn_f32_local", T=200, H=128, E=8, k=2, I=64, act="f32", wdt="f32", e_begin=2, e_end=6,
+                init="fan_in", seed=206),
+]
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "combine"])
+@pytest.mark.parametrize("cfg", FFN_CASES, ids=lambda c: c.name)
+def test_layer_all_tokens_matches_oracle(cfg, fused):
+    inp = host_inputs(cfg)
+    dev = L.to_device(inp)
+    say(f"layer {cfg.name} fused={fused}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} w={cfg.wdt}")
+    ids, w = oracle_routing(cfg)
+    ids_g, w_g = gpu_route(dev, cfg)
+    assert np.array_equal(ids_g, ids)
+    ids_d, w_d = to_dev_routing(ids_g, w_g)
+    y, p = gpu_layer(dev, cfg, ids_d, w_d, fused=fused)
+    y_o = O.layer_tokens(np.arange(cfg.T), inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"],
+                         inp["s_gate_up"], inp["s_down"], round_h=cfg.act != "f32")
+    check_y(y, y_o, cfg.name)
+    if cfg.E_loc < cfg.E:
+        no_local = ~np.any((ids >= cfg.lo) & (ids < cfg.hi), axis=1)
+        assert np.all(y[no_local] == 0)
+
+
+@pytest.mark.parametrize("cfg", [FFN_CASES[0], FFN_CASES[1]], ids=lambda c: c.name)
+def test_layer_with_materialised_x_perm(cfg):
+    """gather=False: the FFN reads x_perm written by moe_permute instead of gathering x."""
+    inp = host_inputs(cfg)
+    dev = L.to_device(inp)
+    ids, w = oracle_routing(cfg)
+    ids_d, w_d = to_dev_routing(ids, w)
+    y, _ = gpu_layer(dev, cfg, ids_d, w_d, fused=False, gather=False)
+    y_o = O.layer_tokens(np.arange(cfg.T), inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"],
+                         inp["s_gate_up"], inp["s_down"])
+    check_y(y, y_o, cfg.name + " x_perm")
+
+
+def test_combine_matches_oracle_and_is_deterministic():
+    rng = np.random.default_rng(5)
+    ids, w, E = routing_case("ragged")
+    p = O.permute(ids, w, 10, 90)
+    yp = rng.standard_normal((max(p["R"], 1), 256)).astype(np.float32)
+    y_o = O.combine(yp, p["token_row"], w)
+    yp_d = torch.from_numpy(yp).cuda()
+    tr_d = torch.from_numpy(p["token_row"]).cuda()
+    w_d = torch.from_numpy(w).cuda()
+    y1 = moe.moe_combine(yp_d, tr_d, w_d).cpu().numpy()
+    y2 = moe.moe_combine(yp_d, tr_d, w_d).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    assert np.max(np.abs(y1 - y_o)) <= 1e-6 * np.max(np.abs(y_o))
+
+
+def test_ffn_empty_batch_zeroes_y():
+    cfg = LayerConfig("e", T=4, H=64, E=2, k=1, I=64, seed=1)
+    y = torch.full((4, 64), 3.0, device="cuda")
+    off = torch.zeros(3, dtype=torch.int32, device="cuda")
+    rt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rw = torch.zeros(1, dtype=torch.float32, device="cuda")
+    wgu = torch.zeros((2, 128, 64), dtype=torch.bfloat16, device="cuda")
+    wd = torch.zeros((2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_ffn(x, off, rt, rw, 4, 4, wgu, wd, y=y, zero_y=True)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
+# ----------------------------------------------------------------------------
+# full workload shapes, benchmark launch configuration, sampled tokens
+# ----------------------------------------------------------------------------
+def sample_tokens(cfg, ids, n=24):
+    rng = np.random.default_rng(cfg.seed + 77)
+    pick = {0, cfg.T - 1}
+    counts = np.bincount(ids.ravel(), minlength=cfg.E)
+    local = [e for e in range(cfg.lo, cfg.hi) if counts[e] > 0]
+    hot = max(local, key=lambda e: counts[e])
+    cold = min(local, key=lambda e: counts[e])
+    for e in (hot, cold):
+        toks = np.nonzero(np.any(ids == e, axis=1))[0]
+        pick.update(int(t) for t in (toks[0], toks[-1]))
+    pick.update(int(t) for t in rng.choice(cfg.T, size=n, replace=False))
+    return np.array(sorted(pick), dtype=np.int32)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "ep_share"])
+def test_full_workload_layer(name):
+    cfg = CONFIGS[name]
+    inp = host_inputs(cfg)
+    say(f"full layer {name}: generating / uploading")
+    dev = L.to_device(inp)
+    bufs = L.LayerBuffers(cfg)
+    say(f"full layer {name}: run_layer fused={bufs.fused} R_cap={bufs.R_cap}")
+    y = L.run_layer(dev, bufs)
+    torch.cuda.synchronize()
+    ids, w = oracle_routing(cfg)
+    assert np.array_equal(bufs.topk_ids.cpu().numpy(), ids)
+    assert np.max(np.abs(bufs.topk_w.cpu().numpy() - w)) <= GATE_TOL
+    p_or = O.permute(ids, w, cfg.lo, cfg.hi)
+    check_permutation(bufs.perm, p_or, cfg.T, cfg.k, same_gates=False)
+    toks = sample_tokens(cfg, ids)
+    say(f"full layer {name}: oracle on {len(toks)} sampled tokens")
+    y_o = O.layer_tokens(toks, inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"], inp["s_gate_up"],
+                         inp["s_down"])
+    yg = y.cpu().numpy()
+    check_y(yg[toks], y_o, name)
+    # a second call reuses the buffers and gives the same routing and (up to atomic order) the same y
+    y2 = L.run_layer(dev, bufs).cpu().numpy()
+    check_y(y2[toks], y_o, name + " (repeat)")
+    del dev, bufs
+    torch.cuda.empty_cache()
