@@ -43,7 +43,8 @@ int moe_route(const void *x, int x_dtype, const void *w_router, int w_dtype, con
 
 int moe_permute(const int32_t *topk_ids, const float *topk_w, int T, int k, int E, int e_begin, int e_end,
                 int32_t *counts, int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
-                const void *x, int x_dtype, int H, void *x_perm, void *stream) {
+                const void *x, int x_dtype, int H, void *x_perm, void *workspace, size_t workspace_bytes,
+                void *stream) {
   if (T < 0 || E < 1 || E > 512 || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
   if (e_begin < 0 || e_end <= e_begin || e_end > E) return MOE_ERR_SHAPE;
   if ((long long)T * k >= (1LL << 31)) return MOE_ERR_SHAPE;
@@ -56,15 +57,23 @@ int moe_permute(const int32_t *topk_ids, const float *topk_w, int T, int k, int 
     if (H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_ALIGN;
   }
-  hipStream_t s = (hipStream_t)stream;
   const int El = e_end - e_begin;
-  hipError_t err = launch_permute(topk_ids, topk_w, T, k, e_begin, El, counts, offsets, row_token, row_w, token_row, s);
+  if (!workspace || workspace_bytes < permute_ws_bytes(T, k, El)) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return MOE_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = launch_permute(topk_ids, topk_w, T, k, e_begin, El, counts, offsets, row_token, row_w, token_row,
+                                  (int32_t *)workspace, s);
   if (err != hipSuccess) return MOE_ERR_HIP;
   if (gather && T > 0) {
     const int R_cap = T * (k < El ? k : El);
     err = launch_gather_rows(x, x_dtype == MOE_BF16 ? 2 : 4, H, offsets, El, row_token, R_cap, x_perm, s);
   }
   return hip_status(err);
+}
+
+size_t moe_permute_workspace_size(int T, int k, int E_loc) {
+  if (T < 0 || k < 1 || E_loc < 1) return 0;
+  return permute_ws_bytes(T, k, E_loc);
 }
 
 size_t moe_ffn_workspace_size(int R_cap, int E_loc, int H, int I, int a_dtype) {

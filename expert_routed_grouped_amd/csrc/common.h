@@ -46,8 +46,10 @@ static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; 
 hipError_t launch_route(const void *x, int x_bf16, const void *w, int w_bf16, const float *bias, int T, int H, int E,
                         int k, int32_t *ids, float *gates, hipStream_t s);
 
+size_t permute_ws_bytes(int T, int k, int El);
 hipError_t launch_permute(const int32_t *ids, const float *w, int T, int k, int lo, int El, int32_t *counts,
-                          int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row, hipStream_t s);
+                          int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row, int32_t *ws,
+                          hipStream_t s);
 
 hipError_t launch_gather_rows(const void *x, int esz, int H, const int32_t *offsets, int El, const int32_t *row_token,
                               int R_cap, void *x_perm, hipStream_t s);

@@ -1,0 +1,215 @@
+// Weight-streaming grouped FFN for small batches (decode).
+//
+// With a few rows per expert the layer is bound by reading each active
+// expert's weights from HBM once (AI-infra book, section 9.3.3: 64 tokens x
+// top-8 touch about 126 of 128 experts, ~4.4 GiB of bf16 weights for 19.3
+// GFLOP; "Hosting Qwen on Blackwell", section "Decoders": small-batch GEMMs are
+// limited by moving weights from HBM to the matrix units).  The design goal is
+// therefore bytes in flight, not reuse:
+//
+//  - no LDS and no barriers: every wave is independent and owns 32 output
+//    columns of one expert (32 gate + 32 up rows for the gate/up half) for up to
+//    64 rows of that expert (two 32-row MFMA blocks);
+//  - the wave streams its weight rows straight from HBM into registers in the
+//    operand layout of v_mfma_f32_32x32x16_bf16.  The contraction index may be
+//    permuted freely as long as both operands use the same permutation, so in
+//    every 64-wide k chunk lane (n, g) reads 64 contiguous bytes of row n at
+//    k-offset 32g and feeds them to four MFMAs; the two lanes of a row cover
+//    one whole 128-byte line.  The activations are read with the same layout
+//    (they are small and stay in L2);
+//  - two chunks are in flight per wave (register double buffering), and many
+//    waves per CU cover the HBM latency.
+//
+// The tile list comes from the same device-side schedule as the tile kernels
+// (64-row M tiles); an expert with more than 64 rows gets more M tiles and its
+// weights are streamed once per M tile, which is still correct.
+#include "ffn_common.h"
+
+namespace {
+
+using ffn::TileParams;
+
+constexpr int SBM = 64;     // rows per M tile
+constexpr int SWAVES = 4;   // waves per block, 32 output columns each
+constexpr int SCOLS = 32 * SWAVES;
+
+// 8 bf16 from 16 bytes of bf16, or from 8 bytes of e4m3.
+template <bool FP8>
+__device__ __forceinline__ bf16x8_t as_operand(const u32x4_t *q, int s) {
+  if constexpr (FP8) {
+    // q[0] holds k 0..15, q[1] k 16..31 of this lane's 32-element slice
+    const u32x4_t v = q[s >> 1];
+    const uint32_t w0 = (s & 1) ? v.z : v.x, w1 = (s & 1) ? v.w : v.y;
+    uint2 a = e4m3x4_to_bf16x4(w0), b = e4m3x4_to_bf16x4(w1);
+    u32x4_t r = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8_t, r);
+  } else {
+    return __builtin_bit_cast(bf16x8_t, q[s]);
+  }
+}
+
+template <int MODE, bool FP8, bool GATHER, bool ATOMIC>
+__global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
+  constexpr int WQ = FP8 ? 2 : 4;  // 16-byte weight loads per lane per 64-wide k chunk
+  const int K = MODE == 0 ? p.H : p.I;
+  const int Ncols = MODE == 0 ? p.I : p.H;
+  const int Nw = MODE == 0 ? 2 * p.I : p.H;
+  const int NT = (Ncols + SCOLS - 1) / SCOLS;
+  int e, nt, r0, rows;
+  if (!ffn::find_tile<SBM>(p, NT, e, nt, r0, rows)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = nt * SCOLS + wave * 32;
+  if (c0 >= Ncols) return;
+  const int n = lane & 31, g = lane >> 5;
+  constexpr int NB = MODE == 0 ? 2 : 1;  // weight row blocks per wave: gate + up, or down
+  const bool two_m = rows > 32;           // wave-uniform
+
+  // weight rows of this lane (k offset 32g inside every 64-wide chunk)
+  const size_t wesz = FP8 ? 1 : 2;
+  const char *wrow[NB];
+  if constexpr (MODE == 0) {
+    wrow[0] = (const char *)p.w + (((size_t)e * Nw + c0 + n) * K + 32 * g) * wesz;
+    wrow[1] = (const char *)p.w + (((size_t)e * Nw + p.I + c0 + n) * K + 32 * g) * wesz;
+  } else {
+    wrow[0] = (const char *)p.w + (((size_t)e * Nw + c0 + n) * K + 32 * g) * wesz;
+  }
+  // activation rows (two 32-row blocks; rows past the end repeat the last valid row)
+  const uint16_t *arow[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; mb++) {
+    const int r = r0 + min(mb * 32 + n, rows - 1);
+    const size_t src = (MODE == 0 && GATHER) ? (size_t)p.row_token[r] : (size_t)r;
+    arow[mb] = (const uint16_t *)p.a + src * K + 32 * g;
+  }
+
+  f32x16_t acc[2][NB];
+#pragma unroll
+  for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[mb][b][r] = 0.0f;
+
+  u32x4_t wq[2][NB][WQ], aq[2][2][4];
+  auto load = [&](int buf, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+#pragma unroll
+      for (int q = 0; q < WQ; q++) wq[buf][b][q] = *(const u32x4_t *)(wrow[b] + (size_t)k0 * wesz + 16 * q);
+#pragma unroll
+    for (int q = 0; q < 4; q++) aq[buf][0][q] = *(const u32x4_t *)(arow[0] + k0 + 8 * q);
+    if (two_m) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) aq[buf][1][q] = *(const u32x4_t *)(arow[1] + k0 + 8 * q);
+    }
+  };
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      bf16x8_t bo[NB];
+#pragma unroll
+      for (int b = 0; b < NB; b++) bo[b] = as_operand<FP8>(wq[buf][b], s);
+      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, aq[buf][0][s]);
+#pragma unroll
+      for (int b = 0; b < NB; b++) acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bo[b], acc[0][b], 0, 0, 0);
+      if (two_m) {
+        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, aq[buf][1][s]);
+#pragma unroll
+        for (int b = 0; b < NB; b++) acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bo[b], acc[1][b], 0, 0, 0);
+      }
+    }
+  };
+
+  const int KC = K / 64;  // K is a multiple of 64
+  load(0, 0);
+  int kc = 0;
+  for (; kc + 2 <= KC; kc += 2) {
+    load(1, (kc + 1) * 64);
+    compute(0);
+    if (kc + 2 < KC) load(0, (kc + 2) * 64);
+    compute(1);
+  }
+  if (kc < KC) compute(0);
+
+  // ---- epilogue: acc[mb][b][r] at lane l is row mb*32 + 8*(r/4) + 4*(l/32) + r%4, column c0 + l%32
+  const int col = c0 + n;
+  if constexpr (MODE == 0) {
+    float sg = 1.0f, su = 1.0f;
+    if constexpr (FP8) {
+      sg = p.scale[(size_t)e * Nw + col];
+      su = p.scale[(size_t)e * Nw + p.I + col];
+    }
+    uint16_t *hout = (uint16_t *)p.out;
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++) {
+      if (mb == 1 && !two_m) break;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (m < rows) {
+          const float gt = acc[mb][0][r] * sg, u = acc[mb][1][r] * su;
+          hout[(size_t)(r0 + m) * p.I + col] = f32_to_bf16(silu_f32(gt) * u);
+        }
+      }
+    }
+  } else {
+    const float sc = FP8 ? p.scale[(size_t)e * Nw + col] : 1.0f;
+    float *out = (float *)p.out;
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++) {
+      if (mb == 1 && !two_m) break;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (m < rows) {
+          const int row = r0 + m;
+          const float o = acc[mb][0][r] * sc;
+          if constexpr (ATOMIC) atomicAdd(out + (size_t)p.row_token[row] * p.H + col, p.row_w[row] * o);
+          else out[(size_t)row * p.H + col] = o;
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, bool FP8, bool GATHER, bool ATOMIC>
+hipError_t launch_s(const TileParams &tp, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((ffn_stream_kernel<MODE, FP8, GATHER, ATOMIC>), dim3(grid), dim3(64 * SWAVES), 0, s, tp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int ffn_stream_bm() { return SBM; }
+
+// Both halves (or one, per ``phase``) of the streaming FFN; the schedule prefix
+// (64-row tiles) must already be in tp.sched.
+hipError_t launch_ffn_stream(const TileParams &base, const FfnArgs &a, hipStream_t s) {
+  hipError_t err = hipSuccess;
+  const long long mt1 = ((long long)a.R_cap + (long long)a.El * (SBM - 1)) / SBM;
+  const long long mt2 = (long long)a.El * ceil_div_i(a.T, SBM);
+  const long long max_mt = mt1 < mt2 ? mt1 : mt2;
+  const bool fp8 = a.w_dt == 2;
+  TileParams tp = base;
+  if (a.phase & 1) {
+    tp.a = a.a;
+    tp.w = a.w_gu;
+    tp.scale = a.s_gu;
+    tp.out = a.h;
+    const int grid = (int)(max_mt * ceil_div_i(a.I, SCOLS));
+    if (fp8) err = a.gather ? launch_s<0, true, true, false>(tp, grid, s) : launch_s<0, true, false, false>(tp, grid, s);
+    else err = a.gather ? launch_s<0, false, true, false>(tp, grid, s) : launch_s<0, false, false, false>(tp, grid, s);
+    if (err != hipSuccess) return err;
+  }
+  if (a.phase & 2) {
+    tp.a = a.h;
+    tp.w = a.w_d;
+    tp.scale = a.s_d;
+    const bool atomic = a.y != nullptr;
+    tp.out = atomic ? (void *)a.y : (void *)a.y_perm;
+    const int grid = (int)(max_mt * ceil_div_i(a.H, SCOLS));
+    if (fp8) err = atomic ? launch_s<1, true, false, true>(tp, grid, s) : launch_s<1, true, false, false>(tp, grid, s);
+    else err = atomic ? launch_s<1, false, false, true>(tp, grid, s) : launch_s<1, false, false, false>(tp, grid, s);
+  }
+  return err;
+}

@@ -7,14 +7,16 @@
 // the per-expert row counts m_j are the AI-infra book's load measure (section
 // 9.4.2) and the padding unit of the grouped GEMM (section 9.4.3).
 //
-// One workgroup of 16 waves does the whole (small) integer problem without any
-// host synchronisation: each wave owns a contiguous slice of the assignments in
-// token-major order.  Pass 1 counts, per wave and expert, with a wave-wide
-// "match" (lanes holding the same expert found with one ballot per expert-id
-// bit) so only one lane per expert touches LDS.  A scan over experts and waves
-// then gives every wave its starting row inside every expert.  Pass 2 repeats
-// the match and hands out rows by lane rank, which keeps the rows of one expert
-// in increasing token order: the unique stable order.
+// No host synchronisation anywhere.  Each wave owns a contiguous slice of the
+// assignments in token-major order.  Pass 1 counts, per wave and expert, with a
+// wave-wide "match" (lanes holding the same expert found with one ballot per
+// expert-id bit) so only one lane per expert touches LDS.  A scan over experts
+// and slices gives every wave its first row inside every expert.  Pass 2
+// repeats the match and hands out rows by lane rank, which keeps the rows of
+// one expert in increasing token order: the unique stable order.  Small
+// batches run in one workgroup of 16 waves; large ones in chunks of 1024
+// assignments (count kernel, one-workgroup scan of the chunk counts, assign
+// kernel), the chunk counts living in the caller's workspace.
 #include "common.h"
 
 namespace {
@@ -36,26 +38,9 @@ __device__ __forceinline__ uint64_t match_lanes(int key, bool active, int nbits)
   return m;
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__restrict__ ids,
-                                                              const float *__restrict__ w, int N, int k, int lo,
-                                                              int El, int nbits, int R_cap,
-                                                              int32_t *__restrict__ counts,
-                                                              int32_t *__restrict__ offsets,
-                                                              int32_t *__restrict__ row_token,
-                                                              float *__restrict__ row_w,
-                                                              int32_t *__restrict__ token_row) {
-  extern __shared__ int smem[];
-  int *cnt = smem;                  // [kPermWaves][El]: per-wave counts, then per-wave next row
-  int *scan = smem + kPermWaves * El;  // [El]
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < kPermWaves * El; i += kPermThreads) cnt[i] = 0;
-  __syncthreads();
-
-  const int per = ((N + kPermThreads - 1) / kPermThreads) * 64;  // multiple of 64
-  const int a0 = min(N, wave * per), a1 = min(N, a0 + per);
-
-  // ---- pass 1: per-wave, per-expert counts
+// Count, per expert, the local assignments a in [a0, a1) of one wave into cnt[] (LDS).
+__device__ __forceinline__ void wave_count(const int32_t *__restrict__ ids, int a0, int a1, int lo, int El, int nbits,
+                                           int *cnt, int lane) {
   for (int base = a0; base < a1; base += 64 * kUnroll) {
     int ev[kUnroll];
 #pragma unroll
@@ -68,49 +53,17 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
       if (base + u * 64 >= a1) break;
       bool local = (unsigned)ev[u] < (unsigned)El;
       uint64_t peers = match_lanes(ev[u], local, nbits);
-      if (local && (peers & lanemask_lt(lane)) == 0) cnt[wave * El + ev[u]] += __popcll(peers);
+      if (local && (peers & lanemask_lt(lane)) == 0) cnt[ev[u]] += __popcll(peers);
     }
   }
-  __syncthreads();
+}
 
-  // ---- scan: offsets over experts, then each wave's first row in each expert
-  for (int e = threadIdx.x; e < El; e += kPermThreads) {
-    int s = 0;
-    for (int v = 0; v < kPermWaves; v++) s += cnt[v * El + e];
-    scan[e] = s;
-    counts[e] = s;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // exclusive scan of scan[0..El) by one wave, 64 experts at a time
-    int carry = 0;
-    for (int b = 0; b < El; b += 64) {
-      int e = b + lane;
-      int v = e < El ? scan[e] : 0;
-      int incl = v;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-      }
-      if (e < El) scan[e] = carry + incl - v;
-      carry += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) offsets[El] = carry;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < El; e += kPermThreads) {
-    int run = scan[e];
-    offsets[e] = run;
-    for (int v = 0; v < kPermWaves; v++) {
-      int c = cnt[v * El + e];
-      cnt[v * El + e] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-
-  // ---- pass 2: rows
+// Give rows to the assignments a in [a0, a1) of one wave, in order; next[e] (LDS)
+// holds this wave's next free row of expert e and is advanced.
+__device__ __forceinline__ void wave_assign(const int32_t *__restrict__ ids, const float *__restrict__ w, int a0,
+                                            int a1, int k, int lo, int El, int nbits, int R_cap, int *next, int lane,
+                                            int32_t *__restrict__ row_token, float *__restrict__ row_w,
+                                            int32_t *__restrict__ token_row) {
   for (int base = a0; base < a1; base += 64 * kUnroll) {
     int ev[kUnroll];
 #pragma unroll
@@ -128,10 +81,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
       int rank = __popcll(peers & lanemask_lt(lane));
       int r = -1;
       if (local) {
-        int slot = wave * El + ev[u];
-        int first = cnt[slot];
+        int first = next[ev[u]];
         r = first + rank;
-        if (rank == 0) cnt[slot] = first + __popcll(peers);
+        if (rank == 0) next[ev[u]] = first + __popcll(peers);
         if (r < R_cap) {  // always true for distinct experts per token; guards bad input
           row_token[r] = a / k;
           row_w[r] = w[a];
@@ -140,6 +92,143 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
       if (valid) token_row[a] = r < R_cap ? r : -1;
     }
   }
+}
+
+// Exclusive scan of v[0..El) in place by one wave; returns the total.
+__device__ __forceinline__ int wave_exclusive_scan(int *v, int El, int lane) {
+  int carry = 0;
+  for (int b = 0; b < El; b += 64) {
+    int e = b + lane;
+    int x = e < El ? v[e] : 0;
+    int incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (e < El) v[e] = carry + incl - x;
+    carry += __shfl(incl, 63, 64);
+  }
+  return carry;
+}
+
+// Small batches: the whole problem in one workgroup of 16 waves.
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__restrict__ ids,
+                                                              const float *__restrict__ w, int N, int k, int lo,
+                                                              int El, int nbits, int R_cap,
+                                                              int32_t *__restrict__ counts,
+                                                              int32_t *__restrict__ offsets,
+                                                              int32_t *__restrict__ row_token,
+                                                              float *__restrict__ row_w,
+                                                              int32_t *__restrict__ token_row) {
+  extern __shared__ int smem[];
+  int *cnt = smem;                     // [kPermWaves][El]: per-wave counts, then per-wave next row
+  int *scan = smem + kPermWaves * El;  // [El]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kPermWaves * El; i += kPermThreads) cnt[i] = 0;
+  __syncthreads();
+  const int per = ((N + kPermThreads - 1) / kPermThreads) * 64;  // multiple of 64
+  const int a0 = min(N, wave * per), a1 = min(N, a0 + per);
+  wave_count(ids, a0, a1, lo, El, nbits, cnt + wave * El, lane);
+  __syncthreads();
+  for (int e = threadIdx.x; e < El; e += kPermThreads) {
+    int s = 0;
+    for (int v = 0; v < kPermWaves; v++) s += cnt[v * El + e];
+    scan[e] = s;
+    counts[e] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int total = wave_exclusive_scan(scan, El, lane);
+    if (lane == 0) offsets[El] = total;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < El; e += kPermThreads) {
+    int run = scan[e];
+    offsets[e] = run;
+    for (int v = 0; v < kPermWaves; v++) {
+      int c = cnt[v * El + e];
+      cnt[v * El + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  wave_assign(ids, w, a0, a1, k, lo, El, nbits, R_cap, cnt + wave * El, lane, row_token, row_w, token_row);
+}
+
+// Large batches: chunks of kChunk assignments, one 4-wave workgroup each.
+constexpr int kChunkWaves = 4;
+constexpr int kChunk = kChunkWaves * 64 * kUnroll / 2;  // 1024 assignments, 256 per wave
+
+// Pass 1: per-chunk, per-expert counts -> cc[chunk][El].
+__global__ __launch_bounds__(kChunkWaves * 64) void chunk_count_kernel(const int32_t *__restrict__ ids, int N, int lo,
+                                                                       int El, int nbits, int32_t *__restrict__ cc) {
+  extern __shared__ int smem[];  // [kChunkWaves][El]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kChunkWaves * El; i += blockDim.x) smem[i] = 0;
+  __syncthreads();
+  const int a0 = min(N, blockIdx.x * kChunk + wave * (kChunk / kChunkWaves));
+  const int a1 = min(N, a0 + kChunk / kChunkWaves);
+  wave_count(ids, a0, a1, lo, El, nbits, smem + wave * El, lane);
+  __syncthreads();
+  for (int e = threadIdx.x; e < El; e += blockDim.x) {
+    int s = 0;
+    for (int v = 0; v < kChunkWaves; v++) s += smem[v * El + e];
+    cc[(size_t)blockIdx.x * El + e] = s;
+  }
+}
+
+// Pass 2 (one workgroup): counts and offsets from the chunk counts (read only).
+__global__ __launch_bounds__(512) void chunk_scan_kernel(const int32_t *__restrict__ cc, int nchunks, int El,
+                                                         int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
+  extern __shared__ int smem[];  // [El]
+  for (int e = threadIdx.x; e < El; e += blockDim.x) {
+    int run = 0;
+#pragma unroll 8
+    for (int c = 0; c < nchunks; c++) run += cc[(size_t)c * El + e];
+    smem[e] = run;
+    counts[e] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int total = wave_exclusive_scan(smem, El, threadIdx.x);
+    if (threadIdx.x == 0) offsets[El] = total;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < El; e += blockDim.x) offsets[e] = smem[e];
+}
+
+// Pass 3: rows of each chunk, starting from its bases.
+__global__ __launch_bounds__(kChunkWaves * 64) void chunk_assign_kernel(const int32_t *__restrict__ ids,
+                                                                        const float *__restrict__ w, int N, int k,
+                                                                        int lo, int El, int nbits, int R_cap,
+                                                                        const int32_t *__restrict__ cc,
+                                                                        const int32_t *__restrict__ offsets,
+                                                                        int32_t *__restrict__ row_token,
+                                                                        float *__restrict__ row_w,
+                                                                        int32_t *__restrict__ token_row) {
+  extern __shared__ int smem[];  // [kChunkWaves][El]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kChunkWaves * El; i += blockDim.x) smem[i] = 0;
+  __syncthreads();
+  const int a0 = min(N, blockIdx.x * kChunk + wave * (kChunk / kChunkWaves));
+  const int a1 = min(N, a0 + kChunk / kChunkWaves);
+  wave_count(ids, a0, a1, lo, El, nbits, smem + wave * El, lane);
+  __syncthreads();
+  // first row of expert e in this chunk: offsets[e] + the counts of the chunks before it
+  for (int e = threadIdx.x; e < El; e += blockDim.x) {
+    int run = offsets[e];
+#pragma unroll 8
+    for (int c = 0; c < (int)blockIdx.x; c++) run += cc[(size_t)c * El + e];
+    for (int v = 0; v < kChunkWaves; v++) {
+      int c = smem[v * El + e];
+      smem[v * El + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  wave_assign(ids, w, a0, a1, k, lo, El, nbits, R_cap, smem + wave * El, lane, row_token, row_w, token_row);
 }
 
 // x_perm[r] = x[row_token[r]] for r < offsets[El]; 16-byte vectors.
@@ -157,14 +246,35 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restric
 
 }  // namespace
 
+size_t permute_ws_bytes(int T, int k, int El) {
+  const long long N = (long long)T * k;
+  const long long nchunks = (N + kChunk - 1) / kChunk;
+  return align_up(sizeof(int32_t) * (size_t)(nchunks > 0 ? nchunks : 1) * (size_t)El, 256);
+}
+
 hipError_t launch_permute(const int32_t *ids, const float *w, int T, int k, int lo, int El, int32_t *counts,
-                          int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row, hipStream_t s) {
+                          int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row, int32_t *ws,
+                          hipStream_t s) {
   int nbits = 0;
   while ((1 << nbits) < El) nbits++;
-  size_t shm = sizeof(int) * (size_t)(kPermWaves + 1) * El;
+  const int N = T * k;
   const int R_cap = T * (k < El ? k : El);
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), shm, s, ids, w, T * k, k, lo, El, nbits, R_cap,
-                     counts, offsets, row_token, row_w, token_row);
+  if (N <= 8192) {
+    size_t shm = sizeof(int) * (size_t)(kPermWaves + 1) * El;
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), shm, s, ids, w, N, k, lo, El, nbits, R_cap,
+                       counts, offsets, row_token, row_w, token_row);
+    return hipGetLastError();
+  }
+  const int nchunks = (N + kChunk - 1) / kChunk;
+  const size_t shm = sizeof(int) * (size_t)kChunkWaves * El;
+  hipLaunchKernelGGL(chunk_count_kernel, dim3(nchunks), dim3(kChunkWaves * 64), shm, s, ids, N, lo, El, nbits, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(512), sizeof(int) * (size_t)El, s, ws, nchunks, El, counts,
+                     offsets);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(chunk_assign_kernel, dim3(nchunks), dim3(kChunkWaves * 64), shm, s, ids, w, N, k, lo, El, nbits,
+                     R_cap, ws, offsets, row_token, row_w, token_row);
   return hipGetLastError();
 }
 

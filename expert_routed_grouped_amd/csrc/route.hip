@@ -79,19 +79,74 @@ __global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__
     xrow[tt] = (const char *)x + (size_t)t * H * esz_x;
   }
   const char *wrow = (const char *)w + (size_t)(ev ? e : 0) * H * esz_w;
+  // VEC: the block's activation rows, staged once in LDS as fp32 ([TT][H], dynamic size)
+  extern __shared__ __attribute__((aligned(16))) float xs[];
+  if constexpr (VEC) {
+    const int rp = H / 8;
+    for (int i = threadIdx.x; i < TT * rp; i += blockDim.x) {
+      const int tt = i / rp, hp = i - tt * rp;
+      float f[8];
+      load8<XB>(xrow[tt] + (size_t)hp * 8 * esz_x, f);
+      *(f32x4_t *)(xs + tt * H + hp * 8) = f32x4_t{f[0], f[1], f[2], f[3]};
+      *(f32x4_t *)(xs + tt * H + hp * 8 + 4) = f32x4_t{f[4], f[5], f[6], f[7]};
+    }
+    __syncthreads();
+  }
 
   float acc[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; tt++) acc[tt] = 0.0f;
 
   if constexpr (VEC) {
-    for (int h = 0; h < H; h += 8) {
+    // 32 h per step; two register sets alternate so the weight pieces of step
+    // s+1 are in flight while step s computes
+    constexpr int HS = 32, P = HS * (WB ? 2 : 4) / 16;
+    const int nsteps = H / HS;
+    u32x4_t b0[P], b1[P];
+    auto wload = [&](u32x4_t(&b)[P], int st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < P; q++) b[q] = *(const u32x4_t *)(wrow + (size_t)st * HS * esz_w + 16 * q);
+    };
+    auto wstep = [&](const u32x4_t(&b)[P], int st) __attribute__((always_inline)) {
+      const int h = st * HS;
+#pragma unroll
+      for (int g = 0; g < HS / 8; g++) {
+        float wf[8];
+        if constexpr (WB) {
+          const u32x4_t v = b[g];
+          wf[0] = bf16_lo(v.x); wf[1] = bf16_hi(v.x); wf[2] = bf16_lo(v.y); wf[3] = bf16_hi(v.y);
+          wf[4] = bf16_lo(v.z); wf[5] = bf16_hi(v.z); wf[6] = bf16_lo(v.w); wf[7] = bf16_hi(v.w);
+        } else {
+          const u32x4_t v0 = b[2 * g], v1 = b[2 * g + 1];
+          wf[0] = __uint_as_float(v0.x); wf[1] = __uint_as_float(v0.y); wf[2] = __uint_as_float(v0.z);
+          wf[3] = __uint_as_float(v0.w); wf[4] = __uint_as_float(v1.x); wf[5] = __uint_as_float(v1.y);
+          wf[6] = __uint_as_float(v1.z); wf[7] = __uint_as_float(v1.w);
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT; tt++) {  // same LDS address in every lane: broadcast
+          const f32x4_t xa = *(const f32x4_t *)(xs + tt * H + h + 8 * g);
+          const f32x4_t xb = *(const f32x4_t *)(xs + tt * H + h + 8 * g + 4);
+          const float xf[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+#pragma unroll
+          for (int j = 0; j < 8; j++) acc[tt] = __builtin_fmaf(xf[j], wf[j], acc[tt]);
+        }
+      }
+    };
+    if (nsteps > 0) wload(b0, 0);
+    for (int st = 0; st < nsteps; st += 2) {
+      if (st + 1 < nsteps) wload(b1, st + 1);
+      wstep(b0, st);
+      if (st + 1 >= nsteps) break;
+      if (st + 2 < nsteps) wload(b0, st + 2);
+      wstep(b1, st + 1);
+    }
+    for (int h = nsteps * HS; h < H; h += 8) {
       float wf[8];
       load8<WB>(wrow + (size_t)h * esz_w, wf);
 #pragma unroll
       for (int tt = 0; tt < TT; tt++) {
-        float xf[8];
-        load8<XB>(xrow[tt] + (size_t)h * esz_x, xf);
+        const float *xp = xs + tt * H + h;
+        const float xf[8] = {xp[0], xp[1], xp[2], xp[3], xp[4], xp[5], xp[6], xp[7]};
 #pragma unroll
         for (int j = 0; j < 8; j++) acc[tt] = __builtin_fmaf(xf[j], wf[j], acc[tt]);
       }
@@ -146,14 +201,164 @@ __global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__
   }
 }
 
+// Top-k + gates of one token from its logits in LDS (wave-wide; every lane of the
+// wave takes part).  Lanes own experts lane + 64q.
+template <int EC>
+__device__ __forceinline__ void topk_token(const float *lgt, int E, int k, int lane, int32_t *ids_t, float *gates_t) {
+  uint64_t key[EC];
+#pragma unroll
+  for (int q = 0; q < EC; q++) {
+    int eq = q * 64 + lane;
+    key[q] = eq < E ? (((uint64_t)ord_key(lgt[eq]) << 32) | (uint32_t)~(uint32_t)eq) : 0ull;
+  }
+  float my_v = 0.0f, m = 0.0f;
+  int my_e = 0;
+  for (int j = 0; j < k; j++) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int q = 1; q < EC; q++) best = key[q] > best ? key[q] : best;
+    best = wave_max_u64(best);
+    const int es = (int)~(uint32_t)best;
+    const float vs = ord_val((uint32_t)(best >> 32));
+#pragma unroll
+    for (int q = 0; q < EC; q++)
+      if (q * 64 + lane == es) key[q] = 0ull;
+    if (j == 0) m = vs;
+    if (lane == j) { my_v = vs; my_e = es; }
+  }
+  float u = lane < k ? expf(my_v - m) : 0.0f;
+  float sum = wave_sum_f32(u);
+  if (lane < k) {
+    ids_t[lane] = my_e;
+    gates_t[lane] = u / sum;
+  }
+}
+
+// Many tokens: the router weight and the workgroup's activations are staged
+// through LDS in 64-wide h chunks, converted to fp32 once per workgroup (the
+// next chunk is in registers while this one computes).  Every wave owns TR
+// tokens, whose activations every lane reads at the same LDS address
+// (broadcast), and every lane the experts lane + 64c.  The chain for each
+// (token, expert) still runs h = 0, 1, 2, ... in order.  Needs H % 64 == 0.
+template <int TR, int EC, bool XB, bool WB>
+__global__ __launch_bounds__(256) void route_staged_kernel(const void *__restrict__ x, const void *__restrict__ w,
+                                                           const float *__restrict__ bias, int T, int H, int E, int k,
+                                                           int32_t *__restrict__ ids, float *__restrict__ gates) {
+  constexpr int NW = 4, TB = NW * TR, HC = 64;
+  constexpr int ROWS = 64 * EC;
+  constexpr int LROW = HC + 4;                  // fp32 row stride in LDS (pad: conflict-free 16-byte reads)
+  constexpr int WESZ = WB ? 2 : 4;
+  constexpr int PIECES = ROWS * HC * WESZ / 16; // 16-byte global pieces per chunk
+  constexpr int PPT = PIECES / 256;
+  constexpr int PPR = HC * WESZ / 16;           // pieces per row
+  __shared__ __attribute__((aligned(16))) float wl[ROWS * LROW];
+  __shared__ __attribute__((aligned(16))) float xl[TB][LROW];  // this chunk of the block's activations, fp32
+  __shared__ float lg[TB][ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int XESZ = XB ? 2 : 4;
+  constexpr int XPR = HC * XESZ / 16;   // 16-byte activation pieces per token row and chunk
+  static_assert(TB * XPR <= 256, "one activation piece per thread");
+  // activation piece of this thread (threads past TB*XPR have none)
+  const bool xhas = tid < TB * XPR;
+  const int xr = xhas ? tid / XPR : 0, xc = xhas ? tid % XPR : 0;
+  const char *xsrc = (const char *)x + (size_t)min(blockIdx.x * TB + xr, T - 1) * H * XESZ + xc * 16;
+  // staging pieces of this thread
+  const char *src[PPT];
+  int dst[PPT];
+#pragma unroll
+  for (int q = 0; q < PPT; q++) {
+    const int pc = tid + 256 * q, row = pc / PPR, col = pc % PPR;
+    const int er = row < E ? row : 0;
+    src[q] = (const char *)w + ((size_t)er * H) * WESZ + col * 16;
+    dst[q] = row * LROW + col * (16 / WESZ);
+  }
+  float acc[TR][EC];
+#pragma unroll
+  for (int t = 0; t < TR; t++)
+#pragma unroll
+    for (int c = 0; c < EC; c++) acc[t][c] = 0.0f;
+
+  u32x4_t pre[PPT], xpre = {0, 0, 0, 0};
+#pragma unroll
+  for (int q = 0; q < PPT; q++) pre[q] = *(const u32x4_t *)src[q];
+  if (xhas) xpre = *(const u32x4_t *)xsrc;
+  for (int h0 = 0; h0 < H; h0 += HC) {
+    // registers -> LDS as fp32
+    if (xhas) {
+      if constexpr (XB) {
+        f32x4_t lo = {bf16_lo(xpre.x), bf16_hi(xpre.x), bf16_lo(xpre.y), bf16_hi(xpre.y)};
+        f32x4_t hi = {bf16_lo(xpre.z), bf16_hi(xpre.z), bf16_lo(xpre.w), bf16_hi(xpre.w)};
+        *(f32x4_t *)(&xl[xr][xc * 8]) = lo;
+        *(f32x4_t *)(&xl[xr][xc * 8 + 4]) = hi;
+      } else {
+        *(u32x4_t *)(&xl[xr][xc * 4]) = xpre;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PPT; q++) {
+      if constexpr (WB) {
+        const u32x4_t v = pre[q];
+        f32x4_t lo = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+        f32x4_t hi = {bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        *(f32x4_t *)(wl + dst[q]) = lo;
+        *(f32x4_t *)(wl + dst[q] + 4) = hi;
+      } else {
+        *(u32x4_t *)(wl + dst[q]) = pre[q];
+      }
+    }
+    __syncthreads();
+    if (h0 + HC < H) {
+#pragma unroll
+      for (int q = 0; q < PPT; q++) pre[q] = *(const u32x4_t *)(src[q] + (size_t)(h0 + HC) * WESZ);
+      if (xhas) xpre = *(const u32x4_t *)(xsrc + (size_t)(h0 + HC) * XESZ);
+    }
+#pragma unroll 2
+    for (int hh = 0; hh < HC; hh += 8) {
+      float xf[TR][8];
+#pragma unroll
+      for (int t = 0; t < TR; t++) {  // same address in every lane: broadcast reads
+        const f32x4_t a = *(const f32x4_t *)(&xl[wave * TR + t][hh]), b = *(const f32x4_t *)(&xl[wave * TR + t][hh + 4]);
+        xf[t][0] = a[0]; xf[t][1] = a[1]; xf[t][2] = a[2]; xf[t][3] = a[3];
+        xf[t][4] = b[0]; xf[t][5] = b[1]; xf[t][6] = b[2]; xf[t][7] = b[3];
+      }
+#pragma unroll
+      for (int c = 0; c < EC; c++) {
+        const float *wr = wl + (lane + 64 * c) * LROW + hh;
+        const f32x4_t w0 = *(const f32x4_t *)wr, w1 = *(const f32x4_t *)(wr + 4);
+        const float wf[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+        for (int t = 0; t < TR; t++)
+#pragma unroll
+          for (int j = 0; j < 8; j++) acc[t][c] = __builtin_fmaf(xf[t][j], wf[j], acc[t][c]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int c = 0; c < EC; c++) {
+    const int e = lane + 64 * c;
+    const float b = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < TR; t++) lg[wave * TR + t][e] = bias != nullptr ? acc[t][c] + b : acc[t][c];
+  }
+  __syncthreads();
+  for (int tt = wave; tt < TB; tt += NW) {
+    const int t = blockIdx.x * TB + tt;
+    if (t >= T) break;
+    topk_token<EC>(lg[tt], E, k, lane, ids + (size_t)t * k, gates + (size_t)t * k);
+  }
+}
+
 template <int TT, int EC>
 hipError_t launch_tt(const void *x, int xb, const void *w, int wb, const float *bias, int T, int H, int E, int k,
                      int32_t *ids, float *gates, hipStream_t s) {
   dim3 grid(ceil_div_i(T, TT)), block(64 * EC);
-  bool vec = (H % 8 == 0) && (((uintptr_t)x | (uintptr_t)w) % 16 == 0);
+  const size_t xs_bytes = sizeof(float) * (size_t)TT * H;
+  const bool vec = (H % 8 == 0) && (((uintptr_t)x | (uintptr_t)w) % 16 == 0) && xs_bytes <= 65536;
+  const size_t shm = vec ? xs_bytes : 0;
 #define ROUTE_CASE(XB, WB, V)                                                                                 \
   if (xb == XB && wb == WB && vec == V) {                                                                   \
-    hipLaunchKernelGGL((route_kernel<TT, EC, XB, WB, V>), grid, block, 0, s, x, w, bias, T, H, E, k, ids, gates); \
+    hipLaunchKernelGGL((route_kernel<TT, EC, XB, WB, V>), grid, block, shm, s, x, w, bias, T, H, E, k, ids, gates); \
     return hipGetLastError();                                                                               \
   }
   ROUTE_CASE(true, true, true) ROUTE_CASE(true, true, false) ROUTE_CASE(false, false, true)
@@ -163,11 +368,35 @@ hipError_t launch_tt(const void *x, int xb, const void *w, int wb, const float *
   return hipErrorInvalidValue;
 }
 
+#ifndef ROUTE_TR
+#define ROUTE_TR 3
+#endif
+
+template <int EC>
+hipError_t launch_staged(const void *x, int xb, const void *w, int wb, const float *bias, int T, int H, int E, int k,
+                         int32_t *ids, float *gates, hipStream_t s) {
+  constexpr int TB = 4 * ROUTE_TR;
+  dim3 grid(ceil_div_i(T, TB)), block(256);
+#define STAGED_CASE(XB, WB)                                                                                      \
+  if (xb == XB && wb == WB) {                                                                                  \
+    hipLaunchKernelGGL((route_staged_kernel<ROUTE_TR, EC, XB, WB>), grid, block, 0, s, x, w, bias, T, H, E, k, ids, \
+                       gates);                                                                                 \
+    return hipGetLastError();                                                                                  \
+  }
+  STAGED_CASE(true, true) STAGED_CASE(false, false) STAGED_CASE(true, false) STAGED_CASE(false, true)
+#undef STAGED_CASE
+  return hipErrorInvalidValue;
+}
+
 template <int EC>
 hipError_t launch_ec(const void *x, int xb, const void *w, int wb, const float *bias, int T, int H, int E, int k,
                      int32_t *ids, float *gates, hipStream_t s) {
-  // Few tokens: one token per block keeps every chain on its own wave (latency);
-  // many tokens: four tokens per block amortise the weight loads.
+  // Few tokens: one token per block keeps every chain on its own wave (latency).
+  // Many tokens: the LDS-staged kernel shares each weight chunk among 4*TR tokens.
+  const bool aligned = (((uintptr_t)x | (uintptr_t)w) % 16 == 0);
+  if constexpr (EC <= 2) {
+    if (T > 256 && H % 64 == 0 && aligned) return launch_staged<EC>(x, xb, w, wb, bias, T, H, E, k, ids, gates, s);
+  }
   if (T <= 512) return launch_tt<1, EC>(x, xb, w, wb, bias, T, H, E, k, ids, gates, s);
   return launch_tt<4, EC>(x, xb, w, wb, bias, T, H, E, k, ids, gates, s);
 }

@@ -57,7 +57,9 @@ class LayerBuffers:
                          offsets=torch.empty(El + 1, dtype=torch.int32, **d),
                          row_token=torch.empty(max(self.R_cap, 1), dtype=torch.int32, **d),
                          row_w=torch.empty(max(self.R_cap, 1), dtype=torch.float32, **d),
-                         token_row=torch.empty((T, k), dtype=torch.int32, **d))
+                         token_row=torch.empty((T, k), dtype=torch.int32, **d),
+                         workspace=torch.empty(max(moe.moe_permute_workspace_size(T, k, El), 256), dtype=torch.uint8,
+                                               **d))
         adt = moe.MOE_F32 if cfg.act == "f32" else moe.MOE_BF16
         self.workspace = torch.empty(moe.moe_ffn_workspace_size(self.R_cap, El, H, I, adt), dtype=torch.uint8, **d)
         self.y = torch.empty((T, H), dtype=torch.float32, **d)

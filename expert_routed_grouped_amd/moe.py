@@ -22,8 +22,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTY
           -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIGN"}
 
 # Every symbol moe.h declares (checked by the CPU test suite).
-EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_ffn_workspace_size",
-           "moe_grouped_ffn", "moe_combine")
+EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_permute_workspace_size",
+           "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine")
 
 
 class MoEError(RuntimeError):
@@ -50,7 +50,9 @@ def lib():
         L.moe_route.restype = I
         L.moe_route.argtypes = [P, I, P, I, P, I, I, I, I, P, P, P]
         L.moe_permute.restype = I
-        L.moe_permute.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, I, I, P, P]
+        L.moe_permute.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, I, I, P, P, Z, P]
+        L.moe_permute_workspace_size.restype = Z
+        L.moe_permute_workspace_size.argtypes = [I, I, I]
         L.moe_ffn_workspace_size.restype = Z
         L.moe_ffn_workspace_size.argtypes = [I, I, I, I, I]
         L.moe_grouped_ffn.restype = I
@@ -125,6 +127,7 @@ def moe_permute(topk_ids: torch.Tensor, topk_w: torch.Tensor, E: int, e_begin: i
     o.setdefault("row_token", torch.empty(max(R_cap, 1), dtype=torch.int32, device=dev))
     o.setdefault("row_w", torch.empty(max(R_cap, 1), dtype=torch.float32, device=dev))
     o.setdefault("token_row", torch.empty((T, k), dtype=torch.int32, device=dev))
+    o.setdefault("workspace", torch.empty(max(moe_permute_workspace_size(T, k, El), 256), dtype=torch.uint8, device=dev))
     H = 0
     xdt = MOE_BF16
     if x is not None:
@@ -136,9 +139,14 @@ def moe_permute(topk_ids: torch.Tensor, topk_w: torch.Tensor, E: int, e_begin: i
     _check("moe_permute", lib().moe_permute(_ptr(topk_ids), _ptr(topk_w), T, k, E, e_begin, e_end,
                                             _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["row_token"]),
                                             _ptr(o["row_w"]), _ptr(o["token_row"]), _ptr(x), xdt, H,
-                                            _ptr(x_perm), _stream(stream)))
+                                            _ptr(x_perm), _ptr(o["workspace"]),
+                                            o["workspace"].numel() * o["workspace"].element_size(), _stream(stream)))
     o["R_cap"] = R_cap
     return o
+
+
+def moe_permute_workspace_size(T: int, k: int, E_loc: int) -> int:
+    return int(lib().moe_permute_workspace_size(T, k, E_loc))
 
 
 def moe_ffn_workspace_size(R_cap: int, E_loc: int, H: int, I: int, a_dtype: int) -> int:

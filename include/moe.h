@@ -128,13 +128,19 @@ int moe_route(const void *x, int x_dtype, const void *w_router, int w_dtype, con
  * row_w [R_cap] fp32 (only the first R entries are written); token_row [T,k]
  * int32; x [T,H] and x_perm [R_cap,H] of element type x_dtype (MOE_F32 or
  * MOE_BF16), 16-byte aligned, H a multiple of 8.  topk_ids must hold distinct
- * experts per token in [0, E) (as moe_route writes them).
+ * experts per token in [0, E) (as moe_route writes them).  workspace: at least
+ * moe_permute_workspace_size(T, k, E_loc) bytes, 256-byte aligned.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (0 <= e_begin < e_end <= E, E <= 512,
- * 1 <= k <= min(E,32), T*k < 2^31), MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ * 1 <= k <= min(E,32), T*k < 2^31), MOE_ERR_DTYPE, MOE_ERR_ALIGN,
+ * MOE_ERR_WORKSPACE, MOE_ERR_HIP.
  */
 int moe_permute(const int32_t *topk_ids, const float *topk_w, int T, int k, int E, int e_begin, int e_end,
                 int32_t *counts, int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
-                const void *x, int x_dtype, int H, void *x_perm, void *stream);
+                const void *x, int x_dtype, int H, void *x_perm, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* Bytes of workspace moe_permute needs (per-chunk expert counts of large batches). */
+size_t moe_permute_workspace_size(int T, int k, int E_loc);
 
 /*
  * Bytes of workspace moe_grouped_ffn needs (the intermediate h [R_cap, I] plus

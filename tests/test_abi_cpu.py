@@ -57,17 +57,17 @@ def test_route_validation(kw, code):
 
 def permute(**kw):
     a = dict(ids=FAKE, w=FAKE, T=4, k=2, E=8, lo=0, hi=8, c=FAKE, o=FAKE, rt=FAKE, rw=FAKE, tr=FAKE, x=None, xd=1,
-             H=0, xp=None)
+             H=0, xp=None, ws=FAKE, wsb=1 << 20)
     a.update(kw)
     return moe.lib().moe_permute(a["ids"], a["w"], a["T"], a["k"], a["E"], a["lo"], a["hi"], a["c"], a["o"], a["rt"],
-                                 a["rw"], a["tr"], a["x"], a["xd"], a["H"], a["xp"], None)
+                                 a["rw"], a["tr"], a["x"], a["xd"], a["H"], a["xp"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(lo=3, hi=3), -2), (dict(lo=-1), -2), (dict(hi=9), -2), (dict(k=9), -2), (dict(E=600, hi=600), -2),
     (dict(c=None), -1), (dict(rt=None), -1), (dict(x=FAKE), -1), (dict(xp=FAKE), -1),
     (dict(x=FAKE, xp=FAKE, H=12), -2), (dict(x=FAKE, xp=FAKE, H=64, xd=2), -3),
-    (dict(x=FAKE_ODD, xp=FAKE, H=64), -6),
+    (dict(x=FAKE_ODD, xp=FAKE, H=64), -6), (dict(ws=None), -4), (dict(wsb=0), -4), (dict(ws=P(0x1010)), -6),
 ])
 def test_permute_validation(kw, code):
     assert permute(**kw) == code
@@ -94,6 +94,9 @@ def test_ffn_validation(kw, code):
 
 def test_workspace_size():
     L = moe.lib()
+    # per-chunk (1024 assignments) expert counts
+    assert L.moe_permute_workspace_size(6000, 8, 128) >= 47 * 128 * 4
+    assert L.moe_permute_workspace_size(0, 8, 128) > 0
     # h [R_cap, I] bf16 plus an aligned schedule prefix
     ws = L.moe_ffn_workspace_size(48000, 128, 4096, 1536, 1)
     assert ws >= 48000 * 1536 * 2 and ws % 256 == 0

@@ -229,6 +229,12 @@ FFN_CASES = [
     CONFIGS["tiny"],
     LayerConfig("ffn_f32_local", T=200, H=128, E=8, k=2, I=64, act="f32", wdt="f32", e_begin=2, e_end=6,
                 init="fan_in", seed=206),
+    # few rows per expert: the weight-streaming kernels (column tails in both halves)
+    LayerConfig("stream_bf16", T=64, H=320, E=32, k=4, I=192, seed=207, w_std=0.05),
+    LayerConfig("stream_fp8_local", T=48, H=256, E=16, k=4, I=128, wdt="fp8", e_begin=4, e_end=12, seed=208,
+                w_std=0.05),
+    # one hot expert with more than 64 rows: several 64-row tiles and both 32-row blocks
+    LayerConfig("stream_hot", T=120, H=256, E=16, k=2, I=128, bias="zipf", seed=209, w_std=0.05),
 ]
 
 
