@@ -44,32 +44,83 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-sample", type=int, default=16, help="tokens of the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(inp, cfg, n_tok):
-    """The oracle as it stands, on the first n_tok tokens: route, permute, token-major FFN + combine."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from a committed counter summary, or None when there is none or the kernel's
+    sources changed since the counters were taken (the summary records their SHA-256)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    try:
+        h = hashlib.sha256()
+        for src in fields["kernel_sources"].split():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != fields["source_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain copy of known size: the profiler's FETCH_SIZE / WRITE_SIZE for it calibrate those counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(inp, cfg, seconds):
+    """The oracle as it stands on a bounded sample of the same workload: whole-layer passes (route,
+    permute, token-major SwiGLU FFN + combine) over consecutive 64-token chunks of the batch, wrapping
+    around, until ``seconds`` of wall time have been spent (at least one chunk)."""
     from oracle import oracle as O
-    n = min(n_tok, cfg.T)
-    x = np.ascontiguousarray(inp["x"][:n])
+    chunk = min(64, cfg.T)
+    done = 0
     t0 = time.perf_counter()
-    ids, w, _ = O.route(x, inp["w_router"], inp["bias"], cfg.k)
-    O.permute(ids, w, cfg.lo, cfg.hi)
-    O.layer_tokens(np.arange(n), x, ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"], inp["s_gate_up"],
-                   inp["s_down"], round_h=cfg.act != "f32")
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"first {n} of {cfg.T} tokens of the same workload, whole layer (route, permute, "
-                      f"token-major SwiGLU FFN + combine), {dt:.2f} s"}
+    while True:
+        lo = done % cfg.T
+        sl = slice(lo, min(lo + chunk, cfg.T))
+        x = np.ascontiguousarray(inp["x"][sl])
+        ids, w, _ = O.route(x, inp["w_router"], inp["bias"], cfg.k)
+        O.permute(ids, w, cfg.lo, cfg.hi)
+        O.layer_tokens(np.arange(x.shape[0]), x, ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"],
+                       inp["s_gate_up"], inp["s_down"], round_h=cfg.act != "f32")
+        done += x.shape[0]
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    return {"value": done / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{done} tokens in {chunk}-token chunks of the same {cfg.T}-token batch (wrapping around), "
+                      f"whole layer per chunk (route, permute, token-major SwiGLU FFN + combine), {dt:.1f} s"}
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
-              "see DESIGN.md for how the layer would shard.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the layer has no multi-GPU path here.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     from expert_routed_grouped_amd import accounting as A
@@ -144,7 +195,10 @@ def main():
         achieved = gu_flops / gu_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    roof.update({"kernel": "ffn_tile_kernel<gate_up> (+ its schedule kernel)", "avg_ms": round(float(np.mean(gu_ms)), 4),
+    kernel = ("ffn_stream_kernel" if bufs.R_cap <= 48 * cfg.E_loc else
+              ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel"))
+    roof["traffic"] = measured_traffic(kernel, args.config)
+    roof.update({"kernel": f"{kernel} (gate/up + SwiGLU half, one launch)", "avg_ms": round(float(np.mean(gu_ms)), 4),
                  "algorithmic_per_launch": gu_bytes if args.config == "decode" else gu_flops})
     layer_s = ms_per_step * 1e-3
     res = {
@@ -176,7 +230,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_sample)
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -80,7 +80,7 @@ size_t moe_ffn_workspace_size(int R_cap, int E_loc, int H, int I, int a_dtype) {
   (void)H;
   if (R_cap < 0 || E_loc < 1 || I < 1) return 0;
   const size_t esz = a_dtype == MOE_F32 ? 4 : 2;
-  return ffn_sched_bytes(E_loc) + align_up((size_t)R_cap * (size_t)I * esz, 256);
+  return align_up((size_t)R_cap * (size_t)I * esz, 256);
 }
 
 int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const int32_t *row_token, const float *row_w,
@@ -130,8 +130,7 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
   fa.s_d = s_down;
   fa.y = y;
   fa.y_perm = y_perm;
-  fa.sched = (int32_t *)workspace;
-  fa.h = (char *)workspace + ffn_sched_bytes(E_loc);
+  fa.h = workspace;
   fa.phase = only == MOE_FFN_ONLY_GATE_UP ? 1 : (only == MOE_FFN_ONLY_DOWN ? 2 : 3);
   return hip_status(launch_ffn(fa, s));
 }

@@ -59,8 +59,7 @@ hipError_t launch_combine(const float *y_perm, const int32_t *token_row, const f
 
 hipError_t launch_zero_f32(float *p, size_t n, hipStream_t s);
 
-// Grouped FFN.  ``sched`` is device scratch of at least ffn_sched_bytes(El) bytes,
-// ``h`` is the intermediate [R_cap, I] (bf16 or fp32 by path).
+// Grouped FFN.  ``h`` is the intermediate [R_cap, I] (bf16 or fp32 by path).
 struct FfnArgs {
   const void *a;          // x [T,H] (gather) or x_perm [R_cap,H]
   int a_bf16;             // 1: bf16 activations, 0: fp32
@@ -76,9 +75,7 @@ struct FfnArgs {
   float *y;               // fused combine target (atomic) or NULL
   float *y_perm;          // per-row outputs when y == NULL
   void *h;                // intermediate
-  int32_t *sched;         // scheduling scratch
   int phase;              // bit 0: gate/up half, bit 1: down half
 };
 
-size_t ffn_sched_bytes(int El);
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t s);

@@ -6,24 +6,26 @@
 // of section 9.3.2 and the weighted combine of "Hosting Qwen on Blackwell",
 // section "MoE Dispatch - Combine", fused into the down-projection epilogue.
 //
-// Work is cut into tiles of BM rows of one expert x BN output columns.  The
-// tile list is never sent to the host: a one-workgroup schedule kernel turns
-// the per-expert row counts into a prefix of M-tiles, and every GEMM workgroup
-// finds its (expert, N-tile, M-tile) by a binary search of that prefix.  The
-// grid is sized for the worst case the host can bound (R_cap rows) and surplus
-// workgroups exit at once; experts without rows get no tile and their weights
-// are never read.  Consecutive tile numbers walk the M-tiles of one (expert,
-// N-tile) first and are kept on one XCD, so the weight tile those M-tiles share
-// is fetched from HBM about once and served from that XCD's L2 afterwards.
+// Work is cut into tiles of rows of one expert x output columns.  The tile
+// list is never sent to the host: every workgroup finds its (expert, N tile,
+// M tile) from the expert offsets on the device (a wave-wide prefix over the
+// experts' M-tile counts).  The grid is sized for the worst case the host can
+// bound (R_cap rows) and surplus workgroups exit at once; experts without rows
+// get no tile and their weights are never read.  Consecutive tile numbers walk
+// the M tiles of one (expert, N tile) first and are kept on one XCD, so the
+// weight tile those M tiles share is fetched from HBM about once and served
+// from that XCD's L2 afterwards.
 //
-// Inside a tile: bf16 operands are staged through LDS (global -> registers ->
-// LDS, two LDS stages, one barrier per K step) in rows of 64 k-elements with
-// the 16-byte chunks XOR-swizzled by row, so the 16-byte MFMA operand reads of
-// a wave hit distinct banks.  fp8 e4m3 weights are converted to bf16 (exact)
-// on their way into LDS, so the MFMA loop is the same for both weight types
-// and the per-output-channel scale is applied in the epilogue.  Four waves
-// each own a 64 x 64 quarter of the 128 x 128 tile as 2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+// Three tile kernels, chosen by batch shape and weight type:
+//  - few rows per expert (decode): the weight-streaming kernel of
+//    ffn_stream.hip, bound by HBM bandwidth;
+//  - bf16 weights, many rows: the direct-to-LDS pipelined kernel of
+//    ffn_dma.hip;
+//  - fp8 e4m3 weights, many rows: the kernel below, which stages operands
+//    through registers so that the e4m3 codes are converted to bf16 (exactly)
+//    on their way into LDS; the MFMA loop is then the same as for bf16 and the
+//    per-output-channel scale is applied in the epilogue.
+// fp32 weights take plain fp32 FMA loops (no matrix cores).
 #include "ffn_common.h"
 
 namespace {
@@ -258,26 +260,6 @@ hipError_t launch_big(const TileParams &tp, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// sched[e] = number of BM-row tiles of experts < e (exclusive prefix), sched[El] = total.
-__global__ __launch_bounds__(64) void schedule_kernel(const int32_t *__restrict__ offsets, int El, int bm,
-                                                      int32_t *__restrict__ sched) {
-  const int lane = threadIdx.x;
-  int carry = 0;
-  for (int b = 0; b < El; b += 64) {
-    int e = b + lane;
-    int v = e < El ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      int o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    if (e < El) sched[e] = carry + incl - v;
-    carry += __shfl(incl, 63, 64);
-  }
-  if (lane == 0) sched[El] = carry;
-}
-
 // ---------------------------------------------------------------------------
 // fp32 path: plain fp32 FMA loops (small fp32 models; no matrix cores).
 // ---------------------------------------------------------------------------
@@ -331,8 +313,6 @@ __global__ __launch_bounds__(64) void down_f32_kernel(const float *__restrict__ 
 
 }  // namespace
 
-size_t ffn_sched_bytes(int El) { return align_up(sizeof(int32_t) * (size_t)(El + 1), 256); }
-
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
   hipError_t err;
   if (a.R_cap == 0 || a.T == 0) return hipSuccess;
@@ -353,17 +333,11 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
   }
   // Few rows per expert on average: stream the weights (HBM bound); else tiles (matrix-core bound).
   const bool stream = (long long)a.R_cap <= 48LL * a.El;
-  const int bm = stream ? ffn_stream_bm() : big::BM;
-  if (first) {
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(64), 0, s, a.offsets, a.El, bm, a.sched);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
   if (stream || a.w_dt == 1) {
     TileParams base{};
     base.offsets = a.offsets;
     base.row_token = a.row_token;
     base.row_w = a.row_w;
-    base.sched = a.sched;
     base.El = a.El;
     base.H = a.H;
     base.I = a.I;
@@ -380,7 +354,6 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
   tp.offsets = a.offsets;
   tp.row_token = a.row_token;
   tp.row_w = a.row_w;
-  tp.sched = a.sched;
   tp.El = a.El;
   tp.H = a.H;
   tp.I = a.I;

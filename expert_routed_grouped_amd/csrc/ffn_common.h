@@ -12,31 +12,73 @@ struct TileParams {
   const void *w;          // this projection's weights [El, Nw, K]
   const float *scale;     // [El, Nw] (fp8 only)
   void *out;              // h [R_cap,I] bf16 (gate-up) / y [T,H] or y_perm [R_cap,H] fp32 (down)
-  const int32_t *sched;   // M-tile prefix [El+1]
   int El, H, I;
   int R_cap;              // rows past R_cap are never touched, whatever the offsets say
 };
 
-// Locate this workgroup's tile.  Returns false for surplus workgroups.
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// M tiles of TBM rows that expert i needs (0 for an empty or malformed range).
 template <int TBM>
-__device__ __forceinline__ bool find_tile(const TileParams &p, int NT, int &e, int &nt, int &r0, int &rows) {
-  const int total = p.sched[p.El] * NT;
+__device__ __forceinline__ int expert_mtiles(const TileParams &p, int i) {
+  if (i >= p.El) return 0;
+  const int c = p.offsets[i + 1] - p.offsets[i];
+  return c > 0 ? (c + TBM - 1) / TBM : 0;
+}
+
+// Locate this workgroup's tile straight from the expert offsets (no schedule buffer): expert e
+// owns ceil(c_e / TBM) M tiles x NT N tiles, numbered expert-major, then N tile, then M tile.
+// Workgroups go round-robin over the 8 XCDs, so workgroup b takes tile number
+// (b % 8) * total/8 + b / 8: runs of consecutive tiles -- the M and N tiles of one expert, which
+// share operands -- stay on one XCD and its L2.  Every wave computes the same answer.
+// Returns false for surplus workgroups.
+template <int TBM>
+__device__ __forceinline__ bool locate_tile(const TileParams &p, int NT, int &e, int &nt, int &mt, int &mtiles) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  for (int b = 0; b < p.El; b += 64) total += wave_sum_i(expert_mtiles<TBM>(p, b + lane));
+  total *= NT;
   const int bid = blockIdx.x;
   if (bid >= total) return false;
-  // Keep consecutive tile numbers on one XCD (workgroups go round-robin over 8 XCDs).
   const int xcd = bid & 7, j = bid >> 3, q = total >> 3, rem = total & 7;
   const int L = xcd * q + min(xcd, rem) + j;
-  int lo = 0, hi = p.El - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (p.sched[mid] * NT <= L) lo = mid;
-    else hi = mid - 1;
+  int carry = 0;  // M tiles of the experts before this chunk
+  for (int b = 0; b < p.El; b += 64) {
+    const int t = expert_mtiles<TBM>(p, b + lane);
+    const int incl = wave_incl_scan_i(t, lane);
+    const unsigned long long hit = __ballot((carry + incl) * NT > L);
+    if (hit) {
+      const int l = __ffsll((long long)hit) - 1;
+      e = b + l;
+      mtiles = __shfl(t, l, 64);
+      const int rr = L - (carry + __shfl(incl, l, 64) - mtiles) * NT;
+      nt = rr / mtiles;
+      mt = rr - nt * mtiles;
+      return true;
+    }
+    carry += __shfl(incl, 63, 64);
   }
-  e = lo;
-  const int mtiles = p.sched[e + 1] - p.sched[e];
-  const int rr = L - p.sched[e] * NT;
-  nt = rr / mtiles;
-  const int mt = rr - nt * mtiles;
+  return false;
+}
+
+// Tile of TBM consecutive rows of one expert (the last tile of an expert may be short).
+template <int TBM>
+__device__ __forceinline__ bool find_tile(const TileParams &p, int NT, int &e, int &nt, int &r0, int &rows) {
+  int mt, mtiles;
+  if (!locate_tile<TBM>(p, NT, e, nt, mt, mtiles)) return false;
   r0 = p.offsets[e] + mt * TBM;
   rows = min(TBM, min(p.offsets[e + 1], p.R_cap) - r0);
   return rows > 0;

@@ -20,9 +20,10 @@
 //  - two chunks are in flight per wave (register double buffering), and many
 //    waves per CU cover the HBM latency.
 //
-// The tile list comes from the same device-side schedule as the tile kernels
-// (64-row M tiles); an expert with more than 64 rows gets more M tiles and its
-// weights are streamed once per M tile, which is still correct.
+// Tiles are located the same way as in the tile kernels (64-row M tiles, found
+// from the expert offsets on the device); an expert with more than 64 rows gets
+// more M tiles and its weights are streamed once per M tile, which is still
+// correct.
 #include "ffn_common.h"
 
 namespace {
@@ -182,8 +183,7 @@ hipError_t launch_s(const TileParams &tp, int grid, hipStream_t s) {
 
 int ffn_stream_bm() { return SBM; }
 
-// Both halves (or one, per ``phase``) of the streaming FFN; the schedule prefix
-// (64-row tiles) must already be in tp.sched.
+// Both halves (or one, per ``phase``) of the streaming FFN.
 hipError_t launch_ffn_stream(const TileParams &base, const FfnArgs &a, hipStream_t s) {
   hipError_t err = hipSuccess;
   const long long mt1 = ((long long)a.R_cap + (long long)a.El * (SBM - 1)) / SBM;

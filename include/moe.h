@@ -143,8 +143,8 @@ int moe_permute(const int32_t *topk_ids, const float *topk_w, int T, int k, int 
 size_t moe_permute_workspace_size(int T, int k, int E_loc);
 
 /*
- * Bytes of workspace moe_grouped_ffn needs (the intermediate h [R_cap, I] plus
- * scheduling scratch), for activations of type a_dtype.
+ * Bytes of workspace moe_grouped_ffn needs (the intermediate h [R_cap, I]), for
+ * activations of type a_dtype.
  */
 size_t moe_ffn_workspace_size(int R_cap, int E_loc, int H, int I, int a_dtype);
 
