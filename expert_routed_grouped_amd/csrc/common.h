@@ -36,6 +36,12 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
 }
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// SiLU for the bf16 epilogues, whose result is rounded to bf16 right after: hardware exp2 and
+// reciprocal (about 1 ulp of fp32 each) instead of the correctly rounded expf and division.
+// Limits hold: g -> -inf gives -0 (exp2 -> inf, rcp -> 0), g -> +inf gives g.
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
 
 static inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(big::NTHR, 1) void ffn_big_kernel(TileParams p) {
         const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (m < mvalid) {
           const float g = acc[i][0][r] * sg, u = acc[i][1][r] * su;
-          hout[(size_t)(r0 + wm * 128 + m) * p.I + col] = f32_to_bf16(silu_f32(g) * u);
+          hout[(size_t)(r0 + wm * 128 + m) * p.I + col] = f32_to_bf16(silu_fast(g) * u);
         }
       }
   } else {

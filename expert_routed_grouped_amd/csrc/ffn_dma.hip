@@ -140,7 +140,7 @@ __device__ __forceinline__ void dma_body(const TileParams &p, const char *abase,
         for (int r = 0; r < 16; r++) {
           const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (m < mvalid)
-            hout[(size_t)(rbase + m) * p.I + col] = f32_to_bf16(silu_f32(acc[i][0][r]) * acc[i][1][r]);
+            hout[(size_t)(rbase + m) * p.I + col] = f32_to_bf16(silu_fast(acc[i][0][r]) * acc[i][1][r]);
         }
     } else {
       float *out = (float *)p.out;

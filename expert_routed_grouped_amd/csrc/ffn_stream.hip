@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
         const int m = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
         if (m < rows) {
           const float gt = acc[mb][0][r] * sg, u = acc[mb][1][r] * su;
-          hout[(size_t)(r0 + m) * p.I + col] = f32_to_bf16(silu_f32(gt) * u);
+          hout[(size_t)(r0 + m) * p.I + col] = f32_to_bf16(silu_fast(gt) * u);
         }
       }
     }

@@ -59,6 +59,10 @@ __device__ __forceinline__ float load1(const void *p, size_t i) {
   else return ((const float *)p)[i];
 }
 
+#ifndef ROUTE_NS
+#define ROUTE_NS 8
+#endif
+
 // Block = EC waves (wave c owns experts 64c .. 64c+63), TT tokens per block.
 // VEC: H % 8 == 0 and 16-byte aligned rows (8-wide loads); otherwise one h at a time.
 template <int TT, int EC, bool XB, bool WB, bool VEC>
@@ -79,6 +83,17 @@ __global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__
     xrow[tt] = (const char *)x + (size_t)t * H * esz_x;
   }
   const char *wrow = (const char *)w + (size_t)(ev ? e : 0) * H * esz_w;
+  // Every block reads all of W_r, which is usually cold (the expert weights of the previous
+  // layer call streamed through L2 since).  Each thread of the grid first touches one
+  // distinct 128-byte line of it, so the whole matrix is pulled into L2 in one round trip
+  // instead of block after block waiting on the same misses.
+  uint32_t touch = 0;
+  {
+    const size_t nlines = (size_t)E * H * esz_w / 128;  // whole lines only: never past the end
+    const size_t nthreads = (size_t)gridDim.x * blockDim.x;
+    for (size_t l = (size_t)blockIdx.x * blockDim.x + threadIdx.x; l < nlines; l += nthreads)
+      touch |= *(const volatile uint32_t *)((const char *)w + l * 128);
+  }
   // VEC: the block's activation rows, staged once in LDS as fp32 ([TT][H], dynamic size)
   extern __shared__ __attribute__((aligned(16))) float xs[];
   if constexpr (VEC) {
@@ -98,11 +113,12 @@ __global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__
   for (int tt = 0; tt < TT; tt++) acc[tt] = 0.0f;
 
   if constexpr (VEC) {
-    // 32 h per step; two register sets alternate so the weight pieces of step
-    // s+1 are in flight while step s computes
-    constexpr int HS = 32, P = HS * (WB ? 2 : 4) / 16;
+    // 32 h per step; a ring of ROUTE_NS register sets keeps the weight pieces of
+    // the next ROUTE_NS-1 steps in flight while a step computes (each lane reads
+    // its own expert row, so only prefetch depth hides the L2 latency)
+    constexpr int HS = 32, P = HS * (WB ? 2 : 4) / 16, NS = ROUTE_NS;
     const int nsteps = H / HS;
-    u32x4_t b0[P], b1[P];
+    u32x4_t ring[NS][P];
     auto wload = [&](u32x4_t(&b)[P], int st) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < P; q++) b[q] = *(const u32x4_t *)(wrow + (size_t)st * HS * esz_w + 16 * q);
@@ -132,13 +148,17 @@ __global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__
         }
       }
     };
-    if (nsteps > 0) wload(b0, 0);
-    for (int st = 0; st < nsteps; st += 2) {
-      if (st + 1 < nsteps) wload(b1, st + 1);
-      wstep(b0, st);
-      if (st + 1 >= nsteps) break;
-      if (st + 2 < nsteps) wload(b0, st + 2);
-      wstep(b1, st + 1);
+#pragma unroll
+    for (int q = 0; q < NS - 1; q++)
+      if (q < nsteps) wload(ring[q], q);
+    for (int st0 = 0; st0 < nsteps; st0 += NS) {
+#pragma unroll
+      for (int q = 0; q < NS; q++) {
+        const int st = st0 + q;
+        if (st >= nsteps) break;
+        if (st + NS - 1 < nsteps) wload(ring[(q + NS - 1) % NS], st + NS - 1);
+        wstep(ring[q], st);
+      }
     }
     for (int h = nsteps * HS; h < H; h += 8) {
       float wf[8];
@@ -163,6 +183,7 @@ __global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__
 #pragma unroll
     for (int tt = 0; tt < TT; tt++) acc[tt] = acc[tt] + b;
   }
+  asm volatile("" ::"v"(touch));  // keeps the warm-up loads
 #pragma unroll
   for (int tt = 0; tt < TT; tt++) lg[tt][e] = acc[tt];
   __syncthreads();

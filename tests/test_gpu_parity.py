@@ -257,6 +257,39 @@ def test_layer_all_tokens_matches_oracle(cfg, fused):
         assert np.all(y[no_local] == 0)
 
 
+# Per-expert row counts around the tile sizes of the large-batch kernels (64-row and 256-row
+# boundaries, one empty expert): each expert's rows are split into equal M tiles.
+TILE_COUNTS = [1, 63, 64, 65, 255, 256, 257, 511, 512, 513, 0, 999, 752, 752]
+
+
+def constructed_routing(counts, T, k, seed):
+    """ids [T,k] with exactly counts[e] assignments of expert e and k distinct experts per token:
+    the expert-sorted assignment list is dealt out with stride T (every run is shorter than T)."""
+    assert sum(counts) == T * k and max(counts) < T
+    flat = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    ids = np.ascontiguousarray(flat.reshape(k, T).T)
+    assert all(len(set(r)) == k for r in ids.tolist())
+    w = np.random.default_rng(seed).random((T, k)).astype(np.float32)
+    return ids, w
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "combine"])
+@pytest.mark.parametrize("wdt", ["bf16", "fp8"])
+def test_layer_tile_boundaries(wdt, fused):
+    cfg = LayerConfig(f"tiles_{wdt}", T=1000, H=320, E=len(TILE_COUNTS), k=5, I=192, wdt=wdt, seed=210,
+                      w_std=0.05)
+    inp = host_inputs(cfg)
+    dev = L.to_device(inp)
+    ids, w = constructed_routing(TILE_COUNTS, cfg.T, cfg.k, seed=211)
+    say(f"layer {cfg.name} fused={fused}: counts {TILE_COUNTS}")
+    ids_d, w_d = to_dev_routing(ids, w)
+    y, p = gpu_layer(dev, cfg, ids_d, w_d, fused=fused)
+    assert p["counts"].cpu().tolist() == TILE_COUNTS
+    y_o = O.layer_tokens(np.arange(cfg.T), inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"],
+                         inp["s_gate_up"], inp["s_down"], round_h=True)
+    check_y(y, y_o, cfg.name)
+
+
 @pytest.mark.parametrize("cfg", [FFN_CASES[0], FFN_CASES[1]], ids=lambda c: c.name)
 def test_layer_with_materialised_x_perm(cfg):
     """gather=False: the FFN reads x_perm written by moe_permute instead of gathering x."""
