@@ -41,10 +41,12 @@ WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time budget of the oracle sample")
+    ap.add_argument("--flush-steps", type=int, default=20,
+                    help="extra steps, each after writing a 1 GiB scratch buffer (cold L2 and Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -95,22 +97,31 @@ def cpu_baseline(inp, cfg, seconds):
     from oracle import oracle as O
     chunk = min(64, cfg.T)
     done = 0
+    stage = {"route": 0.0, "permute": 0.0, "ffn_combine": 0.0}
     t0 = time.perf_counter()
     while True:
         lo = done % cfg.T
         sl = slice(lo, min(lo + chunk, cfg.T))
         x = np.ascontiguousarray(inp["x"][sl])
+        ta = time.perf_counter()
         ids, w, _ = O.route(x, inp["w_router"], inp["bias"], cfg.k)
+        tb = time.perf_counter()
         O.permute(ids, w, cfg.lo, cfg.hi)
+        tc = time.perf_counter()
         O.layer_tokens(np.arange(x.shape[0]), x, ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"],
                        inp["s_gate_up"], inp["s_down"], round_h=cfg.act != "f32")
+        td = time.perf_counter()
+        stage["route"] += tb - ta
+        stage["permute"] += tc - tb
+        stage["ffn_combine"] += td - tc
         done += x.shape[0]
-        dt = time.perf_counter() - t0
+        dt = td - t0
         if dt >= seconds:
             break
     return {"value": done / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
             "sample": f"{done} tokens in {chunk}-token chunks of the same {cfg.T}-token batch (wrapping around), "
-                      f"whole layer per chunk (route, permute, token-major SwiGLU FFN + combine), {dt:.1f} s"}
+                      f"whole layer per chunk (route, permute, token-major SwiGLU FFN + combine), {dt:.1f} s",
+            "stage_tokens_per_s": {k: round(done / v, 1) if v > 0 else None for k, v in stage.items()}}
 
 
 def main():
@@ -173,6 +184,23 @@ def main():
     gu_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     down_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
 
+    flushed = None
+    if args.flush_steps > 0:
+        # each step after a 1 GiB write: the weights come from HBM, as when other layers ran in between
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        fl_ms = []
+        for _ in range(args.flush_steps):
+            scratch.fill_(0x5A)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            step(e)
+            torch.cuda.synchronize()
+            fl_ms.append(e[0].elapsed_time(e[3]))
+        del scratch
+        fl = np.array(fl_ms)
+        flushed = {"steps": args.flush_steps, "ms_p50": round(float(np.median(fl)), 4),
+                   "ms_p10": round(float(np.percentile(fl, 10)), 4), "ms_p90": round(float(np.percentile(fl, 90)), 4),
+                   "tokens_per_s_p50": round(cfg.T / (float(np.median(fl)) * 1e-3), 1)}
+
     counts = p["counts"].cpu().numpy().astype(np.int64)
     R = int(counts.sum())
     U = int((counts > 0).sum())
@@ -198,6 +226,9 @@ def main():
     kernel = ("ffn_stream_kernel" if bufs.R_cap <= 48 * cfg.E_loc else
               ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel"))
     roof["traffic"] = measured_traffic(kernel, args.config)
+    # rows the grouped GEMM actually multiplies, by the tiling of the kernel in use
+    padded = (A.padded_rows(counts, 64) if kernel == "ffn_stream_kernel" else
+              (A.split_padded_rows(counts, 256, 64) if kernel == "ffn_dma_kernel" else A.padded_rows(counts, 256)))
     roof.update({"kernel": f"{kernel} (gate/up + SwiGLU half, one launch)", "avg_ms": round(float(np.mean(gu_ms)), 4),
                  "algorithmic_per_launch": gu_bytes if args.config == "decode" else gu_flops})
     layer_s = ms_per_step * 1e-3
@@ -224,8 +255,9 @@ def main():
                   "down_combine_ms": round(float(np.mean(down_ms)), 4),
                   "hbm_bytes": int(layer_bytes), "hbm_frac": round(layer_bytes / layer_s / 1e9 / PEAK_HBM_GBS, 4),
                   "flops": int(layer_flops), "mfma_frac": round(layer_flops / layer_s / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "flushed_caches": flushed,
         "routing": {"assignments": R, "active_experts": U, "max_rows": int(counts.max()),
-                    "padded_rows_bm128": A.padded_rows(counts, 128),
+                    "padded_rows": padded, "padded_over_R": round(padded / R, 4) if R else None,
                     "skew": round(float(counts.max() / (R / max(len(counts), 1))), 3) if R else None},
     }
     if not args.no_cpu_baseline:

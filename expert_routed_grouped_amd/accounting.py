@@ -53,6 +53,20 @@ def padded_rows(counts: Sequence[int], tile: int) -> int:
     return int(sum(-(-int(c) // tile) * tile for c in counts if c > 0))
 
 
+def split_padded_rows(counts: Sequence[int], max_tile: int, align: int) -> int:
+    """Rows executed when an expert's c rows are cut into ceil(c/max_tile) equal tiles, each rounded
+    up to a multiple of ``align`` (the large-batch bf16 grouped GEMM: max_tile 256, align 64)."""
+    total = 0
+    for c in counts:
+        c = int(c)
+        if c <= 0:
+            continue
+        m = -(-c // max_tile)
+        per = -(-c // m)
+        total += m * min(max_tile, -(-per // align) * align)
+    return total
+
+
 def padded_rows_to_max(counts: Sequence[int]) -> int:
     """Rows executed when every expert (empty ones included) is padded to the largest count."""
     return int(len(counts) * max(int(c) for c in counts))
