@@ -30,9 +30,13 @@ namespace {
 
 using ffn::TileParams;
 
-constexpr int SBM = 64;     // rows per M tile
+#ifndef STREAM_MB
+#define STREAM_MB 2
+#endif
+constexpr int SMB = STREAM_MB;  // 32-row MFMA blocks per M tile
+constexpr int SBM = 32 * SMB;   // rows per M tile
 constexpr int SWAVES = 4;   // waves per block, 32 output columns each
-constexpr int SCOLS = 32 * SWAVES;
+constexpr int SCOLS = 32 * SWAVES;  // gate/up columns per block (down: twice as many)
 
 // 8 bf16 from 16 bytes of bf16, or from 8 bytes of e4m3.
 template <bool FP8>
@@ -55,15 +59,16 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
   const int K = MODE == 0 ? p.H : p.I;
   const int Ncols = MODE == 0 ? p.I : p.H;
   const int Nw = MODE == 0 ? 2 * p.I : p.H;
-  const int NT = (Ncols + SCOLS - 1) / SCOLS;
+  constexpr int WCOLS = MODE == 0 ? 32 : 64;  // output columns per wave
+  const int NT = (Ncols + SWAVES * WCOLS - 1) / (SWAVES * WCOLS);
   int e, nt, r0, rows;
   if (!ffn::find_tile<SBM>(p, NT, e, nt, r0, rows)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c0 = nt * SCOLS + wave * 32;
-  if (c0 >= Ncols) return;
+  const int c0 = (nt * SWAVES + wave) * WCOLS;
+  if (c0 >= Ncols) return;  // Ncols is a multiple of 64: a wave's columns are all valid or all past the end
   const int n = lane & 31, g = lane >> 5;
-  constexpr int NB = MODE == 0 ? 2 : 1;  // weight row blocks per wave: gate + up, or down
-  const bool two_m = rows > 32;           // wave-uniform
+  constexpr int NB = 2;                  // weight row blocks per wave: gate + up, or two down blocks
+  const bool two_m = SMB > 1 && rows > 32;  // wave-uniform
 
   // weight rows of this lane (k offset 32g inside every 64-wide chunk)
   const size_t wesz = FP8 ? 1 : 2;
@@ -73,25 +78,26 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
     wrow[1] = (const char *)p.w + (((size_t)e * Nw + p.I + c0 + n) * K + 32 * g) * wesz;
   } else {
     wrow[0] = (const char *)p.w + (((size_t)e * Nw + c0 + n) * K + 32 * g) * wesz;
+    wrow[1] = (const char *)p.w + (((size_t)e * Nw + c0 + 32 + n) * K + 32 * g) * wesz;
   }
   // activation rows (two 32-row blocks; rows past the end repeat the last valid row)
-  const uint16_t *arow[2];
+  const uint16_t *arow[SMB];
 #pragma unroll
-  for (int mb = 0; mb < 2; mb++) {
+  for (int mb = 0; mb < SMB; mb++) {
     const int r = r0 + min(mb * 32 + n, rows - 1);
     const size_t src = (MODE == 0 && GATHER) ? (size_t)p.row_token[r] : (size_t)r;
     arow[mb] = (const uint16_t *)p.a + src * K + 32 * g;
   }
 
-  f32x16_t acc[2][NB];
+  f32x16_t acc[SMB][NB];
 #pragma unroll
-  for (int mb = 0; mb < 2; mb++)
+  for (int mb = 0; mb < SMB; mb++)
 #pragma unroll
     for (int b = 0; b < NB; b++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[mb][b][r] = 0.0f;
 
-  u32x4_t wq[2][NB][WQ], aq[2][2][4];
+  u32x4_t wq[2][NB][WQ], aq[2][SMB][4];
   auto load = [&](int buf, int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < NB; b++)
@@ -99,9 +105,11 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
       for (int q = 0; q < WQ; q++) wq[buf][b][q] = *(const u32x4_t *)(wrow[b] + (size_t)k0 * wesz + 16 * q);
 #pragma unroll
     for (int q = 0; q < 4; q++) aq[buf][0][q] = *(const u32x4_t *)(arow[0] + k0 + 8 * q);
-    if (two_m) {
+    if constexpr (SMB > 1) {
+      if (two_m) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) aq[buf][1][q] = *(const u32x4_t *)(arow[1] + k0 + 8 * q);
+        for (int q = 0; q < 4; q++) aq[buf][SMB - 1][q] = *(const u32x4_t *)(arow[SMB - 1] + k0 + 8 * q);
+      }
     }
   };
   auto compute = [&](int buf) __attribute__((always_inline)) {
@@ -113,10 +121,13 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
       const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, aq[buf][0][s]);
 #pragma unroll
       for (int b = 0; b < NB; b++) acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bo[b], acc[0][b], 0, 0, 0);
-      if (two_m) {
-        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, aq[buf][1][s]);
+      if constexpr (SMB > 1) {
+        if (two_m) {
+          const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, aq[buf][SMB - 1][s]);
 #pragma unroll
-        for (int b = 0; b < NB; b++) acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bo[b], acc[1][b], 0, 0, 0);
+          for (int b = 0; b < NB; b++)
+            acc[SMB - 1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bo[b], acc[SMB - 1][b], 0, 0, 0);
+        }
       }
     }
   };
@@ -142,7 +153,7 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
     }
     uint16_t *hout = (uint16_t *)p.out;
 #pragma unroll
-    for (int mb = 0; mb < 2; mb++) {
+    for (int mb = 0; mb < SMB; mb++) {
       if (mb == 1 && !two_m) break;
 #pragma unroll
       for (int r = 0; r < 16; r++) {
@@ -154,19 +165,23 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
       }
     }
   } else {
-    const float sc = FP8 ? p.scale[(size_t)e * Nw + col] : 1.0f;
     float *out = (float *)p.out;
 #pragma unroll
-    for (int mb = 0; mb < 2; mb++) {
-      if (mb == 1 && !two_m) break;
+    for (int b = 0; b < NB; b++) {
+      const int cb = col + 32 * b;
+      const float sc = FP8 ? p.scale[(size_t)e * Nw + cb] : 1.0f;
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int m = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (m < rows) {
-          const int row = r0 + m;
-          const float o = acc[mb][0][r] * sc;
-          if constexpr (ATOMIC) atomicAdd(out + (size_t)p.row_token[row] * p.H + col, p.row_w[row] * o);
-          else out[(size_t)row * p.H + col] = o;
+      for (int mb = 0; mb < SMB; mb++) {
+        if (mb == 1 && !two_m) break;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int m = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (m < rows) {
+            const int row = r0 + m;
+            const float o = acc[mb][b][r] * sc;
+            if constexpr (ATOMIC) atomicAdd(out + (size_t)p.row_token[row] * p.H + cb, p.row_w[row] * o);
+            else out[(size_t)row * p.H + cb] = o;
+          }
         }
       }
     }
@@ -207,7 +222,7 @@ hipError_t launch_ffn_stream(const TileParams &base, const FfnArgs &a, hipStream
     tp.scale = a.s_d;
     const bool atomic = a.y != nullptr;
     tp.out = atomic ? (void *)a.y : (void *)a.y_perm;
-    const int grid = (int)(max_mt * ceil_div_i(a.H, SCOLS));
+    const int grid = (int)(max_mt * ceil_div_i(a.H, 2 * SCOLS));  // down: 64 columns per wave
     if (fp8) err = atomic ? launch_s<1, true, false, true>(tp, grid, s) : launch_s<1, true, false, false>(tp, grid, s);
     else err = atomic ? launch_s<1, false, false, true>(tp, grid, s) : launch_s<1, false, false, false>(tp, grid, s);
   }
