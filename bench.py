@@ -30,11 +30,13 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec + % bf16 MFMA peak (prefill) / % HBM BW (decode)"
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix cores
 WORKLOADS = {
     "decode": "decode MoE layer: T=64 tokens x top-8 of E=128 experts (512 assignments), H=4096, SwiGLU I=1536, bf16",
     "prefill": "prefill MoE layer: T=6000 tokens x top-8 of E=128 experts, H=4096, SwiGLU I=1536, bf16",
     "skew": "skewed prefill MoE layer: T=6000, top-8 of 128, logit bias 2*ln Zipf(1.2), H=4096, I=1536, bf16",
     "ep_share": "EP=4 share: T=8192 routed over 128 experts, local experts 0-31, fp8 e4m3 weights, H=4096, I=1536",
+    "prefill_mx": "W8A8 MXFP8 prefill MoE layer: T=6000 tokens x top-8 of E=128 experts, H=4096, SwiGLU I=1536",
 }
 
 
@@ -108,8 +110,12 @@ def cpu_baseline(inp, cfg, seconds):
         tb = time.perf_counter()
         O.permute(ids, w, cfg.lo, cfg.hi)
         tc = time.perf_counter()
-        O.layer_tokens(np.arange(x.shape[0]), x, ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"],
-                       inp["s_gate_up"], inp["s_down"], round_h=cfg.act != "f32")
+        if cfg.wdt == "mxfp8":
+            O.layer_tokens_mx(np.arange(x.shape[0]), x, ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["s_gate_up"],
+                              inp["w_down"], inp["s_down"])
+        else:
+            O.layer_tokens(np.arange(x.shape[0]), x, ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"],
+                           inp["s_gate_up"], inp["s_down"], round_h=cfg.act != "f32")
         td = time.perf_counter()
         stage["route"] += tb - ta
         stage["permute"] += tc - tb
@@ -145,22 +151,38 @@ def main():
     bufs = L.LayerBuffers(cfg)
     stream = torch.cuda.current_stream()
     p = bufs.perm
+    mx = cfg.wdt == "mxfp8"
+    if mx:  # activations quantised on the fly into these, h lives in the MX workspace
+        xq = torch.empty((cfg.T, cfg.H), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((cfg.T, cfg.H // 32), dtype=torch.uint8, device="cuda")
+        bufs.workspace = torch.empty(moe.moe_ffn_mx_workspace_size(bufs.R_cap, cfg.I), dtype=torch.uint8,
+                                     device="cuda")
+
+    def ffn_half(phase, outs, common):
+        if mx:
+            moe.moe_grouped_ffn_mx(xq, xs, p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
+                                   dev["w_gate_up"], dev["s_gate_up"], dev["w_down"], dev["s_down"], phase=phase,
+                                   **outs, **common)
+        else:
+            moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
+                                dev["w_gate_up"], dev["w_down"], dev["s_gate_up"], dev["s_down"], phase=phase,
+                                **outs, **common)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=stream)
         moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=p, stream=stream)
+        if mx:
+            moe.moe_quantize_mx(dev["x"], xq, xs, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         common = dict(workspace=bufs.workspace, gather=True, stream=stream)
         outs = dict(y=bufs.y, zero_y=True) if bufs.fused else dict(y_perm=bufs.y_perm, zero_y=False)
-        moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap, dev["w_gate_up"],
-                            dev["w_down"], dev["s_gate_up"], dev["s_down"], phase="gate_up", **outs, **common)
+        ffn_half("gate_up", outs, common)
         if ev is not None:
             ev[2].record(stream)
-        moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap, dev["w_gate_up"],
-                            dev["w_down"], dev["s_gate_up"], dev["s_down"], phase="down", **outs, **common)
+        ffn_half("down", outs, common)
         if not bufs.fused:
             moe.moe_combine(bufs.y_perm, p["token_row"], bufs.topk_w, y=bufs.y, stream=stream)
         if ev is not None:
@@ -205,11 +227,13 @@ def main():
     R = int(counts.sum())
     U = int((counts > 0).sum())
     H, I, T = cfg.H, cfg.I, cfg.T
-    wbytes = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.wdt]
+    # MXFP8 tensors carry one E8M0 scale byte per 32 codes
+    wbytes = {"bf16": 2, "fp8": 1, "f32": 4, "mxfp8": 1 + 1 / 32}[cfg.wdt]
     abytes = 4 if cfg.act == "f32" else 2
+    gu_abytes = 1 + 1 / 32 if mx else abytes   # x codes read, h codes written
     scale_gu = 4 * 2 * I if cfg.wdt == "fp8" else 0
     # gate/up half, algorithmic: each active expert's gate/up weights once, x read once, h written once
-    gu_bytes = U * (2 * I * H * wbytes + scale_gu) + T * H * abytes + R * I * abytes
+    gu_bytes = int(U * (2 * I * H * wbytes + scale_gu) + T * H * gu_abytes + R * I * gu_abytes)
     gu_flops = 4 * R * H * I
     layer_flops = A.useful_flops(R, H, I) + A.router_flops(T, H, cfg.E)
     layer_bytes = A.layer_hbm_bytes(counts, T, H, I, cfg.E, abytes,
@@ -221,14 +245,17 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     else:
         achieved = gu_flops / gu_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
-    kernel = ("ffn_stream_kernel" if bufs.R_cap <= 48 * cfg.E_loc else
-              ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel"))
+        peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None}
+    kernel = ("ffn_mx_kernel" if mx else
+              ("ffn_stream_kernel" if bufs.R_cap <= 48 * cfg.E_loc else
+               ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel")))
     roof["traffic"] = measured_traffic(kernel, args.config)
     # rows the grouped GEMM actually multiplies, by the tiling of the kernel in use
     padded = (A.padded_rows(counts, 64) if kernel == "ffn_stream_kernel" else
-              (A.split_padded_rows(counts, 256, 64) if kernel == "ffn_dma_kernel" else A.padded_rows(counts, 256)))
+              (A.split_padded_rows(counts, 256, 64) if kernel == "ffn_dma_kernel" else
+               (A.split_padded_rows(counts, 192, 64) if kernel == "ffn_mx_kernel" else A.padded_rows(counts, 256))))
     roof.update({"kernel": f"{kernel} (gate/up + SwiGLU half, one launch)", "avg_ms": round(float(np.mean(gu_ms)), 4),
                  "algorithmic_per_launch": gu_bytes if args.config == "decode" else gu_flops})
     layer_s = ms_per_step * 1e-3
@@ -243,7 +270,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.wdt == "bf16" else ("fp8-weights/bf16" if cfg.wdt == "fp8" else "f32"),
+        "dtype": {"bf16": "bf16", "fp8": "fp8-weights/bf16", "mxfp8": "mxfp8 (e4m3 + e8m0 block scales)"}.get(cfg.wdt,
+                                                                                                            "f32"),
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "T": T, "H": H, "E": cfg.E, "k": cfg.k, "I": I,
                    "local_experts": [cfg.lo, cfg.hi], "parallelism": "none (one GPU)",
@@ -254,7 +282,8 @@ def main():
                   "route_permute_ms": round(float(np.mean(route_ms)), 4), "gate_up_ms": round(float(np.mean(gu_ms)), 4),
                   "down_combine_ms": round(float(np.mean(down_ms)), 4),
                   "hbm_bytes": int(layer_bytes), "hbm_frac": round(layer_bytes / layer_s / 1e9 / PEAK_HBM_GBS, 4),
-                  "flops": int(layer_flops), "mfma_frac": round(layer_flops / layer_s / 1e12 / PEAK_BF16_TFLOPS, 4)},
+                  "flops": int(layer_flops),
+                  "mfma_frac": round(layer_flops / layer_s / 1e12 / (PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS), 4)},
         "flushed_caches": flushed,
         "routing": {"assignments": R, "active_experts": U, "max_rows": int(counts.max()),
                     "padded_rows": padded, "padded_over_R": round(padded / R, 4) if R else None,

@@ -89,7 +89,10 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
                     size_t workspace_bytes, unsigned flags, void *stream) {
   if (T < 0 || R_cap < 0 || E_loc < 1 || E_loc > 512 || H < 64 || I < 64 || H % 64 != 0 || I % 64 != 0)
     return MOE_ERR_SHAPE;
-  if ((long long)R_cap > (long long)T * E_loc || (long long)R_cap * (H > I ? H : I) >= (1LL << 40)) return MOE_ERR_SHAPE;
+  if ((long long)R_cap > (long long)T * E_loc) return MOE_ERR_SHAPE;
+  // the tile kernels address a row-major operand with 32-bit byte offsets (rows x dim x 4 < 2^32)
+  if ((long long)(T > R_cap ? T : R_cap) * (H > I ? H : I) >= (1LL << 30) || (long long)H * I >= (1LL << 30))
+    return MOE_ERR_SHAPE;
   const bool bf16_path = a_dtype == MOE_BF16 && (w_dtype == MOE_BF16 || w_dtype == MOE_FP8_E4M3);
   const bool f32_path = a_dtype == MOE_F32 && w_dtype == MOE_F32;
   if (!bf16_path && !f32_path) return MOE_ERR_DTYPE;
@@ -146,3 +149,66 @@ int moe_combine(const float *y_perm, const int32_t *token_row, const float *topk
 }
 
 }  // extern "C"
+
+int moe_quantize_mx(const void *x, int x_dtype, int rows, int K, uint8_t *codes, uint8_t *scales, void *stream) {
+  if (rows < 0 || K < 32 || K % 32 != 0 || (long long)rows * K >= (1LL << 40)) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales) return MOE_ERR_NULL;
+  return hip_status(launch_quantize_mx(x, x_dtype == MOE_BF16, rows, K, codes, scales, (hipStream_t)stream));
+}
+
+size_t moe_ffn_mx_workspace_size(int R_cap, int I) {
+  if (R_cap < 0 || I < 1) return 0;
+  return ffn_mx_h_bytes(R_cap, I) + align_up((size_t)R_cap * (size_t)(I / 32), 256);
+}
+
+int moe_grouped_ffn_mx(const uint8_t *a_codes, const uint8_t *a_scales, const int32_t *offsets,
+                       const int32_t *row_token, const float *row_w, int E_loc, int T, int R_cap, int H, int I,
+                       const uint8_t *wgu_codes, const uint8_t *wgu_scales, const uint8_t *wd_codes,
+                       const uint8_t *wd_scales, float *y, float *y_perm, void *workspace, size_t workspace_bytes,
+                       unsigned flags, void *stream) {
+  if (T < 0 || R_cap < 0 || E_loc < 1 || E_loc > 512 || H < 128 || I < 128 || H % 128 != 0 || I % 128 != 0)
+    return MOE_ERR_SHAPE;
+  if ((long long)R_cap > (long long)T * E_loc) return MOE_ERR_SHAPE;
+  if ((long long)(T > R_cap ? T : R_cap) * (H > I ? H : I) >= (1LL << 30) || (long long)H * I >= (1LL << 30))
+    return MOE_ERR_SHAPE;
+  if ((y == nullptr) == (y_perm == nullptr)) return MOE_ERR_NULL;
+  const bool gather = (flags & MOE_FFN_GATHER) != 0;
+  if (!a_codes || !a_scales || !offsets || !wgu_codes || !wgu_scales || !wd_codes || !wd_scales) return MOE_ERR_NULL;
+  if ((gather || y) && !row_token) return MOE_ERR_NULL;
+  if (y && !row_w) return MOE_ERR_NULL;
+  if (!workspace) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < moe_ffn_mx_workspace_size(R_cap, I)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(a_codes) || !aligned16(wgu_codes) || !aligned16(wd_codes) || (y && !aligned16(y)) ||
+      (y_perm && !aligned16(y_perm)) || ((uintptr_t)workspace & 255u) != 0 || ((uintptr_t)a_scales & 3u) != 0 ||
+      ((uintptr_t)wgu_scales & 3u) != 0 || ((uintptr_t)wd_scales & 3u) != 0)
+    return MOE_ERR_ALIGN;
+  const unsigned only = flags & (MOE_FFN_ONLY_GATE_UP | MOE_FFN_ONLY_DOWN);
+  if (only == (MOE_FFN_ONLY_GATE_UP | MOE_FFN_ONLY_DOWN)) return MOE_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (y && (flags & MOE_FFN_ZERO_Y) && only != MOE_FFN_ONLY_GATE_UP) {
+    if (launch_zero_f32(y, (size_t)T * H, s) != hipSuccess) return MOE_ERR_HIP;
+  }
+  FfnMxArgs fa{};
+  fa.a = a_codes;
+  fa.a_s = a_scales;
+  fa.gather = gather;
+  fa.offsets = offsets;
+  fa.row_token = row_token;
+  fa.row_w = row_w;
+  fa.El = E_loc;
+  fa.T = T;
+  fa.R_cap = R_cap;
+  fa.H = H;
+  fa.I = I;
+  fa.wgu = wgu_codes;
+  fa.wgu_s = wgu_scales;
+  fa.wd = wd_codes;
+  fa.wd_s = wd_scales;
+  fa.y = y;
+  fa.y_perm = y_perm;
+  fa.ws = workspace;
+  fa.phase = only == MOE_FFN_ONLY_GATE_UP ? 1 : (only == MOE_FFN_ONLY_DOWN ? 2 : 3);
+  return hip_status(launch_ffn_mx(fa, s));
+}

@@ -85,3 +85,25 @@ struct FfnArgs {
 };
 
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t s);
+
+// MXFP8 quantisation of rows x K values (K % 32 == 0).
+hipError_t launch_quantize_mx(const void *x, int x_bf16, int rows, int K, uint8_t *codes, uint8_t *scales,
+                              hipStream_t s);
+
+// W8A8 MXFP8 grouped FFN.  ``ws`` holds h as MXFP8: R_cap*I codes (ffn_mx_h_bytes)
+// followed by R_cap*I/32 scale bytes.
+struct FfnMxArgs {
+  const uint8_t *a, *a_s;      // activation codes [rows, H] and scales [rows, H/32]
+  int gather;                  // 1: row r reads a[row_token[r]]
+  const int32_t *offsets;      // [El+1]
+  const int32_t *row_token;
+  const float *row_w;
+  int El, T, R_cap, H, I;
+  const uint8_t *wgu, *wgu_s;  // [El, 2I, H], [El, 2I, H/32]
+  const uint8_t *wd, *wd_s;    // [El, H, I], [El, H, I/32]
+  float *y, *y_perm;
+  void *ws;
+  int phase;                   // bit 0: gate/up half, bit 1: down half
+};
+size_t ffn_mx_h_bytes(int R_cap, int I);
+hipError_t launch_ffn_mx(const FfnMxArgs &a, hipStream_t s);

@@ -1,0 +1,316 @@
+// W8A8 MXFP8 grouped FFN (moe_grouped_ffn_mx) for gfx950.
+//
+// Tiling as in the bf16 direct-to-LDS kernel (ffn_dma.hip), with at most 192 rows
+// of one expert per tile (equal M tiles per expert, rounded to 64 rows; the fp8
+// operand fragments are twice as wide, so 4 x 2 accumulator blocks would spill) x 256 weight rows,
+// eight waves as 2 (M) x 4 (N), operands moved HBM/L2 -> LDS by global_load_lds
+// with load issue spread over the MFMAs.  The K step is 128 E4M3 values (one
+// full 128-byte line per row) plus the four E8M0 scale bytes of each row, and
+// the product is v_mfma_scale_f32_32x32x64_f8f6f4: 64 k per instruction with
+// the block scales applied inside the matrix core.
+//
+// Operand layout of that instruction (measured on MI355X): lane l holds row (or
+// column) l % 32; with h = l / 32, its bytes 0-15 are k = 16h .. 16h+15 and
+// bytes 16-31 are k = 32+16h .. 32+16h+15, so lanes of half h supply the scale
+// of the 32-wide block h of the 64 k.  Each lane therefore reads two 16-byte
+// chunks of its row per 64 k and passes the row's scale dword shifted by 8h,
+// with the byte selector picking block 2*kk of the K step.
+//
+// LDS: two slots, each holding one K step of A (256 x 128 B) and its scales
+// (up to 256 x 4 B) and of B likewise (116 KB); the loads of step kt+1 are issued
+// while step kt computes.  Chunk c of LDS row r sits in slot c ^ ((r >> 1) & 7).
+//
+// Gate/up epilogue: h = silu(G) * U in fp32, quantised per row in blocks of 32
+// intermediate columns (a wave's 32 columns are one block) into MXFP8 codes and
+// scales.  Down epilogue: fp32 per-row outputs or the fused atomic combine.
+#include "ffn_common.h"
+#include "mx_common.h"
+#include <type_traits>
+
+namespace {
+
+using ffn::TileParams;
+
+constexpr int BM = 192, BN = 256, BK = 128, NTHR = 512;
+// scale areas hold 32 rows per wave (8 x 32 = 256 >= BM, BN): wave w fills rows 32w .. 32w+31
+constexpr int A_BYTES = BM * BK, AS_BYTES = NTHR / 64 * 32 * 4, B_BYTES = BN * BK, BS_BYTES = NTHR / 64 * 32 * 4;
+static_assert(AS_BYTES >= BM * 4 && BS_BYTES >= BN * 4, "scale areas cover every tile row");
+constexpr int OFF_AS = A_BYTES, OFF_B = A_BYTES + AS_BYTES, OFF_BS = OFF_B + B_BYTES;
+constexpr int SLOT_BYTES = OFF_BS + BS_BYTES;  // 58 KB
+constexpr int LDS_BYTES = 2 * SLOT_BYTES;       // 116 KB
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int lds_off64(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+struct MxParams {
+  TileParams tp;               // offsets, row_token, row_w, El, H, I, R_cap; tp.a / tp.w / tp.out: codes
+  const uint8_t *a_scales;     // [rows, K/32]
+  const uint8_t *w_scales;     // [El, Nw, K/32]
+  uint8_t *out_scales;         // gate/up: h scales [R_cap, I/32]
+};
+
+struct Src {
+  uint32_t aoff[3], boff[4];   // byte offsets of this lane's A / B segment chunks at K step 0
+  uint32_t asoff, bsoff;       // byte offsets of this lane's A / B scale dwords at K step 0 (lanes < 32)
+};
+
+template <int NMB>
+__device__ __forceinline__ void kloop(const char *abase, const char *bbase, const uint8_t *asb, const uint8_t *bsb,
+                                      const Src &src, int nA, int K, int wave, int lane, int arow0, int wn, char *lds,
+                                      f32x16_t (&acc)[NMB > 0 ? NMB : 1][2]) {
+  const int KT = K / BK;
+  const int h = lane >> 5;
+  auto loadA = [&](int kt, int u) __attribute__((always_inline)) {
+    char *st = lds + (kt & 1) * SLOT_BYTES;
+    if (u < nA)
+      __builtin_amdgcn_global_load_lds((const void *)(abase + (size_t)kt * BK + src.aoff[u]),
+                                       (lds_void *)(st + (wave + 8 * u) * 1024), 16, 0, 0);
+  };
+  auto loadB = [&](int kt, int u) __attribute__((always_inline)) {
+    char *st = lds + (kt & 1) * SLOT_BYTES;
+    __builtin_amdgcn_global_load_lds((const void *)(bbase + (size_t)kt * BK + src.boff[u]),
+                                     (lds_void *)(st + OFF_B + (wave + 8 * u) * 1024), 16, 0, 0);
+  };
+  auto loadS = [&](int kt) __attribute__((always_inline)) {  // four scale bytes per row and K step
+    char *st = lds + (kt & 1) * SLOT_BYTES;
+    if (lane < 32) {
+      __builtin_amdgcn_global_load_lds((const void *)(asb + (size_t)kt * 4 + src.asoff),
+                                       (lds_void *)(st + OFF_AS + wave * 128), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(bsb + (size_t)kt * 4 + src.bsoff),
+                                       (lds_void *)(st + OFF_BS + wave * 128), 4, 0, 0);
+    }
+  };
+  auto step = [&](int kt, bool next) __attribute__((always_inline)) {
+    const char *st = lds + (kt & 1) * SLOT_BYTES;
+    const char *A = st, *B = st + OFF_B;
+    uint32_t sa[NMB > 0 ? NMB : 1], sb[2];
+    if constexpr (NMB > 0) {
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        sb[j] = *(const uint32_t *)(st + OFF_BS + (wn * 64 + j * 32 + (lane & 31)) * 4) >> (8 * h);
+#pragma unroll
+      for (int i = 0; i < NMB; i++) sa[i] = *(const uint32_t *)(st + OFF_AS + (arow0 + i * 32 + (lane & 31)) * 4) >> (8 * h);
+    }
+    // one 64-k half of the K step; KK is a compile-time constant (the scale byte selector must be)
+    auto half_step = [&](auto KKC) __attribute__((always_inline)) {
+      constexpr int kk = decltype(KKC)::value;
+      v8i_t bf[2], af[NMB > 0 ? NMB : 1];
+      if constexpr (NMB > 0) {
+        auto frag = [&](const char *base, int row) __attribute__((always_inline)) {
+          const u32x4_t lo = *(const u32x4_t *)(base + lds_off64(row, 4 * kk + h));
+          const u32x4_t hi = *(const u32x4_t *)(base + lds_off64(row, 4 * kk + 2 + h));
+          v8i_t v;
+          v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+          return v;
+        };
+#pragma unroll
+        for (int j = 0; j < 2; j++) bf[j] = frag(B, wn * 64 + j * 32 + (lane & 31));
+#pragma unroll
+        for (int i = 0; i < NMB; i++) af[i] = frag(A, arow0 + i * 32 + (lane & 31));
+      }
+      if (next) {
+        if constexpr (kk == 0) {
+#pragma unroll
+          for (int u = 0; u < 3; u++) loadA(kt + 1, u);
+          loadS(kt + 1);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; u++) loadB(kt + 1, u);
+        }
+      }
+      if constexpr (NMB > 0) {
+#pragma unroll
+        for (int i = 0; i < NMB; i++)
+#pragma unroll
+          for (int j = 0; j < 2; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 2 * kk, sa[i],
+                                                                        2 * kk, sb[j]);
+      }
+    };
+    half_step(std::integral_constant<int, 0>{});
+    half_step(std::integral_constant<int, 1>{});
+  };
+#pragma unroll
+  for (int u = 0; u < 3; u++) loadA(0, u);
+  loadS(0);
+#pragma unroll
+  for (int u = 0; u < 4; u++) loadB(0, u);
+  for (int kt = 0; kt < KT; kt++) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier_no_fence();
+    step(kt, kt + 1 < KT);
+  }
+}
+
+template <int MODE, bool ATOMIC, int NMB>
+__device__ __forceinline__ void body(const MxParams &mp, const char *abase, const char *bbase, const uint8_t *asb,
+                                     const uint8_t *bsb, const Src &src, int nA, int K, int nt, int rbase, int mvalid,
+                                     int wave, int lane, int arow0, int wn, char *lds) {
+  const TileParams &p = mp.tp;
+  constexpr int NA = NMB > 0 ? NMB : 1;
+  f32x16_t acc[NA][2];
+#pragma unroll
+  for (int i = 0; i < NA; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+  kloop<NMB>(abase, bbase, asb, bsb, src, nA, K, wave, lane, arow0, wn, lds, acc);
+  if constexpr (NMB > 0) {
+    // acc[i][j][r] at lane l is tile row arow0 + i*32 + 8*(r/4) + 4*(l/32) + r%4,
+    // weight row wn*64 + j*32 + l%32 of the tile
+    if constexpr (MODE == 0) {
+      const int col = nt * 128 + wn * 32 + (lane & 31);  // intermediate index; I % 128 == 0
+      uint8_t *hq = (uint8_t *)p.out;
+      const int ib = p.I / 32;
+#pragma unroll
+      for (int i = 0; i < NA; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
+          const uint32_t s = mx_scale_of(halfwave_amax(hv));  // every lane joins the shuffles
+          if (m < mvalid) {
+            const size_t row = (size_t)(rbase + m);
+            hq[row * p.I + col] = (uint8_t)e4m3_encode(ldexpf(hv, 127 - (int)s));
+            if ((lane & 31) == 0) mp.out_scales[row * ib + col / 32] = (uint8_t)s;
+          }
+        }
+    } else {
+      float *out = (float *)p.out;
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int n = nt * BN + wn * 64 + j * 32 + (lane & 31);
+        if (n >= p.H) continue;
+#pragma unroll
+        for (int i = 0; i < NA; i++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m < mvalid) {
+              const int row = rbase + m;
+              if constexpr (ATOMIC) atomicAdd(out + (size_t)p.row_token[row] * p.H + n, p.row_w[row] * acc[i][j][r]);
+              else out[(size_t)row * p.H + n] = acc[i][j][r];
+            }
+          }
+      }
+    }
+  }
+}
+
+// MODE 0: gate/up + SwiGLU -> h (MXFP8).  MODE 1: down + combine epilogue.
+// GATHER (mode 0): A row r is a[row_token[r]].  ATOMIC (mode 1): fused combine.
+template <int MODE, bool GATHER, bool ATOMIC>
+__global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  const TileParams &p = mp.tp;
+  const int K = MODE == 0 ? p.H : p.I;
+  const int Nw = MODE == 0 ? 2 * p.I : p.H;
+  const int NT = MODE == 0 ? p.I / 128 : (p.H + BN - 1) / BN;
+  int e, nt, mt, mtiles;
+  if (!ffn::locate_tile<BM>(p, NT, e, nt, mt, mtiles)) return;
+  const int beg = p.offsets[e], cnt = p.offsets[e + 1] - beg;
+  const int trows = __builtin_amdgcn_readfirstlane(min(BM, (((cnt + mtiles - 1) / mtiles) + 63) & ~63));
+  const int r0 = beg + mt * trows;
+  const int rows = min(trows, min(beg + cnt, p.R_cap) - r0);
+  if (rows <= 0) return;
+  const int half = trows >> 1;
+  const int nA = trows >> 6;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int mvalid = rows - wm * half;
+  const int nmb = __builtin_amdgcn_readfirstlane(mvalid <= 0 ? 0 : min(half >> 5, (mvalid + 31) >> 5));
+
+  const int kb = K / 32;  // scale bytes per row
+  auto a_row = [&](int row) -> uint32_t {  // source row of tile row ``row`` (rows past the end repeat the last)
+    const int r = r0 + min(row, rows - 1);
+    return (MODE == 0 && GATHER) ? (uint32_t)p.row_token[r] : (uint32_t)r;
+  };
+  auto w_row = [&](int row) -> int {  // weight row of tile row ``row``
+    if constexpr (MODE == 0) return ((row >> 5) & 1) * p.I + nt * 128 + (row >> 6) * 32 + (row & 31);
+    else return min(nt * BN + row, p.H - 1);
+  };
+  Src src;
+  const char *abase = (const char *)p.a;
+  const char *bbase = (const char *)p.w + (size_t)e * Nw * K;
+  const uint8_t *asb = mp.a_scales;
+  const uint8_t *bsb = mp.w_scales + (size_t)e * Nw * kb;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int row = (wave + 8 * u) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    if (u < 3) src.aoff[u] = a_row(row) * (uint32_t)K + (uint32_t)chunk * 16u;
+    src.boff[u] = (uint32_t)w_row(row) * (uint32_t)K + (uint32_t)chunk * 16u;
+  }
+  {
+    const int row = wave * 32 + (lane & 31);
+    src.asoff = a_row(row) * (uint32_t)kb;
+    src.bsoff = (uint32_t)w_row(row) * (uint32_t)kb;
+  }
+  const int arow0 = wm * half;
+  const int rbase = r0 + arow0;
+#define MX_BODY(n) body<MODE, ATOMIC, n>(mp, abase, bbase, asb, bsb, src, nA, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
+  switch (nmb) {
+    case 0: MX_BODY(0); break;
+    case 1: MX_BODY(1); break;
+    case 2: MX_BODY(2); break;
+    default: MX_BODY(3); break;
+  }
+#undef MX_BODY
+}
+
+template <int MODE, bool GATHER, bool ATOMIC>
+hipError_t launch_m(const MxParams &mp, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((ffn_mx_kernel<MODE, GATHER, ATOMIC>), dim3(grid), dim3(NTHR), 0, s, mp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t ffn_mx_h_bytes(int R_cap, int I) { return align_up((size_t)R_cap * (size_t)I, 256); }
+
+hipError_t launch_ffn_mx(const FfnMxArgs &a, hipStream_t s) {
+  if (a.R_cap == 0 || a.T == 0) return hipSuccess;
+  hipError_t err = hipSuccess;
+  const long long mt1 = ((long long)a.R_cap + (long long)a.El * (BM - 1)) / BM;
+  const long long mt2 = (long long)a.El * ceil_div_i(a.T, BM);
+  const long long max_mt = mt1 < mt2 ? mt1 : mt2;
+  uint8_t *hq = (uint8_t *)a.ws;
+  uint8_t *hs = hq + ffn_mx_h_bytes(a.R_cap, a.I);
+  MxParams mp{};
+  mp.tp.offsets = a.offsets;
+  mp.tp.row_token = a.row_token;
+  mp.tp.row_w = a.row_w;
+  mp.tp.El = a.El;
+  mp.tp.H = a.H;
+  mp.tp.I = a.I;
+  mp.tp.R_cap = a.R_cap;
+  if (a.phase & 1) {
+    MxParams m = mp;
+    m.tp.a = a.a;
+    m.a_scales = a.a_s;
+    m.tp.w = a.wgu;
+    m.w_scales = a.wgu_s;
+    m.tp.out = hq;
+    m.out_scales = hs;
+    const int grid = (int)(max_mt * (a.I / 128));
+    err = a.gather ? launch_m<0, true, false>(m, grid, s) : launch_m<0, false, false>(m, grid, s);
+    if (err != hipSuccess) return err;
+  }
+  if (a.phase & 2) {
+    MxParams m = mp;
+    m.tp.a = hq;
+    m.a_scales = hs;
+    m.tp.w = a.wd;
+    m.w_scales = a.wd_s;
+    const bool atomic = a.y != nullptr;
+    m.tp.out = atomic ? (void *)a.y : (void *)a.y_perm;
+    const int grid = (int)(max_mt * ceil_div_i(a.H, BN));
+    err = atomic ? launch_m<1, false, true>(m, grid, s) : launch_m<1, false, false>(m, grid, s);
+  }
+  return err;
+}

@@ -16,14 +16,15 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP8 = 0, 1, 2, 3
 MOE_FFN_GATHER, MOE_FFN_ZERO_Y, MOE_FFN_ONLY_GATE_UP, MOE_FFN_ONLY_DOWN = 1, 2, 4, 8
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE", -4: "MOE_ERR_WORKSPACE",
           -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIGN"}
 
 # Every symbol moe.h declares (checked by the CPU test suite).
 EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_permute_workspace_size",
-           "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine")
+           "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_quantize_mx", "moe_ffn_mx_workspace_size",
+           "moe_grouped_ffn_mx")
 
 
 class MoEError(RuntimeError):
@@ -59,6 +60,12 @@ def lib():
         L.moe_grouped_ffn.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, P, Z, ctypes.c_uint, P]
         L.moe_combine.restype = I
         L.moe_combine.argtypes = [P, P, P, I, I, I, P, P]
+        L.moe_quantize_mx.restype = I
+        L.moe_quantize_mx.argtypes = [P, I, I, I, P, P, P]
+        L.moe_ffn_mx_workspace_size.restype = Z
+        L.moe_ffn_mx_workspace_size.argtypes = [I, I]
+        L.moe_grouped_ffn_mx.restype = I
+        L.moe_grouped_ffn_mx.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, Z, ctypes.c_uint, P]
         _lib = L
     return _lib
 
@@ -173,6 +180,43 @@ def moe_grouped_ffn(a: torch.Tensor, offsets: torch.Tensor, row_token: torch.Ten
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(
         _ptr(a), adt, _ptr(offsets), _ptr(row_token), _ptr(row_w), El, T, R_cap, H, I, _ptr(w_gate_up),
         _ptr(w_down), _dtype(w_gate_up), _ptr(s_gate_up), _ptr(s_down), _ptr(y), _ptr(y_perm), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), flags, _stream(stream)))
+    return y if y is not None else y_perm
+
+
+def moe_quantize_mx(x: torch.Tensor, codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                    stream=None):
+    """MXFP8 quantisation of a [rows, K] fp32/bf16 tensor -> (codes uint8 [rows, K], scales uint8 [rows, K/32])."""
+    rows, K = x.shape
+    if codes is None:
+        codes = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    _check("moe_quantize_mx", lib().moe_quantize_mx(_ptr(x), _dtype(x), rows, K, _ptr(codes), _ptr(scales),
+                                                    _stream(stream)))
+    return codes, scales
+
+
+def moe_ffn_mx_workspace_size(R_cap: int, I: int) -> int:
+    return int(lib().moe_ffn_mx_workspace_size(R_cap, I))
+
+
+def moe_grouped_ffn_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, offsets: torch.Tensor, row_token: torch.Tensor,
+                       row_w: torch.Tensor, T: int, R_cap: int, wgu_codes: torch.Tensor, wgu_scales: torch.Tensor,
+                       wd_codes: torch.Tensor, wd_scales: torch.Tensor, y: Optional[torch.Tensor] = None,
+                       y_perm: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       gather: bool = True, zero_y: bool = True, phase: str = "both", stream=None):
+    """W8A8 MXFP8 SwiGLU expert FFN (activations and weights as MX codes + E8M0 scales)."""
+    El, twoI, H = wgu_codes.shape
+    I = twoI // 2
+    need = moe_ffn_mx_workspace_size(R_cap, I)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a_codes.device)
+    flags = (MOE_FFN_GATHER if gather else 0) | (MOE_FFN_ZERO_Y if zero_y else 0)
+    flags |= {"both": 0, "gate_up": MOE_FFN_ONLY_GATE_UP, "down": MOE_FFN_ONLY_DOWN}[phase]
+    _check("moe_grouped_ffn_mx", lib().moe_grouped_ffn_mx(
+        _ptr(a_codes), _ptr(a_scales), _ptr(offsets), _ptr(row_token), _ptr(row_w), El, T, R_cap, H, I,
+        _ptr(wgu_codes), _ptr(wgu_scales), _ptr(wd_codes), _ptr(wd_scales), _ptr(y), _ptr(y_perm), _ptr(workspace),
         workspace.numel() * workspace.element_size(), flags, _stream(stream)))
     return y if y is not None else y_perm
 

@@ -54,7 +54,7 @@ class LayerConfig:
     k: int
     I: int
     act: str = "bf16"          # 'f32' | 'bf16'  (activations and router weight)
-    wdt: str = "bf16"          # 'f32' | 'bf16' | 'fp8' (expert weights)
+    wdt: str = "bf16"          # 'f32' | 'bf16' | 'fp8' | 'mxfp8' (expert weights)
     e_begin: int = 0
     e_end: Optional[int] = None  # None -> E
     bias: str = "none"         # 'none' | 'zipf'
@@ -93,6 +93,8 @@ CONFIGS = {
     "prefill": LayerConfig("prefill", T=6000, H=4096, E=128, k=8, I=1536, seed=3),
     "skew": LayerConfig("skew", T=6000, H=4096, E=128, k=8, I=1536, bias="zipf", seed=4),
     "ep_share": LayerConfig("ep_share", T=8192, H=4096, E=128, k=8, I=1536, wdt="fp8", e_begin=0, e_end=32, seed=5),
+    # W8A8 MXFP8 variant of the prefill layer (weights converted offline, activations on the fly)
+    "prefill_mx": LayerConfig("prefill_mx", T=6000, H=4096, E=128, k=8, I=1536, wdt="mxfp8", seed=6),
 }
 
 
@@ -152,6 +154,20 @@ def quantize_e4m3_per_row(w: np.ndarray):
     return codes, scale
 
 
+def quantize_mx_blocks(w: np.ndarray):
+    """Offline MXFP8 conversion of float32 weights along the last axis (blocks of 32):
+    scale byte s = clip(floor(log2 amax) - 8 + 127, 0, 254) (0 for an all-zero block),
+    code = RNE-saturate(w / 2^(s-127)).  Returns (codes uint8, scales uint8 [..., K/32])."""
+    w = np.asarray(w, dtype=np.float32)
+    K = w.shape[-1]
+    blocks = w.astype(np.float64).reshape(w.shape[:-1] + (K // 32, 32))
+    amax = np.max(np.abs(blocks), axis=-1)
+    _, ex = np.frexp(amax)
+    s = np.where(amax > 0, np.clip(ex - 1 - 8 + 127, 0, 254), 0).astype(np.int64)
+    codes = _encode_e4m3(blocks * np.ldexp(1.0, 127 - s)[..., None])
+    return codes.reshape(w.shape), s.astype(np.uint8)
+
+
 def zipf_logit_bias(E: int, s: float = 1.2, scale: float = 2.0) -> np.ndarray:
     """bias[e] = scale * ln(p_{e+1}), p_r = r^-s / sum_{r=1..E} r^-s (fp64, stored fp32)."""
     r = np.arange(1, E + 1, dtype=np.float64)
@@ -205,6 +221,10 @@ def gen_expert(cfg: LayerConfig, e: int):
         qgu, s_gu = quantize_e4m3_per_row(gu)
         qd, s_d = quantize_e4m3_per_row(dn)
         return qgu, qd, s_gu, s_d
+    if cfg.wdt == "mxfp8":
+        qgu, s_gu = quantize_mx_blocks(gu)
+        qd, s_d = quantize_mx_blocks(dn)
+        return qgu, qd, s_gu, s_d
     return _store(gu, cfg.wdt), _store(dn, cfg.wdt), None, None
 
 
@@ -223,12 +243,15 @@ def make_inputs(cfg: LayerConfig, experts: Optional[list] = None, with_weights: 
     out["bias"] = zipf_logit_bias(cfg.E, cfg.zipf_s, cfg.bias_scale) if cfg.bias == "zipf" else None
     if not with_weights:
         return out
-    wd = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[cfg.wdt]
+    wd = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "mxfp8": np.uint8}[cfg.wdt]
     El = cfg.E_loc
     w_gu = np.zeros((El, 2 * cfg.I, cfg.H), dtype=wd)
     w_d = np.zeros((El, cfg.H, cfg.I), dtype=wd)
     s_gu = np.ones((El, 2 * cfg.I), dtype=np.float32) if cfg.wdt == "fp8" else None
     s_d = np.ones((El, cfg.H), dtype=np.float32) if cfg.wdt == "fp8" else None
+    if cfg.wdt == "mxfp8":  # E8M0 block scales along the contraction axis
+        s_gu = np.zeros((El, 2 * cfg.I, cfg.H // 32), dtype=np.uint8)
+        s_d = np.zeros((El, cfg.H, cfg.I // 32), dtype=np.uint8)
     ids = list(range(cfg.lo, cfg.hi)) if experts is None else sorted(set(int(e) for e in experts if cfg.lo <= e < cfg.hi))
 
     def one(e):

@@ -37,7 +37,10 @@
  *    synchronisation of the stream.  NaN/Inf input values are not checked.
  *  - Element types: MOE_F32 (float), MOE_BF16 (bfloat16 bit patterns, uint16),
  *    MOE_FP8_E4M3 (OCP E4M3 codes, uint8; only for expert weights, always with
- *    fp32 per-output-channel scales).
+ *    fp32 per-output-channel scales), MOE_MXFP8 (OCP microscaling: E4M3 codes,
+ *    uint8, plus one E8M0 scale byte 2^(s-127) per 32 consecutive values along
+ *    the contraction axis, in a separate uint8 array [rows, K/32]; used by
+ *    moe_quantize_mx and moe_grouped_ffn_mx).
  *  - Sizes: T >= 0 tokens, hidden H, E experts with 1 <= k <= min(E, 32),
  *    E <= 512, intermediate I.  Local experts are [e_begin, e_end) with
  *    E_loc = e_end - e_begin >= 1; R_cap = T * min(k, E_loc) bounds the number
@@ -58,6 +61,7 @@ extern "C" {
 #define MOE_F32 0
 #define MOE_BF16 1
 #define MOE_FP8_E4M3 2
+#define MOE_MXFP8 3
 
 /* status codes */
 #define MOE_OK 0
@@ -190,6 +194,53 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
                     const void *w_gate_up, const void *w_down, int w_dtype,
                     const float *s_gate_up, const float *s_down, float *y, float *y_perm,
                     void *workspace, size_t workspace_bytes, unsigned flags, void *stream);
+
+/*
+ * moe_quantize_mx - MXFP8 quantisation of a row-major matrix along its rows.
+ *
+ * Defined by: "Hosting Qwen on Blackwell", section "Quantization" (the deployed
+ * model runs MXFP8: 8-bit E4M3 values sharing a power-of-two scale per block of
+ * 32); the block rule below is the reading this library takes of it.
+ *
+ * For every row r and block b (values v = x[r, 32b .. 32b+31]):
+ *   amax = max |v|;  s = amax == 0 ? 0 : clamp(floor(log2 amax) - 8 + 127, 0, 254)
+ *   scales[r, b] = s;  codes[r, 32b+i] = E4M3 code nearest to v_i / 2^(s-127),
+ *   ties to the even code, magnitudes >= 448 saturate to 448, sign bit kept.
+ * x: rows x K, MOE_F32 or MOE_BF16; codes [rows, K] uint8; scales [rows, K/32]
+ * uint8.  K must be a multiple of 32 and rows >= 0.  Errors: MOE_ERR_NULL,
+ * MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_HIP.
+ */
+int moe_quantize_mx(const void *x, int x_dtype, int rows, int K, uint8_t *codes, uint8_t *scales, void *stream);
+
+/* Bytes of workspace moe_grouped_ffn_mx needs (h as MXFP8: R_cap*I codes and R_cap*I/32 scales). */
+size_t moe_ffn_mx_workspace_size(int R_cap, int I);
+
+/*
+ * moe_grouped_ffn_mx - the SwiGLU expert FFN of moe_grouped_ffn in W8A8 MXFP8.
+ *
+ * Defined by: the passages of moe_grouped_ffn, with the MXFP8 format of the
+ * "Quantization" section of "Hosting Qwen on Blackwell" for activations and
+ * weights (weights converted offline, activations quantised on the fly).
+ *
+ * Same per-row definition as moe_grouped_ffn with every operand an MX tensor:
+ * a_r is row r (MOE_FFN_GATHER: row row_token[r]) of the MX activations
+ * (a_codes [rows, H], a_scales [rows, H/32], e.g. from moe_quantize_mx);
+ * weights wgu_codes [E_loc, 2I, H] + wgu_scales [E_loc, 2I, H/32] and
+ * wd_codes [E_loc, H, I] + wd_scales [E_loc, H, I/32].  G and U accumulate
+ * exact E4M3 products times their two block scales in fp32 on the fp8 matrix
+ * cores; h_r = silu(G) * U in fp32 is quantised per row with the rule of
+ * moe_quantize_mx (blocks of 32 along I) into the workspace before the down
+ * projection.  Outputs, flags and the combine are those of moe_grouped_ffn.
+ * H and I must be multiples of 128; pointers 16-byte aligned (scale arrays
+ * 4-byte aligned); workspace at least moe_ffn_mx_workspace_size(R_cap, I)
+ * bytes, 256-byte aligned.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE,
+ * MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_grouped_ffn_mx(const uint8_t *a_codes, const uint8_t *a_scales, const int32_t *offsets,
+                       const int32_t *row_token, const float *row_w, int E_loc, int T, int R_cap, int H, int I,
+                       const uint8_t *wgu_codes, const uint8_t *wgu_scales, const uint8_t *wd_codes,
+                       const uint8_t *wd_scales, float *y, float *y_perm, void *workspace,
+                       size_t workspace_bytes, unsigned flags, void *stream);
 
 /*
  * moe_combine - gate-weighted gather-sum of per-row outputs back to token order.

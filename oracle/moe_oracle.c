@@ -38,6 +38,15 @@
  *   R6 output y[t] = sum over kept j of gate_j * o_j, accumulated in fp64 and
  *      stored fp32;
  *   R7 permuted rows are ordered by (expert ascending, token ascending).
+ *   R8 MXFP8 (the OCP microscaling format the "Quantization" section of
+ *      "Hosting Qwen on Blackwell" deploys): every 32 consecutive values along
+ *      the contraction axis share one E8M0 scale 2^(s-127); with amax the
+ *      block's largest magnitude, s = clamp(floor(log2 amax) - 8 + 127, 0, 254)
+ *      (8 = exponent of the largest e4m3 power of two), s = 0 for an all-zero
+ *      block; each value becomes the e4m3 code nearest to v / 2^(s-127),
+ *      ties to the even code, magnitudes above 448 saturate to 448, the sign
+ *      bit is kept.  In the W8A8 layer x is quantised per token row, h from
+ *      its fp32 value per row, and the weights arrive already quantised.
  *
  * Everything else accumulates in fp64 over the exact stored input values.
  */
@@ -83,6 +92,73 @@ uint16_t oracle_bf16_round(float f)
     memcpy(&u, &f, sizeof u);
     uint32_t lsb = (u >> 16) & 1u;
     return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* R8: value -> e4m3 code, round to nearest, ties to the even code, saturating at 448,
+ * sign bit kept.  The positive codes 0x00..0x7E are ordered by value, so the nearest
+ * code is found by bisection over their exact values. */
+uint8_t oracle_e4m3_encode(double v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a >= oracle_e4m3_value(126))
+        return sign | 126;
+    int lo = 0, hi = 126; /* value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (oracle_e4m3_value((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dl = a - oracle_e4m3_value((uint8_t)lo), dh = oracle_e4m3_value((uint8_t)hi) - a;
+    int c = dl < dh ? lo : (dh < dl ? hi : ((lo & 1) ? hi : lo));
+    return sign | (uint8_t)c;
+}
+
+/* R8: E8M0 scale byte of a block with largest magnitude amax. */
+uint8_t oracle_mx_scale(double amax)
+{
+    if (amax == 0.0)
+        return 0;
+    int ex;
+    frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+    int s = ex - 1 - 8 + 127;
+    return (uint8_t)(s < 0 ? 0 : (s > 254 ? 254 : s));
+}
+
+/* R8: one block of n (<= 32) values -> codes and its scale byte. */
+static uint8_t mx_block(const double *v, int n, uint8_t *codes)
+{
+    double amax = 0.0;
+    for (int i = 0; i < n; i++)
+        amax = fmax(amax, fabs(v[i]));
+    uint8_t s = oracle_mx_scale(amax);
+    for (int i = 0; i < n; i++)
+        codes[i] = oracle_e4m3_encode(ldexp(v[i], 127 - (int)s));
+    return s;
+}
+
+static double elem(const void *p, int dt, size_t i);
+
+/* R8: rows x K values (f32 or bf16) -> codes [rows, K], scales [rows, K/32]; K % 32 == 0. */
+void oracle_mx_quantize(const void *x, int x_dt, int rows, int K, uint8_t *codes, uint8_t *scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; r++) {
+        double v[32];
+        for (int b = 0; b < K / 32; b++) {
+            for (int i = 0; i < 32; i++)
+                v[i] = elem(x, x_dt, (size_t)r * K + 32 * b + i);
+            scales[(size_t)r * (K / 32) + b] = mx_block(v, 32, codes + (size_t)r * K + 32 * b);
+        }
+    }
+}
+
+/* Exact value of MX element i of a row: code * 2^(scale of its block - 127). */
+static double mx_elem(const uint8_t *codes, const uint8_t *scales, size_t row, int K, int i)
+{
+    return ldexp(oracle_e4m3_value(codes[row * (size_t)K + i]), (int)scales[row * (size_t)(K / 32) + i / 32] - 127);
 }
 
 static double elem(const void *p, int dt, size_t i)
@@ -269,6 +345,115 @@ void oracle_layer_tokens(const int32_t *tokens, int n_tok, const void *x, int x_
         free(yacc);
         free(xt);
         free(hb);
+    }
+}
+
+/* R5 + R6 + R8, token-major, W8A8 MXFP8: x is quantised per token row, each selected
+ * local expert runs on the quantised row with MX weights (codes [E_loc, 2I, H] and
+ * [E_loc, H, I], scales [E_loc, 2I, H/32] and [E_loc, H, I/32]); h is computed in fp64,
+ * rounded to fp32 and quantised per row (blocks of 32 along I) before the down projection. */
+void oracle_layer_tokens_mx(const int32_t *tokens, int n_tok, const void *x, int x_dt,
+                            const int32_t *topk_ids, const float *topk_w, int H, int k,
+                            int e_begin, int e_end, int I, const uint8_t *wgu_q, const uint8_t *wgu_s,
+                            const uint8_t *wd_q, const uint8_t *wd_s, float *y_out)
+{
+#pragma omp parallel
+    {
+        double *yacc = (double *)malloc(sizeof(double) * (size_t)H);
+        double *xv = (double *)malloc(sizeof(double) * (size_t)H);
+        double *xq = (double *)malloc(sizeof(double) * (size_t)H);
+        double *hv = (double *)malloc(sizeof(double) * (size_t)I);
+        double *hq = (double *)malloc(sizeof(double) * (size_t)I);
+        uint8_t codes[32];
+#pragma omp for schedule(dynamic, 1)
+        for (int q = 0; q < n_tok; q++) {
+            int t = tokens[q];
+            for (int n = 0; n < H; n++) {
+                yacc[n] = 0.0;
+                xv[n] = elem(x, x_dt, (size_t)t * H + n);
+            }
+            for (int b = 0; b < H / 32; b++) {
+                uint8_t sb = mx_block(xv + 32 * b, 32, codes);
+                for (int i = 0; i < 32; i++)
+                    xq[32 * b + i] = ldexp(oracle_e4m3_value(codes[i]), (int)sb - 127);
+            }
+            for (int j = 0; j < k; j++) {
+                int e = topk_ids[(size_t)t * k + j];
+                if (e < e_begin || e >= e_end)
+                    continue; /* R4 */
+                size_t le = (size_t)(e - e_begin);
+                double g = (double)topk_w[(size_t)t * k + j];
+                for (int i = 0; i < I; i++) {
+                    double G = 0.0, U = 0.0;
+                    size_t rg = le * 2 * I + i, ru = le * 2 * I + I + i;
+                    for (int h = 0; h < H; h++) {
+                        G += xq[h] * mx_elem(wgu_q, wgu_s, rg, H, h);
+                        U += xq[h] * mx_elem(wgu_q, wgu_s, ru, H, h);
+                    }
+                    hv[i] = (double)(float)(G / (1.0 + exp(-G)) * U);
+                }
+                for (int b = 0; b < I / 32; b++) {
+                    uint8_t sb = mx_block(hv + 32 * b, 32, codes);
+                    for (int i = 0; i < 32; i++)
+                        hq[32 * b + i] = ldexp(oracle_e4m3_value(codes[i]), (int)sb - 127);
+                }
+                for (int n = 0; n < H; n++) {
+                    double o = 0.0;
+                    size_t rd = le * H + n;
+                    for (int i = 0; i < I; i++)
+                        o += hq[i] * mx_elem(wd_q, wd_s, rd, I, i);
+                    yacc[n] += g * o;
+                }
+            }
+            for (int n = 0; n < H; n++)
+                y_out[(size_t)q * H + n] = (float)yacc[n];
+        }
+        free(yacc);
+        free(xv);
+        free(xq);
+        free(hv);
+        free(hq);
+    }
+}
+
+/* R5 + R8, per assignment row: the MXFP8 intermediate of row r (token row_token[r], local
+ * expert row_expert[r]), exactly as oracle_layer_tokens_mx forms it before the down
+ * projection: h_codes [R, I], h_scales [R, I/32]. */
+void oracle_h_mx(const int32_t *row_token, const int32_t *row_expert, int R, const void *x, int x_dt, int H, int I,
+                 const uint8_t *wgu_q, const uint8_t *wgu_s, uint8_t *h_codes, uint8_t *h_scales)
+{
+#pragma omp parallel
+    {
+        double *xq = (double *)malloc(sizeof(double) * (size_t)H);
+        double *xv = (double *)malloc(sizeof(double) * (size_t)H);
+        double *hv = (double *)malloc(sizeof(double) * (size_t)I);
+        uint8_t codes[32];
+#pragma omp for schedule(dynamic, 4)
+        for (int r = 0; r < R; r++) {
+            int t = row_token[r];
+            size_t le = (size_t)row_expert[r];
+            for (int n = 0; n < H; n++)
+                xv[n] = elem(x, x_dt, (size_t)t * H + n);
+            for (int b = 0; b < H / 32; b++) {
+                uint8_t sb = mx_block(xv + 32 * b, 32, codes);
+                for (int i = 0; i < 32; i++)
+                    xq[32 * b + i] = ldexp(oracle_e4m3_value(codes[i]), (int)sb - 127);
+            }
+            for (int i = 0; i < I; i++) {
+                double G = 0.0, U = 0.0;
+                size_t rg = le * 2 * I + i, ru = le * 2 * I + I + i;
+                for (int h = 0; h < H; h++) {
+                    G += xq[h] * mx_elem(wgu_q, wgu_s, rg, H, h);
+                    U += xq[h] * mx_elem(wgu_q, wgu_s, ru, H, h);
+                }
+                hv[i] = (double)(float)(G / (1.0 + exp(-G)) * U);
+            }
+            for (int b = 0; b < I / 32; b++)
+                h_scales[(size_t)r * (I / 32) + b] = mx_block(hv + 32 * b, 32, h_codes + (size_t)r * I + 32 * b);
+        }
+        free(xq);
+        free(xv);
+        free(hv);
     }
 }
 

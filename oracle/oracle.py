@@ -64,6 +64,13 @@ def lib():
         L.oracle_layer_tokens.argtypes = [P, i, P, i, P, P, i, i, i, i, i, i, P, P, i, P, P, i, P]
         L.oracle_combine.argtypes = [P, P, P, i, i, i, P]
         L.oracle_num_threads.restype = i
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        L.oracle_mx_scale.restype = ctypes.c_uint8
+        L.oracle_mx_scale.argtypes = [ctypes.c_double]
+        L.oracle_mx_quantize.argtypes = [P, i, i, i, P, P]
+        L.oracle_layer_tokens_mx.argtypes = [P, i, P, i, P, P, i, i, i, i, i, P, P, P, P, P]
+        L.oracle_h_mx.argtypes = [P, P, i, P, i, i, i, P, P, P, P]
         _lib = L
     return _lib
 
@@ -156,6 +163,68 @@ def layer_tokens(tokens, x, topk_ids, topk_w, e_begin: int, e_end: int, w_gate_u
     lib().oracle_layer_tokens(_p(tok), len(tok), _p(x), _dt_of(x), _p(ids), _p(w), T, H, k, e_begin, e_end, I,
                               _p(wgu), _p(wd), _dt_of(wgu), _p(sgu), _p(sd), 1 if round_h else 0, _p(y))
     return y
+
+
+def e4m3_encode(v: float) -> int:
+    """R8: nearest e4m3 code (ties to even, saturating at 448, sign kept)."""
+    return int(lib().oracle_e4m3_encode(float(v)))
+
+
+def mx_scale(amax: float) -> int:
+    """R8: E8M0 scale byte of a block whose largest magnitude is ``amax``."""
+    return int(lib().oracle_mx_scale(float(amax)))
+
+
+def mx_quantize(x) -> tuple:
+    """R8: rows x K (fp32 or bf16 bits) -> (codes uint8 [rows, K], scales uint8 [rows, K/32])."""
+    x = np.ascontiguousarray(x)
+    rows, K = x.shape
+    assert K % 32 == 0
+    codes = np.empty((rows, K), dtype=np.uint8)
+    scales = np.empty((rows, K // 32), dtype=np.uint8)
+    lib().oracle_mx_quantize(_p(x), _dt_of(x), rows, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mx_dequantize(codes, scales) -> np.ndarray:
+    """Exact values of an MX tensor (fp64)."""
+    table = np.array([e4m3_value(c) for c in range(256)])
+    v = table[np.asarray(codes)]
+    return v * np.ldexp(1.0, np.repeat(np.asarray(scales, dtype=np.int64), 32, axis=-1) - 127)
+
+
+def layer_tokens_mx(tokens, x, topk_ids, topk_w, e_begin: int, e_end: int, wgu_q, wgu_s, wd_q, wd_s) -> np.ndarray:
+    """W8A8 MXFP8 layer: y rows (fp32 [len(tokens), H]) of the listed tokens, token-major."""
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    x = np.ascontiguousarray(x)
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    wgu_q, wgu_s = np.ascontiguousarray(wgu_q, dtype=np.uint8), np.ascontiguousarray(wgu_s, dtype=np.uint8)
+    wd_q, wd_s = np.ascontiguousarray(wd_q, dtype=np.uint8), np.ascontiguousarray(wd_s, dtype=np.uint8)
+    T, H = x.shape
+    k = ids.shape[1]
+    I = wd_q.shape[2]
+    assert wgu_q.shape[1:] == (2 * I, H) and wd_q.shape[1:] == (H, I)
+    assert wgu_s.shape[1:] == (2 * I, H // 32) and wd_s.shape[1:] == (H, I // 32)
+    y = np.empty((len(tok), H), dtype=np.float32)
+    lib().oracle_layer_tokens_mx(_p(tok), len(tok), _p(x), _dt_of(x), _p(ids), _p(w), H, k, e_begin, e_end, I,
+                                 _p(wgu_q), _p(wgu_s), _p(wd_q), _p(wd_s), _p(y))
+    return y
+
+
+def h_mx(row_token, row_expert, x, wgu_q, wgu_s) -> tuple:
+    """MXFP8 intermediate (codes [R, I], scales [R, I/32]) of assignment rows (token, local expert)."""
+    rt = np.ascontiguousarray(row_token, dtype=np.int32)
+    re_ = np.ascontiguousarray(row_expert, dtype=np.int32)
+    x = np.ascontiguousarray(x)
+    wgu_q, wgu_s = np.ascontiguousarray(wgu_q, dtype=np.uint8), np.ascontiguousarray(wgu_s, dtype=np.uint8)
+    T, H = x.shape
+    I = wgu_q.shape[1] // 2
+    R = len(rt)
+    codes = np.empty((R, I), dtype=np.uint8)
+    scales = np.empty((R, I // 32), dtype=np.uint8)
+    lib().oracle_h_mx(_p(rt), _p(re_), R, _p(x), _dt_of(x), H, I, _p(wgu_q), _p(wgu_s), _p(codes), _p(scales))
+    return codes, scales
 
 
 def combine(y_perm, token_row, topk_w) -> np.ndarray:

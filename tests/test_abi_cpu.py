@@ -87,9 +87,39 @@ def ffn(**kw):
     (dict(ad=0), -3), (dict(wdt=0), -3), (dict(ad=2, wdt=2), -3),
     (dict(y=None), -1), (dict(yp=FAKE), -1), (dict(wdt=2), -1), (dict(rt=None), -1), (dict(rw=None), -1),
     (dict(ws=None), -4), (dict(wsb=10), -4), (dict(a=FAKE_ODD), -6), (dict(ws=P(0x1010)), -6),
+    (dict(T=1 << 20, R=1 << 20, H=1024), -2),
 ])
 def test_ffn_validation(kw, code):
     assert ffn(**kw) == code
+
+
+def ffn_mx(**kw):
+    a = dict(a=FAKE, as_=FAKE, off=FAKE, rt=FAKE, rw=FAKE, El=8, T=16, R=32, H=256, I=128, wgu=FAKE, wgus=FAKE,
+             wd=FAKE, wds=FAKE, y=FAKE, yp=None, ws=FAKE, wsb=1 << 30, flags=3)
+    a.update(kw)
+    return moe.lib().moe_grouped_ffn_mx(a["a"], a["as_"], a["off"], a["rt"], a["rw"], a["El"], a["T"], a["R"], a["H"],
+                                        a["I"], a["wgu"], a["wgus"], a["wd"], a["wds"], a["y"], a["yp"], a["ws"],
+                                        a["wsb"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=192), -2), (dict(I=64), -2), (dict(El=0), -2), (dict(R=16 * 8 + 1), -2), (dict(T=1 << 20, R=1 << 20, H=1024), -2),
+    (dict(y=None), -1), (dict(yp=FAKE), -1), (dict(as_=None), -1), (dict(wds=None), -1), (dict(rt=None), -1),
+    (dict(ws=None), -4), (dict(wsb=10), -4), (dict(a=FAKE_ODD), -6), (dict(as_=P(0x1002)), -6),
+    (dict(ws=P(0x1010)), -6), (dict(flags=3 | 4 | 8), -2),
+])
+def test_ffn_mx_validation(kw, code):
+    assert ffn_mx(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=48), -2), (dict(K=0), -2), (dict(rows=-1), -2), (dict(xd=2), -3), (dict(x=None), -1),
+    (dict(q=None), -1), (dict(rows=0), 0),
+])
+def test_quantize_mx_validation(kw, code):
+    a = dict(x=FAKE, xd=1, rows=4, K=64, q=FAKE, s=FAKE)
+    a.update(kw)
+    assert moe.lib().moe_quantize_mx(a["x"], a["xd"], a["rows"], a["K"], a["q"], a["s"], None) == code
 
 
 def test_workspace_size():
@@ -101,6 +131,9 @@ def test_workspace_size():
     ws = L.moe_ffn_workspace_size(48000, 128, 4096, 1536, 1)
     assert ws >= 48000 * 1536 * 2 and ws % 256 == 0
     assert L.moe_ffn_workspace_size(100, 4, 64, 64, 0) >= 100 * 64 * 4
+    # h as MXFP8: codes [R_cap, I] and scales [R_cap, I/32], each 256-byte aligned
+    ws = L.moe_ffn_mx_workspace_size(48000, 1536)
+    assert ws >= 48000 * 1536 + 48000 * 48 and ws % 256 == 0
 
 
 @pytest.mark.parametrize("kw,code", [

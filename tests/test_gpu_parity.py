@@ -17,7 +17,7 @@ import torch
 from oracle import oracle as O
 from expert_routed_grouped_amd import layer as L
 from expert_routed_grouped_amd import moe, synth
-from expert_routed_grouped_amd.synth import CONFIGS, LayerConfig
+from expert_routed_grouped_amd.synth import CONFIGS, LayerConfig, f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -375,3 +375,197 @@ def test_full_workload_layer(name):
     check_y(y2[toks], y_o, name + " (repeat)")
     del dev, bufs
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# W8A8 MXFP8: quantisation (bit-exact) and the MX grouped FFN against the MX oracle
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_quantize_mx_matches_oracle(dt):
+    rng = np.random.default_rng(301)
+    rows, K = 333, 384
+    x32 = (rng.standard_normal((rows, K)) * np.exp2(rng.integers(-20, 20, (rows, 1)))).astype(np.float32)
+    x32[0, :32] = 0.0                                  # all-zero block
+    x32[1, :32] = -0.0                                 # negative zeros keep their sign bit
+    x32[2, 0] = 500.0                                  # saturating element
+    x32[3, 5] = 1e-30                                  # flushes to a zero code inside a normal block
+    x32[4, 32:64] = np.linspace(-3, 3, 32)
+    x = f32_to_bf16_bits(x32) if dt == "bf16" else x32
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() if dt == "bf16" else torch.from_numpy(x).cuda()
+    codes, scales = moe.moe_quantize_mx(xd)
+    torch.cuda.synchronize()
+    oc, os_ = O.mx_quantize(x)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+
+
+def mx_layer(dev, cfg, ids_d, w_d, fused):
+    """The W8A8 layer on the GPU; returns (y, perm dict, MX intermediate (codes, scales) from the workspace)."""
+    p = moe.moe_permute(ids_d, w_d, cfg.E, cfg.lo, cfg.hi)
+    R_cap = p["R_cap"]
+    xq, xs = moe.moe_quantize_mx(dev["x"])
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_ffn_mx_workspace_size(R_cap, cfg.I), dtype=torch.uint8, device="cuda")
+    args = (xq, xs, p["offsets"], p["row_token"], p["row_w"], cfg.T, R_cap, dev["w_gate_up"], dev["s_gate_up"],
+            dev["w_down"], dev["s_down"])
+    if fused:
+        y.fill_(float("nan"))
+        moe.moe_grouped_ffn_mx(*args, y=y, zero_y=True, workspace=ws)
+    else:
+        yp = torch.empty((max(R_cap, 1), cfg.H), dtype=torch.float32, device="cuda")
+        moe.moe_grouped_ffn_mx(*args, y_perm=yp, workspace=ws)
+        moe.moe_combine(yp, p["token_row"], w_d, y=y)
+    torch.cuda.synchronize()
+    wsn = ws.cpu().numpy()
+    hbytes = -(-R_cap * cfg.I // 256) * 256
+    h_codes = wsn[:R_cap * cfg.I].reshape(R_cap, cfg.I)
+    h_scales = wsn[hbytes:hbytes + R_cap * cfg.I // 32].reshape(R_cap, cfg.I // 32)
+    return y.cpu().numpy(), p, (h_codes, h_scales)
+
+
+E4M3 = np.array([O.e4m3_value(c) for c in range(256)])
+U32 = 2.0 ** -24
+
+
+def h_exact_and_slack(inp, t, e, cols, I, H):
+    """Unrounded h = silu(G) * U (fp64) of token t, local expert e, intermediate columns ``cols``,
+    and a bound on how far an fp32 evaluation may stray from it: the fp32 sum of the H exact
+    products of G (or U) is within H * 2^-24 * sum|products| of the exact sum (twice that
+    allowed here), and SiLU, its product with U and the rounding of h add a few units of
+    2^-24 relative."""
+    xq, xs = O.mx_quantize(np.asarray(inp["x"])[t:t + 1])
+    xv = O.mx_dequantize(xq, xs)[0]
+    wg = O.mx_dequantize(inp["w_gate_up"][e][cols], inp["s_gate_up"][e][cols])
+    wu = O.mx_dequantize(inp["w_gate_up"][e][I + cols], inp["s_gate_up"][e][I + cols])
+    G, U = wg @ xv, wu @ xv
+    dG, dU = 2 * H * U32 * (np.abs(wg) @ np.abs(xv)), 2 * H * U32 * (np.abs(wu) @ np.abs(xv))
+    sg = G / (1.0 + np.exp(-G))
+    h = sg * U
+    slack = 1.1 * dG * np.abs(U) + np.abs(sg) * dU + dG * dU + 8 * U32 * np.abs(h)
+    return h, slack
+
+
+def check_mx_layer(cfg, inp, ids, w, y, h_gpu, tokens=None):
+    """MX parity.  h is the quantisation of an fp32 value whose last bits depend on the order
+    of the fp32 accumulation, so a GPU code may differ from the oracle's where the exact h lies
+    within that rounding noise of the boundary between two E4M3 codes (or a block scale one
+    step off where the block maximum lies that close to a power of two).  Checked: every
+    differing code is a correct rounding of some value within the fp32 error bound of the exact
+    h; every differing scale has its block maximum within that bound of the power of two
+    between; every token whose intermediate rows agree matches the oracle within 1e-2 * RMS,
+    every other token within that plus the exact effect of its differing h values through the
+    down projection.  The permutation is the oracle's (the GPU's is bit-exact)."""
+    perm = O.permute(ids, w, cfg.lo, cfg.hi)
+    R, I, H = perm["R"], cfg.I, cfg.H
+    counts = perm["counts"]
+    row_tok = perm["row_token"]
+    row_exp = np.repeat(np.arange(cfg.E_loc, dtype=np.int32), counts)
+    sel = np.arange(R) if tokens is None else np.nonzero(np.isin(row_tok, tokens))[0]
+    hq_o, hs_o = O.h_mx(row_tok[sel], row_exp[sel], inp["x"], inp["w_gate_up"], inp["s_gate_up"])
+    hq_g, hs_g = h_gpu[0][sel], h_gpu[1][sel]
+    sc_o = np.repeat(hs_o.astype(np.int64), 32, axis=1) - 127
+    sc_g = np.repeat(hs_g.astype(np.int64), 32, axis=1) - 127
+    v_o = E4M3[hq_o] * np.exp2(sc_o)
+    v_g = E4M3[hq_g] * np.exp2(sc_g)
+    sdiff = hs_g != hs_o
+    diff = v_g != v_o
+    say(f"  {cfg.name}: {int(diff.sum())} of {diff.size} h values and {int(sdiff.sum())} of {sdiff.size} "
+        f"block scales differ from the oracle's ({diff.mean() if diff.size else 0:.2e})")
+    assert np.all(np.abs(hs_g.astype(np.int64) - hs_o) <= 1), "block scale more than one step off"
+    worst = 0.0
+    for q, blk in zip(*np.nonzero(sdiff)):
+        cols = np.arange(32 * blk, 32 * blk + 32)
+        h, slack = h_exact_and_slack(inp, int(row_tok[sel[q]]), int(row_exp[sel[q]]), cols, I, H)
+        m = int(np.argmax(np.abs(h)))
+        edge = 2.0 ** (max(int(hs_o[q, blk]), int(hs_g[q, blk])) - 127 + 8)
+        worst = max(worst, abs(abs(h[m]) - edge) / slack[m])
+    # every differing value is a correct E4M3 rounding, at the GPU's block scale, of some value
+    # within the fp32 error bound of the exact h (small h, where G or U cancel, may move by
+    # several codes: the bound is absolute, the E4M3 step near zero is 2^-9 of a block unit)
+    for q in np.nonzero(diff.any(axis=1))[0]:
+        cols = np.nonzero(diff[q])[0]
+        h, slack = h_exact_and_slack(inp, int(row_tok[sel[q]]), int(row_exp[sel[q]]), cols, I, H)
+        unit = np.exp2(sc_g[q, cols].astype(np.float64))
+        code = hq_g[q, cols]
+        a = np.abs(E4M3[code])
+        step = np.where(a < 2.0 ** -6, 2.0 ** -9, np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+        dist = np.abs(h / unit - E4M3[code]) - step / 2
+        sat = ((code & 0x7F) == 0x7E) & (np.sign(h) == np.sign(E4M3[code])) & (np.abs(h) / unit >= 448)
+        dist = np.where(sat, 0.0, dist)
+        worst = max(worst, float(np.max(np.maximum(dist, 0.0) / (slack / unit))))
+    say(f"  {cfg.name}: largest distance of a differing value from its rounding boundary = "
+        f"{worst:.3f} x the fp32 error bound")
+    assert worst <= 1.0, "an h value differs where fp32 rounding cannot explain it"
+    # y: oracle rows, tolerance widened only by the differing h values of each token
+    toks = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
+    y_o = O.layer_tokens_mx(toks, inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["s_gate_up"],
+                            inp["w_down"], inp["s_down"])
+    rms = np.sqrt(np.mean(y_o.astype(np.float64) ** 2))
+    bound = np.full(len(toks), Y_TOL * rms)
+    pos = {int(t): n for n, t in enumerate(toks)}
+    wd = {}
+    for q in np.nonzero(diff.any(axis=1))[0]:
+        r = sel[q]
+        e = int(row_exp[r])
+        if e not in wd:
+            wd[e] = O.mx_dequantize(inp["w_down"][e], inp["s_down"][e])
+        cols = np.nonzero(diff[q])[0]
+        dh = np.abs(v_g[q, cols] - v_o[q, cols])
+        bound[pos[int(row_tok[r])]] += abs(perm["row_w"][r]) * np.max(np.abs(wd[e][:, cols]) @ dh)
+    err = np.max(np.abs(y[toks].astype(np.float64) - y_o), axis=1)
+    say(f"  {cfg.name}: max|err| = {err.max():.3e}, RMS = {rms:.3e}, tokens with differing h: "
+        f"{int((bound > Y_TOL * rms).sum())}")
+    assert np.all(err <= bound)
+
+
+def mx_dev(inp):
+    dev = L.to_device(inp)
+    for kname in ("s_gate_up", "s_down"):
+        dev[kname] = torch.from_numpy(np.ascontiguousarray(inp[kname])).cuda()
+    return dev
+
+
+MX_CASES = [
+    # several M and N tiles with ragged expert counts; N tail of the down projection (H % 256 == 128)
+    LayerConfig("mx_small", T=700, H=384, E=6, k=3, I=256, wdt="mxfp8", seed=302, w_std=0.05),
+    LayerConfig("mx_local", T=500, H=256, E=8, k=2, I=384, wdt="mxfp8", e_begin=2, e_end=6, seed=303, w_std=0.05),
+]
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "combine"])
+@pytest.mark.parametrize("cfg", MX_CASES, ids=lambda c: c.name)
+def test_layer_mx_matches_oracle(cfg, fused):
+    inp = host_inputs(cfg)
+    dev = mx_dev(inp)
+    ids, w = oracle_routing(cfg)
+    say(f"layer {cfg.name} fused={fused}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} MXFP8")
+    ids_d, w_d = to_dev_routing(ids, w)
+    y, p, h = mx_layer(dev, cfg, ids_d, w_d, fused)
+    check_mx_layer(cfg, inp, ids, w, y, h)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "combine"])
+def test_layer_mx_tile_boundaries(fused):
+    counts = TILE_COUNTS
+    cfg = LayerConfig("mx_tiles", T=1000, H=256, E=len(counts), k=5, I=256, wdt="mxfp8", seed=304, w_std=0.05)
+    inp = host_inputs(cfg)
+    dev = mx_dev(inp)
+    ids, w = constructed_routing(counts, cfg.T, cfg.k, seed=305)
+    ids_d, w_d = to_dev_routing(ids, w)
+    y, p, h = mx_layer(dev, cfg, ids_d, w_d, fused)
+    assert p["counts"].cpu().tolist() == counts
+    check_mx_layer(cfg, inp, ids, w, y, h)
+
+
+def test_full_workload_layer_mx():
+    cfg = CONFIGS["prefill_mx"]
+    ids, w = oracle_routing(cfg)
+    toks = sample_tokens(cfg, ids)
+    used = sorted(set(int(e) for e in ids[toks].ravel()))
+    inp = synth.make_inputs(cfg)
+    dev = mx_dev(inp)
+    say(f"full MX layer {cfg.name}: T={cfg.T}, sampled tokens {toks.tolist()}")
+    ids_d, w_d = to_dev_routing(ids, w)
+    y, p, h = mx_layer(dev, cfg, ids_d, w_d, fused=False)
+    assert len(used) > 0
+    check_mx_layer(cfg, inp, ids, w, y, h, tokens=toks)

@@ -41,6 +41,15 @@ MUTANTS = {
     "bf16_round_truncates": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "return (uint16_t)((u + 0u * lsb) >> 16);"),
     "combine_ignores_gate": ("acc += (double)topk_w[(size_t)t * k + j] * (double)y_perm[(size_t)r * H + n];",
                              "acc += (double)y_perm[(size_t)r * H + n];"),
+    "mx_emax_7": ("int s = ex - 1 - 8 + 127;", "int s = ex - 1 - 7 + 127;"),
+    "e4m3_ties_away_from_zero": ("(lo & 1) ? hi : lo", "hi"),
+    "e4m3_overflow_to_nan": ("        return sign | 126;\n    int lo", "        return sign | 127;\n    int lo"),
+    "mx_x_not_quantised": ("xq[32 * b + i] = ldexp(oracle_e4m3_value(codes[i]), (int)sb - 127);",
+                           "xq[32 * b + i] = xv[32 * b + i];"),
+    "mx_h_not_quantised": ("hq[32 * b + i] = ldexp(oracle_e4m3_value(codes[i]), (int)sb - 127);",
+                           "hq[32 * b + i] = hv[32 * b + i];"),
+    "mx_weight_scale_wrong_block": ("return ldexp(oracle_e4m3_value(codes[row * (size_t)K + i]), (int)scales[row * (size_t)(K / 32) + i / 32] - 127);",
+                                    "return ldexp(oracle_e4m3_value(codes[row * (size_t)K + i]), (int)scales[row * (size_t)(K / 32) + (i / 32 + 1) % (K / 32)] - 127);"),
     "combine_gate_added_not_multiplied": ("acc += (double)topk_w[(size_t)t * k + j] * (double)y_perm[(size_t)r * H + n];",
                                           "acc += (double)topk_w[(size_t)t * k + j] + (double)y_perm[(size_t)r * H + n];"),
 }

@@ -426,3 +426,140 @@ def test_decode_routing_touches_about_E_U_experts():
     assert 120 <= U <= 128
     p = O.permute(ids, np.ones_like(ids, dtype=np.float32), 0, cfg.E)
     assert p["counts"].sum() == 512
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 (R8): e4m3 encoding, E8M0 block scales, W8A8 layer
+# ----------------------------------------------------------------------------
+def torch_e4m3_codes(v):
+    """torch's own float -> float8_e4m3fn conversion (RNE; finite for |v| <= 464)."""
+    return torch.from_numpy(np.asarray(v, dtype=np.float64)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encode_matches_torch_rne_in_range():
+    # catches: ties away from zero, truncation, wrong subnormal step, lost sign
+    rng = np.random.default_rng(11)
+    mags = np.concatenate([rng.uniform(0, 2.0 ** -6, 3000), np.exp2(rng.uniform(-6, 8.85, 6000))])
+    v = mags * rng.choice([-1.0, 1.0], mags.size)
+    # every midpoint between adjacent codes (exact ties) and every code value itself
+    vals = np.array([O.e4m3_value(c) for c in range(127)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    v = np.concatenate([v, mids, -mids, vals, -vals])
+    v = v[np.abs(v) < 464]
+    ours = np.array([O.e4m3_encode(x) for x in v], dtype=np.uint8)
+    assert np.array_equal(ours, torch_e4m3_codes(v))
+
+
+def test_e4m3_encode_closed_forms_and_saturation():
+    # catches: NaN instead of saturation, missing sign on saturation, sign of zero
+    assert O.e4m3_encode(1.0) == 0x38 and O.e4m3_encode(448.0) == 0x7E
+    assert O.e4m3_encode(500.0) == 0x7E and O.e4m3_encode(1e30) == 0x7E and O.e4m3_encode(-1e30) == 0xFE
+    assert O.e4m3_encode(0.0) == 0x00 and O.e4m3_encode(-0.0) == 0x80
+    assert O.e4m3_encode(2.0 ** -9) == 0x01                 # smallest subnormal
+    assert O.e4m3_encode(2.0 ** -10) == 0x00                # tie between 0 and 2^-9 -> even code 0
+    assert O.e4m3_encode(3 * 2.0 ** -10) == 0x02            # tie between codes 1 and 2 -> even
+    assert O.e4m3_encode(1.0625) == 0x38 and O.e4m3_encode(1.1875) == 0x3A   # ties to even mantissa
+
+
+def test_mx_scale_closed_forms():
+    # catches: emax other than 8, floor/ceil mix-up, missing clamps, zero block
+    assert O.mx_scale(0.0) == 0
+    assert O.mx_scale(1.0) == 119                           # 2^(0-8)
+    assert O.mx_scale(448.0) == 127 and O.mx_scale(256.0) == 127 and O.mx_scale(255.99) == 126
+    assert O.mx_scale(0.75) == 118 and O.mx_scale(2.0 ** -140) == 0 and O.mx_scale(2.0 ** 200) == 254
+
+
+def test_mx_quantize_blocks_against_definition_properties():
+    # catches: scale from the wrong block, scale per row instead of per 32, no saturation in a block
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((37, 256)) * np.exp2(rng.integers(-12, 12, (37, 1)))).astype(np.float32)
+    x[3, 32:64] = 0.0                                       # an all-zero block
+    x[5, 0] = 1e-30                                         # tiny value inside a normal block
+    codes, scales = O.mx_quantize(x)
+    assert codes.shape == (37, 256) and scales.shape == (37, 8)
+    assert scales[3, 1] == 0 and np.all(codes[3, 32:64] == 0)
+    deq = O.mx_dequantize(codes, scales)
+    xb = x.astype(np.float64).reshape(37, 8, 32)
+    amax = np.abs(xb).max(axis=2)
+    nz = amax > 0
+    # the block maximum lands in [256, 512) after scaling, i.e. 2^(s-127) = 2^(floor(log2 amax) - 8)
+    e = np.floor(np.log2(np.where(nz, amax, 1.0)))
+    assert np.array_equal(scales[nz].astype(np.int64), (e[nz] - 8 + 127).astype(np.int64))
+    # every element is the nearest representable value of its block (codes at most 448)
+    step = np.exp2(np.repeat(scales.astype(np.float64) - 127, 32, axis=1)).reshape(37, 8, 32)
+    err = np.abs(deq.reshape(37, 8, 32) - xb)
+    gridstep = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(xb) / step, 2.0 ** -6))) - 3), 2.0 ** -9) * step
+    sat = np.abs(xb) / step > 448
+    assert np.all(err[~sat] <= gridstep[~sat] / 2 + 1e-300)
+    assert np.all(np.abs(deq.reshape(37, 8, 32)[sat]) == 448 * step[sat])
+    # re-quantising quantised values changes nothing
+    c2, s2 = O.mx_quantize(deq.astype(np.float32))
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+
+
+def mx_weights(rng, shape, std):
+    """MX-quantised random weights through the oracle's own (pinned) quantiser."""
+    w = (rng.standard_normal(shape) * std).astype(np.float32)
+    q, s = O.mx_quantize(w.reshape(-1, shape[-1]))
+    return q.reshape(shape), s.reshape(shape[:-1] + (shape[-1] // 32,))
+
+
+def test_layer_mx_matches_dense_numpy_formulation():
+    # catches: unquantised x or h, h quantised along the wrong axis, weight scales from the
+    # wrong block, gate and up swapped, missing gate weights in the combine
+    rng = np.random.default_rng(13)
+    T, H, E, k, I = 9, 64, 4, 2, 96
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    ids = np.array([rng.choice(E, k, replace=False) for _ in range(T)], dtype=np.int32)
+    gw = rng.random((T, k)).astype(np.float32)
+    wgu_q, wgu_s = mx_weights(rng, (E, 2 * I, H), 0.1)
+    wd_q, wd_s = mx_weights(rng, (E, H, I), 0.1)
+    y = O.layer_tokens_mx(np.arange(T), x, ids, gw, 0, E, wgu_q, wgu_s, wd_q, wd_s)
+    xq, xs = O.mx_quantize(x)
+    xd = O.mx_dequantize(xq, xs)
+    wgu = O.mx_dequantize(wgu_q, wgu_s)
+    wd = O.mx_dequantize(wd_q, wd_s)
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            gu = wgu[e] @ xd[t]
+            h = (silu(gu[:I]) * gu[I:]).astype(np.float32)[None, :]
+            hq, hs = O.mx_quantize(h)
+            ref[t] += gw[t, j] * (wd[e] @ O.mx_dequantize(hq, hs)[0])
+    assert np.max(np.abs(y - ref)) <= 1e-6 * np.max(np.abs(ref))
+
+
+def test_layer_mx_local_share_drops_foreign_experts():
+    # catches: EP filter missing in the MX layer
+    rng = np.random.default_rng(14)
+    T, H, E, k, I = 6, 32, 4, 2, 32
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    ids = np.array([[0, 1], [2, 3], [1, 2], [3, 0], [0, 2], [1, 3]], dtype=np.int32)
+    gw = rng.random((T, k)).astype(np.float32)
+    wgu_q, wgu_s = mx_weights(rng, (E, 2 * I, H), 0.2)
+    wd_q, wd_s = mx_weights(rng, (E, H, I), 0.2)
+    full = O.layer_tokens_mx(np.arange(T), x, ids, gw, 0, E, wgu_q, wgu_s, wd_q, wd_s)
+    lo = O.layer_tokens_mx(np.arange(T), x, ids, gw, 0, 2, wgu_q[:2], wgu_s[:2], wd_q[:2], wd_s[:2])
+    hi = O.layer_tokens_mx(np.arange(T), x, ids, gw, 2, 4, wgu_q[2:], wgu_s[2:], wd_q[2:], wd_s[2:])
+    assert np.allclose(lo.astype(np.float64) + hi, full, rtol=0, atol=1e-5 * np.abs(full).max())
+    assert np.all(lo[1] == 0) and np.all(hi[0] == 0)
+
+
+def test_h_mx_rows_match_dense_numpy_formulation():
+    # catches: h quantised before rounding to fp32, wrong expert or token of a row
+    rng = np.random.default_rng(15)
+    T, H, E, I = 7, 64, 3, 64
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wgu_q, wgu_s = mx_weights(rng, (E, 2 * I, H), 0.1)
+    rt = np.array([0, 3, 6, 2, 2], dtype=np.int32)
+    re_ = np.array([1, 0, 2, 2, 0], dtype=np.int32)
+    hq, hs = O.h_mx(rt, re_, x, wgu_q, wgu_s)
+    xq, xs = O.mx_quantize(x)
+    xd = O.mx_dequantize(xq, xs)
+    wgu = O.mx_dequantize(wgu_q, wgu_s)
+    for r in range(len(rt)):
+        gu = wgu[re_[r]] @ xd[rt[r]]
+        h = (silu(gu[:I]) * gu[I:]).astype(np.float32)[None, :]
+        q, s = O.mx_quantize(h)
+        assert np.array_equal(hq[r], q[0]) and np.array_equal(hs[r], s[0])
