@@ -16,9 +16,16 @@
 // chunks of its row per 64 k and passes the row's scale dword shifted by 8h,
 // with the byte selector picking block 2*kk of the K step.
 //
-// LDS: two slots, each holding one K step of A (256 x 128 B) and its scales
-// (up to 256 x 4 B) and of B likewise (116 KB); the loads of step kt+1 are issued
-// while step kt computes.  Chunk c of LDS row r sits in slot c ^ ((r >> 1) & 7).
+// LDS: the activation operand of a K step (192 x 128 B) sits in a two-slot ring
+// and is fetched one step ahead; the weight operand (256 x 128 B) together with
+// the scale dwords of both operands sits in a three-slot ring and is fetched two
+// steps ahead (2 x 24 KB + 3 x 34 KB = 150 KB, one workgroup per CU).  Every
+// wave issues the same loads every step (past the last K step they refetch it
+// into slots nobody reads again), so the loop has no branches and the wait at
+// the top of a step is a fixed count: everything but this wave's five newest
+// loads has landed.  One barrier per step.  Chunk c of LDS row r sits in slot
+// c ^ ((r >> 1) & 7); wave w's 256-byte scale segment holds the A scales of
+// tile rows 32w .. 32w+31, then the B scales of weight rows 32w .. 32w+31.
 //
 // Gate/up epilogue: h = silu(G) * U in fp32, quantised per row in blocks of 32
 // intermediate columns (a wave's 32 columns are one block) into MXFP8 codes and
@@ -32,12 +39,13 @@ namespace {
 using ffn::TileParams;
 
 constexpr int BM = 192, BN = 256, BK = 128, NTHR = 512;
-// scale areas hold 32 rows per wave (8 x 32 = 256 >= BM, BN): wave w fills rows 32w .. 32w+31
-constexpr int A_BYTES = BM * BK, AS_BYTES = NTHR / 64 * 32 * 4, B_BYTES = BN * BK, BS_BYTES = NTHR / 64 * 32 * 4;
-static_assert(AS_BYTES >= BM * 4 && BS_BYTES >= BN * 4, "scale areas cover every tile row");
-constexpr int OFF_AS = A_BYTES, OFF_B = A_BYTES + AS_BYTES, OFF_BS = OFF_B + B_BYTES;
-constexpr int SLOT_BYTES = OFF_BS + BS_BYTES;  // 58 KB
-constexpr int LDS_BYTES = 2 * SLOT_BYTES;       // 116 KB
+constexpr int A_BYTES = BM * BK;                 // 24 KB: one activation slot
+constexpr int S_BYTES = NTHR / 64 * 256;         // 2 KB: scale dwords of 8 x 32 A rows and 8 x 32 B rows
+constexpr int BSLOT = BN * BK + S_BYTES;         // 34 KB: one weight + scales slot
+constexpr int OFF_B = 2 * A_BYTES;
+constexpr int LDS_BYTES = OFF_B + 3 * BSLOT;     // 150 KB
+static_assert(NTHR / 64 * 32 >= BM && NTHR / 64 * 32 >= BN, "scale segments cover every tile row");
+static_assert(LDS_BYTES <= 160 * 1024, "fits the LDS of one CU");
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -54,45 +62,44 @@ struct MxParams {
 
 struct Src {
   uint32_t aoff[3], boff[4];   // byte offsets of this lane's A / B segment chunks at K step 0
-  uint32_t asoff, bsoff;       // byte offsets of this lane's A / B scale dwords at K step 0 (lanes < 32)
+  const uint8_t *sptr;         // this lane's scale dword at K step 0: A row (lanes < 32) or B row
 };
 
 template <int NMB>
-__device__ __forceinline__ void kloop(const char *abase, const char *bbase, const uint8_t *asb, const uint8_t *bsb,
-                                      const Src &src, int nA, int K, int wave, int lane, int arow0, int wn, char *lds,
-                                      f32x16_t (&acc)[NMB > 0 ? NMB : 1][2]) {
+__device__ __forceinline__ void kloop(const char *abase, const char *bbase, const Src &src, int K, int wave, int lane,
+                                      int arow0, int wn, char *lds, f32x16_t (&acc)[NMB > 0 ? NMB : 1][2]) {
   const int KT = K / BK;
   const int h = lane >> 5;
+  // A of step kt: A slot kt % 2; B and the scales of step kt: B slot kt % 3.  Source steps past
+  // the end are clamped to the last one.
   auto loadA = [&](int kt, int u) __attribute__((always_inline)) {
-    char *st = lds + (kt & 1) * SLOT_BYTES;
-    if (u < nA)
-      __builtin_amdgcn_global_load_lds((const void *)(abase + (size_t)kt * BK + src.aoff[u]),
-                                       (lds_void *)(st + (wave + 8 * u) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void *)(abase + (size_t)min(kt, KT - 1) * BK + src.aoff[u]),
+                                     (lds_void *)(lds + (kt & 1) * A_BYTES + (wave + 8 * u) * 1024), 16, 0, 0);
   };
   auto loadB = [&](int kt, int u) __attribute__((always_inline)) {
-    char *st = lds + (kt & 1) * SLOT_BYTES;
-    __builtin_amdgcn_global_load_lds((const void *)(bbase + (size_t)kt * BK + src.boff[u]),
-                                     (lds_void *)(st + OFF_B + (wave + 8 * u) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void *)(bbase + (size_t)min(kt, KT - 1) * BK + src.boff[u]),
+                                     (lds_void *)(lds + OFF_B + (kt % 3) * BSLOT + (wave + 8 * u) * 1024), 16, 0, 0);
   };
   auto loadS = [&](int kt) __attribute__((always_inline)) {  // four scale bytes per row and K step
-    char *st = lds + (kt & 1) * SLOT_BYTES;
-    if (lane < 32) {
-      __builtin_amdgcn_global_load_lds((const void *)(asb + (size_t)kt * 4 + src.asoff),
-                                       (lds_void *)(st + OFF_AS + wave * 128), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(bsb + (size_t)kt * 4 + src.bsoff),
-                                       (lds_void *)(st + OFF_BS + wave * 128), 4, 0, 0);
-    }
+    __builtin_amdgcn_global_load_lds((const void *)(src.sptr + (size_t)min(kt, KT - 1) * 4),
+                                     (lds_void *)(lds + OFF_B + (kt % 3) * BSLOT + BN * BK + wave * 256), 4, 0, 0);
   };
-  auto step = [&](int kt, bool next) __attribute__((always_inline)) {
-    const char *st = lds + (kt & 1) * SLOT_BYTES;
-    const char *A = st, *B = st + OFF_B;
+  auto step = [&](int kt) __attribute__((always_inline)) {
+    const char *A = lds + (kt & 1) * A_BYTES;
+    const char *B = lds + OFF_B + (kt % 3) * BSLOT;
+    const char *S = B + BN * BK;
     uint32_t sa[NMB > 0 ? NMB : 1], sb[2];
     if constexpr (NMB > 0) {
 #pragma unroll
-      for (int j = 0; j < 2; j++)
-        sb[j] = *(const uint32_t *)(st + OFF_BS + (wn * 64 + j * 32 + (lane & 31)) * 4) >> (8 * h);
+      for (int j = 0; j < 2; j++) {
+        const int row = wn * 64 + j * 32 + (lane & 31);
+        sb[j] = *(const uint32_t *)(S + (row >> 5) * 256 + 128 + (row & 31) * 4) >> (8 * h);
+      }
 #pragma unroll
-      for (int i = 0; i < NMB; i++) sa[i] = *(const uint32_t *)(st + OFF_AS + (arow0 + i * 32 + (lane & 31)) * 4) >> (8 * h);
+      for (int i = 0; i < NMB; i++) {
+        const int row = arow0 + i * 32 + (lane & 31);
+        sa[i] = *(const uint32_t *)(S + (row >> 5) * 256 + (row & 31) * 4) >> (8 * h);
+      }
     }
     // one 64-k half of the K step; KK is a compile-time constant (the scale byte selector must be)
     auto half_step = [&](auto KKC) __attribute__((always_inline)) {
@@ -111,15 +118,13 @@ __device__ __forceinline__ void kloop(const char *abase, const char *bbase, cons
 #pragma unroll
         for (int i = 0; i < NMB; i++) af[i] = frag(A, arow0 + i * 32 + (lane & 31));
       }
-      if (next) {
-        if constexpr (kk == 0) {
+      if constexpr (kk == 0) {
 #pragma unroll
-          for (int u = 0; u < 3; u++) loadA(kt + 1, u);
-          loadS(kt + 1);
-        } else {
+        for (int u = 0; u < 3; u++) loadA(kt + 1, u);
+      } else {
 #pragma unroll
-          for (int u = 0; u < 4; u++) loadB(kt + 1, u);
-        }
+        for (int u = 0; u < 4; u++) loadB(kt + 2, u);
+        loadS(kt + 2);
       }
       if constexpr (NMB > 0) {
 #pragma unroll
@@ -134,21 +139,26 @@ __device__ __forceinline__ void kloop(const char *abase, const char *bbase, cons
     half_step(std::integral_constant<int, 1>{});
   };
 #pragma unroll
-  for (int u = 0; u < 3; u++) loadA(0, u);
+  for (int u = 0; u < 4; u++) loadB(0, u);
   loadS(0);
 #pragma unroll
-  for (int u = 0; u < 4; u++) loadB(0, u);
+  for (int u = 0; u < 3; u++) loadA(0, u);
+#pragma unroll
+  for (int u = 0; u < 4; u++) loadB(1, u);
+  loadS(1);
   for (int kt = 0; kt < KT; kt++) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // this wave's newest five loads are the weights and scales of step kt + 1; all older ones,
+    // among them everything of step kt, have landed once at most five are in flight
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     barrier_no_fence();
-    step(kt, kt + 1 < KT);
+    step(kt);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int MODE, bool ATOMIC, int NMB>
-__device__ __forceinline__ void body(const MxParams &mp, const char *abase, const char *bbase, const uint8_t *asb,
-                                     const uint8_t *bsb, const Src &src, int nA, int K, int nt, int rbase, int mvalid,
-                                     int wave, int lane, int arow0, int wn, char *lds) {
+__device__ __forceinline__ void body(const MxParams &mp, const char *abase, const char *bbase, const Src &src, int K,
+                                     int nt, int rbase, int mvalid, int wave, int lane, int arow0, int wn, char *lds) {
   const TileParams &p = mp.tp;
   constexpr int NA = NMB > 0 ? NMB : 1;
   f32x16_t acc[NA][2];
@@ -158,7 +168,7 @@ __device__ __forceinline__ void body(const MxParams &mp, const char *abase, cons
     for (int j = 0; j < 2; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
-  kloop<NMB>(abase, bbase, asb, bsb, src, nA, K, wave, lane, arow0, wn, lds, acc);
+  kloop<NMB>(abase, bbase, src, K, wave, lane, arow0, wn, lds, acc);
   if constexpr (NMB > 0) {
     // acc[i][j][r] at lane l is tile row arow0 + i*32 + 8*(r/4) + 4*(l/32) + r%4,
     // weight row wn*64 + j*32 + l%32 of the tile
@@ -218,7 +228,6 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
   const int rows = min(trows, min(beg + cnt, p.R_cap) - r0);
   if (rows <= 0) return;
   const int half = trows >> 1;
-  const int nA = trows >> 6;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -248,12 +257,11 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
   }
   {
     const int row = wave * 32 + (lane & 31);
-    src.asoff = a_row(row) * (uint32_t)kb;
-    src.bsoff = (uint32_t)w_row(row) * (uint32_t)kb;
+    src.sptr = lane < 32 ? asb + (size_t)a_row(row) * kb : bsb + (size_t)w_row(row) * kb;
   }
   const int arow0 = wm * half;
   const int rbase = r0 + arow0;
-#define MX_BODY(n) body<MODE, ATOMIC, n>(mp, abase, bbase, asb, bsb, src, nA, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
+#define MX_BODY(n) body<MODE, ATOMIC, n>(mp, abase, bbase, src, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
   switch (nmb) {
     case 0: MX_BODY(0); break;
     case 1: MX_BODY(1); break;

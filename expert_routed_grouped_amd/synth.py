@@ -154,18 +154,18 @@ def quantize_e4m3_per_row(w: np.ndarray):
     return codes, scale
 
 
-def quantize_mx_blocks(w: np.ndarray):
-    """Offline MXFP8 conversion of float32 weights along the last axis (blocks of 32):
-    scale byte s = clip(floor(log2 amax) - 8 + 127, 0, 254) (0 for an all-zero block),
-    code = RNE-saturate(w / 2^(s-127)).  Returns (codes uint8, scales uint8 [..., K/32])."""
-    w = np.asarray(w, dtype=np.float32)
-    K = w.shape[-1]
-    blocks = w.astype(np.float64).reshape(w.shape[:-1] + (K // 32, 32))
-    amax = np.max(np.abs(blocks), axis=-1)
-    _, ex = np.frexp(amax)
-    s = np.where(amax > 0, np.clip(ex - 1 - 8 + 127, 0, 254), 0).astype(np.int64)
-    codes = _encode_e4m3(blocks * np.ldexp(1.0, 127 - s)[..., None])
-    return codes.reshape(w.shape), s.astype(np.uint8)
+def mx_weights(rng: np.random.Generator, shape: tuple, std: float):
+    """A synthetic MXFP8 weight tensor (blocks of 32 along the last axis) with a spread close to
+    ``std``: the power of two nearest std/32, times a per-block jitter of 1/2, 1 or 2, is each
+    block's E8M0 scale, and its e4m3 codes are the nearest codes of N(0, 32^2) draws divided
+    by that jitter.  Returns (codes uint8 shape, scales uint8 shape[:-1] + (K/32,))."""
+    K = shape[-1]
+    base = 127 + int(np.round(np.log2(std / 32.0)))
+    jitter = rng.integers(-1, 2, size=shape[:-1] + (K // 32,))
+    v = rng.standard_normal(shape, dtype=np.float32).astype(np.float64) * 32.0
+    v = v.reshape(shape[:-1] + (K // 32, 32)) * np.ldexp(1.0, -jitter)[..., None]
+    codes = _encode_e4m3(v).reshape(shape)
+    return codes, (base + jitter).astype(np.uint8)
 
 
 def zipf_logit_bias(E: int, s: float = 1.2, scale: float = 2.0) -> np.ndarray:
@@ -215,15 +215,15 @@ def gen_expert(cfg: LayerConfig, e: int):
     Rows 0..I-1 of w_gate_up are the gate projection, rows I..2I-1 the up projection.
     Scales are None unless the weight type is fp8."""
     _, _, sgu, sd = _stds(cfg)
+    if cfg.wdt == "mxfp8":  # weights arrive already converted: draw codes and block scales directly
+        qgu, s_gu = mx_weights(_rng(cfg, 3, e), (2 * cfg.I, cfg.H), sgu)
+        qd, s_d = mx_weights(_rng(cfg, 4, e), (cfg.H, cfg.I), sd)
+        return qgu, qd, s_gu, s_d
     gu = _rng(cfg, 3, e).standard_normal((2 * cfg.I, cfg.H), dtype=np.float32) * np.float32(sgu)
     dn = _rng(cfg, 4, e).standard_normal((cfg.H, cfg.I), dtype=np.float32) * np.float32(sd)
     if cfg.wdt == "fp8":
         qgu, s_gu = quantize_e4m3_per_row(gu)
         qd, s_d = quantize_e4m3_per_row(dn)
-        return qgu, qd, s_gu, s_d
-    if cfg.wdt == "mxfp8":
-        qgu, s_gu = quantize_mx_blocks(gu)
-        qd, s_d = quantize_mx_blocks(dn)
         return qgu, qd, s_gu, s_d
     return _store(gu, cfg.wdt), _store(dn, cfg.wdt), None, None
 
