@@ -37,6 +37,9 @@ WORKLOADS = {
     "skew": "skewed prefill MoE layer: T=6000, top-8 of 128, logit bias 2*ln Zipf(1.2), H=4096, I=1536, bf16",
     "ep_share": "EP=4 share: T=8192 routed over 128 experts, local experts 0-31, fp8 e4m3 weights, H=4096, I=1536",
     "prefill_mx": "W8A8 MXFP8 prefill MoE layer: T=6000 tokens x top-8 of E=128 experts, H=4096, SwiGLU I=1536",
+    "decode_shared": "decode MoE layer (T=64, top-8 of 128, H=4096, I=1536, bf16) plus one shared expert (I_s=1536)",
+    "prefill_shared": "prefill MoE layer (T=6000, top-8 of 128, H=4096, I=1536, bf16) plus one shared expert "
+                      "(I_s=1536)",
 }
 
 
@@ -116,6 +119,9 @@ def cpu_baseline(inp, cfg, seconds):
         else:
             O.layer_tokens(np.arange(x.shape[0]), x, ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"],
                            inp["s_gate_up"], inp["s_down"], round_h=cfg.act != "f32")
+        if cfg.I_s > 0:
+            O.shared_tokens(np.arange(x.shape[0]), x, inp["ws_gate_up"], inp["ws_down"], inp["ss_gate_up"],
+                            inp["ss_down"], round_h=cfg.act != "f32")
         td = time.perf_counter()
         stage["route"] += tb - ta
         stage["permute"] += tc - tb
@@ -126,7 +132,8 @@ def cpu_baseline(inp, cfg, seconds):
             break
     return {"value": done / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
             "sample": f"{done} tokens in {chunk}-token chunks of the same {cfg.T}-token batch (wrapping around), "
-                      f"whole layer per chunk (route, permute, token-major SwiGLU FFN + combine), {dt:.1f} s",
+                      f"whole layer per chunk (route, permute, token-major SwiGLU FFN + combine"
+                      f"{' + shared expert' if cfg.I_s > 0 else ''}), {dt:.1f} s",
             "stage_tokens_per_s": {k: round(done / v, 1) if v > 0 else None for k, v in stage.items()}}
 
 
@@ -185,8 +192,14 @@ def main():
         ffn_half("down", outs, common)
         if not bufs.fused:
             moe.moe_combine(bufs.y_perm, p["token_row"], bufs.topk_w, y=bufs.y, stream=stream)
+        if bufs.shared_ws is not None:
+            shared()
         if ev is not None:
             ev[3].record(stream)
+
+    def shared():
+        moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], bufs.y, dev.get("ss_gate_up"),
+                              dev.get("ss_down"), workspace=bufs.shared_ws, stream=stream)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -205,6 +218,16 @@ def main():
     route_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     gu_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     down_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    shared_ms = None
+    if bufs.shared_ws is not None:  # the shared expert alone, on the same stream
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a, b in sev:
+            a.record(stream)
+            shared()
+            b.record(stream)
+        torch.cuda.synchronize()
+        shared_ms = float(np.mean([a.elapsed_time(b) for a, b in sev]))
 
     flushed = None
     if args.flush_steps > 0:
@@ -238,6 +261,9 @@ def main():
     layer_flops = A.useful_flops(R, H, I) + A.router_flops(T, H, cfg.E)
     layer_bytes = A.layer_hbm_bytes(counts, T, H, I, cfg.E, abytes,
                                     A.expert_bytes(H, I, wbytes, cfg.wdt == "fp8"), cfg.E * H * abytes)
+    if cfg.I_s > 0:  # the shared expert: every token once, its weights once
+        layer_flops += A.useful_flops(T, H, cfg.I_s)
+        layer_bytes += A.expert_bytes(H, cfg.I_s, wbytes, cfg.wdt == "fp8")
     gu_s = float(np.mean(gu_ms)) * 1e-3
     if args.config == "decode":
         achieved = gu_bytes / gu_s / 1e9
@@ -281,6 +307,7 @@ def main():
                   "ms_p90": round(float(np.percentile(layer_ms, 90)), 4),
                   "route_permute_ms": round(float(np.mean(route_ms)), 4), "gate_up_ms": round(float(np.mean(gu_ms)), 4),
                   "down_combine_ms": round(float(np.mean(down_ms)), 4),
+                  "shared_expert_ms": None if shared_ms is None else round(shared_ms, 4),
                   "hbm_bytes": int(layer_bytes), "hbm_frac": round(layer_bytes / layer_s / 1e9 / PEAK_HBM_GBS, 4),
                   "flops": int(layer_flops),
                   "mfma_frac": round(layer_flops / layer_s / 1e12 / (PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS), 4)},

@@ -138,6 +138,80 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
   return hip_status(launch_ffn(fa, s));
 }
 
+// Up to this many tokens the shared expert streams its weights (every token in one or two 64-row
+// tiles) with K split over enough workgroups to keep HBM busy; above it the tile kernels run.
+constexpr int SHARED_STREAM_ROWS = 128;
+
+size_t moe_shared_workspace_size(int T, int I_s, int a_dtype) {
+  if (T < 0 || I_s < 1) return 0;
+  const size_t esz = a_dtype == MOE_F32 ? 4 : 2;
+  // h [T, I_s], the identity row maps (offsets {0, T}, row_token [T], row_w [T]), then for a
+  // decode-sized batch the fp32 G/U partial sums of the split-K gate/up projection [T, 2 I_s]
+  size_t b = align_up((size_t)T * (size_t)I_s * esz, 256) + 256 + 2 * align_up((size_t)T * 4, 256);
+  if (T <= SHARED_STREAM_ROWS) b += align_up((size_t)T * 2 * (size_t)I_s * 4, 256);
+  return b;
+}
+
+int moe_shared_expert(const void *x, int x_dtype, int T, int H, int I_s, const void *w_gate_up, const void *w_down,
+                      int w_dtype, const float *s_gate_up, const float *s_down, float *y, void *workspace,
+                      size_t workspace_bytes, unsigned flags, void *stream) {
+  if (T < 0 || H < 64 || I_s < 64 || H % 64 != 0 || I_s % 64 != 0) return MOE_ERR_SHAPE;
+  if ((long long)T * (H > I_s ? H : I_s) >= (1LL << 30) || (long long)H * I_s >= (1LL << 30)) return MOE_ERR_SHAPE;
+  const bool bf16_path = x_dtype == MOE_BF16 && (w_dtype == MOE_BF16 || w_dtype == MOE_FP8_E4M3);
+  const bool f32_path = x_dtype == MOE_F32 && w_dtype == MOE_F32;
+  if (!bf16_path && !f32_path) return MOE_ERR_DTYPE;
+  if ((flags & ~MOE_FFN_ZERO_Y) != 0) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate_up || !w_down || !y) return MOE_ERR_NULL;
+  if (w_dtype == MOE_FP8_E4M3 && (!s_gate_up || !s_down)) return MOE_ERR_NULL;
+  if (!workspace) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < moe_shared_workspace_size(T, I_s, x_dtype)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y) ||
+      ((uintptr_t)workspace & 255u) != 0)
+    return MOE_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t esz = x_dtype == MOE_F32 ? 4 : 2;
+  char *ws = (char *)workspace;
+  char *maps = ws + align_up((size_t)T * (size_t)I_s * esz, 256);
+  int32_t *offsets = (int32_t *)maps;
+  int32_t *row_token = (int32_t *)(maps + 256);
+  float *row_w = (float *)(maps + 256 + align_up((size_t)T * 4, 256));
+  hipError_t err = launch_identity_rows(T, offsets, row_token, row_w, s);
+  if (err == hipSuccess && (flags & MOE_FFN_ZERO_Y)) err = launch_zero_f32(y, (size_t)T * H, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  FfnArgs fa{};
+  fa.a = x;
+  fa.a_bf16 = x_dtype == MOE_BF16;
+  fa.gather = 0;
+  fa.offsets = offsets;
+  fa.row_token = row_token;
+  fa.row_w = row_w;
+  fa.El = 1;
+  fa.T = T;
+  fa.R_cap = T;
+  fa.H = H;
+  fa.I = I_s;
+  fa.w_gu = w_gate_up;
+  fa.w_d = w_down;
+  fa.w_dt = w_dtype == MOE_F32 ? 0 : (w_dtype == MOE_BF16 ? 1 : 2);
+  fa.s_gu = s_gate_up;
+  fa.s_d = s_down;
+  fa.y = y;  // every row once with weight 1: the "atomic" add is the single add y + o
+  fa.h = workspace;
+  fa.phase = 3;
+  fa.kernel = T <= SHARED_STREAM_ROWS ? 1 : 2;
+  if (T <= SHARED_STREAM_ROWS && x_dtype == MOE_BF16) {
+    // one expert gives only I_s / 128 gate/up workgroups per 64-row tile: split K over up to half
+    // the 64-wide chunks so that about a thousand workgroups stream the weights
+    const int tiles = (T + 63) / 64 * ((I_s + 127) / 128);
+    int ks = (1024 + tiles - 1) / tiles;
+    if (ks > H / 128) ks = H / 128;
+    fa.ksplit = ks > 1 ? ks : 1;
+    fa.gu32 = (float *)(maps + 256 + 2 * align_up((size_t)T * 4, 256));
+  }
+  return hip_status(launch_ffn(fa, s));
+}
+
 int moe_combine(const float *y_perm, const int32_t *token_row, const float *topk_w, int T, int k, int H, float *y,
                 void *stream) {
   if (T < 0 || k < 1 || k > 32 || H < 4 || H % 4 != 0) return MOE_ERR_SHAPE;

@@ -65,6 +65,10 @@ hipError_t launch_combine(const float *y_perm, const int32_t *token_row, const f
 
 hipError_t launch_zero_f32(float *p, size_t n, hipStream_t s);
 
+// Row maps of one group holding every token once, in order: offsets = {0, T},
+// row_token[i] = i, row_w[i] = 1 (the shared expert as a one-expert grouped FFN).
+hipError_t launch_identity_rows(int T, int32_t *offsets, int32_t *row_token, float *row_w, hipStream_t s);
+
 // Grouped FFN.  ``h`` is the intermediate [R_cap, I] (bf16 or fp32 by path).
 struct FfnArgs {
   const void *a;          // x [T,H] (gather) or x_perm [R_cap,H]
@@ -82,6 +86,9 @@ struct FfnArgs {
   float *y_perm;          // per-row outputs when y == NULL
   void *h;                // intermediate
   int phase;              // bit 0: gate/up half, bit 1: down half
+  int kernel;             // bf16 / fp8 weights: 0 pick by rows per expert, 1 weight streaming, 2 tiles
+  int ksplit;             // weight streaming only: split K over this many workgroups per tile (needs y and
+  float *gu32;            // gu32, an fp32 [R_cap, 2I] scratch for the G and U partial sums)
 };
 
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t s);

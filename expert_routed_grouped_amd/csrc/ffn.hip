@@ -332,7 +332,7 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
     return hipSuccess;
   }
   // Few rows per expert on average: stream the weights (HBM bound); else tiles (matrix-core bound).
-  const bool stream = (long long)a.R_cap <= 48LL * a.El;
+  const bool stream = a.kernel == 1 || (a.kernel == 0 && (long long)a.R_cap <= 48LL * a.El);
   if (stream || a.w_dt == 1) {
     TileParams base{};
     base.offsets = a.offsets;

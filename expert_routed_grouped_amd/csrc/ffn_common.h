@@ -14,6 +14,8 @@ struct TileParams {
   void *out;              // h [R_cap,I] bf16 (gate-up) / y [T,H] or y_perm [R_cap,H] fp32 (down)
   int El, H, I;
   int R_cap;              // rows past R_cap are never touched, whatever the offsets say
+  int ksplit;             // weight-streaming kernel: K slices per tile (0 or 1: none)
+  float *gu32;            // with ksplit > 1: fp32 G and U partial sums [R_cap, 2I], zeroed beforehand
 };
 
 __device__ __forceinline__ int wave_sum_i(int v) {

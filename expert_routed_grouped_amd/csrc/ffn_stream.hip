@@ -61,8 +61,10 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
   const int Nw = MODE == 0 ? 2 * p.I : p.H;
   constexpr int WCOLS = MODE == 0 ? 32 : 64;  // output columns per wave
   const int NT = (Ncols + SWAVES * WCOLS - 1) / (SWAVES * WCOLS);
-  int e, nt, r0, rows;
-  if (!ffn::find_tile<SBM>(p, NT, e, nt, r0, rows)) return;
+  const int KS = p.ksplit > 1 ? p.ksplit : 1;  // K slices: tile "column" index = nt * KS + slice
+  int e, ntk, r0, rows;
+  if (!ffn::find_tile<SBM>(p, NT * KS, e, ntk, r0, rows)) return;
+  const int nt = ntk / KS, ks = ntk - nt * KS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = (nt * SWAVES + wave) * WCOLS;
   if (c0 >= Ncols) return;  // Ncols is a multiple of 64: a wave's columns are all valid or all past the end
@@ -132,8 +134,14 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
     }
   };
 
-  const int KC = K / 64;  // K is a multiple of 64
-  load(0, 0);
+  // this workgroup's 64-wide k chunks: [kb, kb + KC) of the K / 64 (K is a multiple of 64)
+  const int kb = ks * (K / 64) / KS;
+  const int KC = (ks + 1) * (K / 64) / KS - kb;
+#pragma unroll
+  for (int b = 0; b < NB; b++) wrow[b] += (size_t)kb * 64 * wesz;
+#pragma unroll
+  for (int mb = 0; mb < SMB; mb++) arow[mb] += (size_t)kb * 64;
+  if (KC > 0) load(0, 0);
   int kc = 0;
   for (; kc + 2 <= KC; kc += 2) {
     load(1, (kc + 1) * 64);
@@ -160,7 +168,12 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
         const int m = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
         if (m < rows) {
           const float gt = acc[mb][0][r] * sg, u = acc[mb][1][r] * su;
-          hout[(size_t)(r0 + m) * p.I + col] = f32_to_bf16(silu_fast(gt) * u);
+          if (KS > 1) {  // partial sums of one K slice; SwiGLU runs once they are complete
+            atomicAdd(p.gu32 + (size_t)(r0 + m) * 2 * p.I + col, gt);
+            atomicAdd(p.gu32 + (size_t)(r0 + m) * 2 * p.I + p.I + col, u);
+          } else {
+            hout[(size_t)(r0 + m) * p.I + col] = f32_to_bf16(silu_fast(gt) * u);
+          }
         }
       }
     }
@@ -188,6 +201,23 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
   }
 }
 
+// h = bf16(silu(G) * U) from the completed K-slice sums (rows < R_cap, 8 columns per thread).
+__global__ __launch_bounds__(256) void swiglu_rows_kernel(const float *__restrict__ gu32, int rows, int I,
+                                                          uint16_t *__restrict__ h) {
+  const int per_row = I / 8;
+  const size_t n = (size_t)rows * per_row;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / per_row;
+    const int c = (int)(i - r * per_row) * 8;
+    const float *g = gu32 + r * 2 * I + c;
+    uint16_t o[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) o[j] = f32_to_bf16(silu_fast(g[j]) * g[I + j]);
+    *(u32x4_t *)(h + r * I + c) = u32x4_t{o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16),
+                                         o[4] | ((uint32_t)o[5] << 16), o[6] | ((uint32_t)o[7] << 16)};
+  }
+}
+
 template <int MODE, bool FP8, bool GATHER, bool ATOMIC>
 hipError_t launch_s(const TileParams &tp, int grid, hipStream_t s) {
   hipLaunchKernelGGL((ffn_stream_kernel<MODE, FP8, GATHER, ATOMIC>), dim3(grid), dim3(64 * SWAVES), 0, s, tp);
@@ -206,15 +236,27 @@ hipError_t launch_ffn_stream(const TileParams &base, const FfnArgs &a, hipStream
   const long long max_mt = mt1 < mt2 ? mt1 : mt2;
   const bool fp8 = a.w_dt == 2;
   TileParams tp = base;
+  // split K only with the fused combine (partial down-projection sums add straight into y)
+  const int ks = (a.ksplit > 1 && a.y != nullptr && a.gu32 != nullptr) ? a.ksplit : 1;
+  tp.ksplit = ks;
+  tp.gu32 = a.gu32;
   if (a.phase & 1) {
     tp.a = a.a;
     tp.w = a.w_gu;
     tp.scale = a.s_gu;
     tp.out = a.h;
-    const int grid = (int)(max_mt * ceil_div_i(a.I, SCOLS));
+    if (ks > 1 && (err = launch_zero_f32(a.gu32, (size_t)a.R_cap * 2 * a.I, s)) != hipSuccess) return err;
+    const int grid = (int)(max_mt * ceil_div_i(a.I, SCOLS) * ks);
     if (fp8) err = a.gather ? launch_s<0, true, true, false>(tp, grid, s) : launch_s<0, true, false, false>(tp, grid, s);
     else err = a.gather ? launch_s<0, false, true, false>(tp, grid, s) : launch_s<0, false, false, false>(tp, grid, s);
     if (err != hipSuccess) return err;
+    if (ks > 1) {
+      const size_t n = (size_t)a.R_cap * (a.I / 8);
+      const int g = (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+      hipLaunchKernelGGL(swiglu_rows_kernel, dim3(g > 0 ? g : 1), dim3(256), 0, s, a.gu32, a.R_cap, a.I,
+                         (uint16_t *)a.h);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
   }
   if (a.phase & 2) {
     tp.a = a.h;
@@ -222,7 +264,8 @@ hipError_t launch_ffn_stream(const TileParams &base, const FfnArgs &a, hipStream
     tp.scale = a.s_d;
     const bool atomic = a.y != nullptr;
     tp.out = atomic ? (void *)a.y : (void *)a.y_perm;
-    const int grid = (int)(max_mt * ceil_div_i(a.H, 2 * SCOLS));  // down: 64 columns per wave
+    tp.ksplit = ks > 1 ? (ks < a.I / 64 ? ks : a.I / 64) : 1;  // at most one 64-wide chunk per slice
+    const int grid = (int)(max_mt * ceil_div_i(a.H, 2 * SCOLS) * tp.ksplit);  // down: 64 columns per wave
     if (fp8) err = atomic ? launch_s<1, true, false, true>(tp, grid, s) : launch_s<1, true, false, false>(tp, grid, s);
     else err = atomic ? launch_s<1, false, false, true>(tp, grid, s) : launch_s<1, false, false, false>(tp, grid, s);
   }

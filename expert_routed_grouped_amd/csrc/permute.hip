@@ -244,6 +244,19 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restric
   }
 }
 
+__global__ __launch_bounds__(256) void identity_rows_kernel(int T, int32_t *__restrict__ offsets,
+                                                           int32_t *__restrict__ row_token, float *__restrict__ row_w) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < T) {
+    row_token[i] = i;
+    row_w[i] = 1.0f;
+  }
+  if (i == 0) {
+    offsets[0] = 0;
+    offsets[1] = T;
+  }
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(int T, int k, int El) {
@@ -285,5 +298,11 @@ hipError_t launch_gather_rows(const void *x, int esz, int H, const int32_t *offs
   int grid = R_cap < 4096 ? R_cap : 4096;
   hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), 0, s, (const uint4 *)x, row_vecs, offsets, El,
                      row_token, R_cap, (uint4 *)x_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_identity_rows(int T, int32_t *offsets, int32_t *row_token, float *row_w, hipStream_t s) {
+  const int grid = T > 0 ? (T + 255) / 256 : 1;
+  hipLaunchKernelGGL(identity_rows_kernel, dim3(grid), dim3(256), 0, s, T, offsets, row_token, row_w);
   return hipGetLastError();
 }

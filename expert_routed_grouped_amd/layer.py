@@ -39,6 +39,11 @@ def to_device(inputs: dict, device="cuda") -> dict:
         out["w_down"] = t(inputs["w_down"], cfg.wdt)
         out["s_gate_up"] = t(inputs.get("s_gate_up"), "f32")
         out["s_down"] = t(inputs.get("s_down"), "f32")
+    if "ws_gate_up" in inputs:  # shared expert
+        out["ws_gate_up"] = t(inputs["ws_gate_up"], cfg.wdt)
+        out["ws_down"] = t(inputs["ws_down"], cfg.wdt)
+        out["ss_gate_up"] = t(inputs.get("ss_gate_up"), "f32")
+        out["ss_down"] = t(inputs.get("ss_down"), "f32")
     return out
 
 
@@ -64,10 +69,12 @@ class LayerBuffers:
         self.workspace = torch.empty(moe.moe_ffn_workspace_size(self.R_cap, El, H, I, adt), dtype=torch.uint8, **d)
         self.y = torch.empty((T, H), dtype=torch.float32, **d)
         self.y_perm = None if self.fused else torch.empty((max(self.R_cap, 1), H), dtype=torch.float32, **d)
+        self.shared_ws = (torch.empty(moe.moe_shared_workspace_size(T, cfg.I_s, adt), dtype=torch.uint8, **d)
+                          if cfg.I_s > 0 else None)
 
 
 def run_layer(dev: dict, bufs: LayerBuffers, stream=None) -> torch.Tensor:
-    """route -> permute -> grouped FFN (-> combine).  Returns y [T,H] fp32."""
+    """route -> permute -> grouped FFN (-> combine) (-> shared expert).  Returns y [T,H] fp32."""
     cfg = bufs.cfg
     moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=stream)
     p = moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=bufs.perm, stream=stream)
@@ -80,4 +87,7 @@ def run_layer(dev: dict, bufs: LayerBuffers, stream=None) -> torch.Tensor:
                             dev["w_gate_up"], dev["w_down"], dev.get("s_gate_up"), dev.get("s_down"),
                             y_perm=bufs.y_perm, workspace=bufs.workspace, gather=True, stream=stream)
         moe.moe_combine(bufs.y_perm, p["token_row"], bufs.topk_w, y=bufs.y, stream=stream)
+    if bufs.shared_ws is not None:
+        moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], bufs.y, dev.get("ss_gate_up"),
+                              dev.get("ss_down"), workspace=bufs.shared_ws, stream=stream)
     return bufs.y

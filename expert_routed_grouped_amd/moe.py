@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTY
 # Every symbol moe.h declares (checked by the CPU test suite).
 EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_permute_workspace_size",
            "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_quantize_mx", "moe_ffn_mx_workspace_size",
-           "moe_grouped_ffn_mx")
+           "moe_grouped_ffn_mx", "moe_shared_workspace_size", "moe_shared_expert")
 
 
 class MoEError(RuntimeError):
@@ -66,6 +66,10 @@ def lib():
         L.moe_ffn_mx_workspace_size.argtypes = [I, I]
         L.moe_grouped_ffn_mx.restype = I
         L.moe_grouped_ffn_mx.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, Z, ctypes.c_uint, P]
+        L.moe_shared_workspace_size.restype = Z
+        L.moe_shared_workspace_size.argtypes = [I, I, I]
+        L.moe_shared_expert.restype = I
+        L.moe_shared_expert.argtypes = [P, I, I, I, I, P, P, I, P, P, P, P, Z, ctypes.c_uint, P]
         _lib = L
     return _lib
 
@@ -229,4 +233,25 @@ def moe_combine(y_perm: torch.Tensor, token_row: torch.Tensor, topk_w: torch.Ten
         y = torch.empty((T, H), dtype=torch.float32, device=y_perm.device)
     _check("moe_combine", lib().moe_combine(_ptr(y_perm), _ptr(token_row), _ptr(topk_w), T, k, H, _ptr(y),
                                             _stream(stream)))
+    return y
+
+
+def moe_shared_workspace_size(T: int, I_s: int, x_dtype: int) -> int:
+    return int(lib().moe_shared_workspace_size(T, I_s, x_dtype))
+
+
+def moe_shared_expert(x: torch.Tensor, w_gate_up: torch.Tensor, w_down: torch.Tensor, y: torch.Tensor,
+                      s_gate_up: Optional[torch.Tensor] = None, s_down: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, zero_y: bool = False, stream=None):
+    """y += shared-expert SwiGLU FFN of x (every token, weight 1); ``zero_y`` zeroes y first."""
+    T, H = x.shape
+    I_s = w_gate_up.shape[0] // 2
+    xdt = _dtype(x)
+    need = moe_shared_workspace_size(T, I_s, xdt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check("moe_shared_expert", lib().moe_shared_expert(
+        _ptr(x), xdt, T, H, I_s, _ptr(w_gate_up), _ptr(w_down), _dtype(w_gate_up), _ptr(s_gate_up), _ptr(s_down),
+        _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(), MOE_FFN_ZERO_Y if zero_y else 0,
+        _stream(stream)))
     return y

@@ -64,6 +64,7 @@ class LayerConfig:
     x_std: float = 1.0
     w_std: float = 0.02
     seed: int = 0
+    I_s: int = 0               # intermediate size of the shared expert (0: none)
 
     @property
     def lo(self) -> int:
@@ -95,6 +96,9 @@ CONFIGS = {
     "ep_share": LayerConfig("ep_share", T=8192, H=4096, E=128, k=8, I=1536, wdt="fp8", e_begin=0, e_end=32, seed=5),
     # W8A8 MXFP8 variant of the prefill layer (weights converted offline, activations on the fly)
     "prefill_mx": LayerConfig("prefill_mx", T=6000, H=4096, E=128, k=8, I=1536, wdt="mxfp8", seed=6),
+    # the decode and prefill layers with one always-active shared expert of a routed expert's shape
+    "decode_shared": LayerConfig("decode_shared", T=64, H=4096, E=128, k=8, I=1536, seed=7, I_s=1536),
+    "prefill_shared": LayerConfig("prefill_shared", T=6000, H=4096, E=128, k=8, I=1536, seed=8, I_s=1536),
 }
 
 
@@ -228,6 +232,16 @@ def gen_expert(cfg: LayerConfig, e: int):
     return _store(gu, cfg.wdt), _store(dn, cfg.wdt), None, None
 
 
+SHARED_INDEX = 1 << 20  # draw index of the shared expert's weights (routed experts use 0..E-1)
+
+
+def gen_shared(cfg: LayerConfig):
+    """Weights of the shared expert, drawn like a routed expert's with intermediate size I_s:
+    (w_gate_up [2 I_s, H], w_down [H, I_s], s_gate_up, s_down)."""
+    assert cfg.I_s > 0 and cfg.wdt != "mxfp8"
+    return gen_expert(cfg.replace(I=cfg.I_s), SHARED_INDEX)
+
+
 def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
@@ -270,4 +284,7 @@ def make_inputs(cfg: LayerConfig, experts: Optional[list] = None, with_weights: 
         for e in ids:
             one(e)
     out.update(w_gate_up=w_gu, w_down=w_d, s_gate_up=s_gu, s_down=s_d, experts=ids)
+    if cfg.I_s > 0:
+        a, b, sa, sb = gen_shared(cfg)
+        out.update(ws_gate_up=a, ws_down=b, ss_gate_up=sa, ss_down=sb)
     return out

@@ -10,6 +10,9 @@
  *                    down-projection epilogue (or per-row outputs for moe_combine)
  *   moe_combine      gate-weighted gather-sum of per-row outputs to token order
  *
+ * plus moe_shared_expert (an always-active expert added to y) and the W8A8
+ * MXFP8 variant of the expert FFN (moe_quantize_mx, moe_grouped_ffn_mx).
+ *
  * The method follows three pages: "AI-infra book, ch. 9 Distributed inference"
  * (section 9.3.4, Fig. 9-16: route, group rows by expert, expert GEMMs, weighted
  * combine; section 9.3.2: the expert is three 4096 x 1536 matrices), "Hosting
@@ -258,6 +261,39 @@ int moe_grouped_ffn_mx(const uint8_t *a_codes, const uint8_t *a_scales, const in
  */
 int moe_combine(const float *y_perm, const int32_t *token_row, const float *topk_w, int T, int k, int H,
                 float *y, void *stream);
+
+/* Bytes of workspace moe_shared_expert needs (h [T, I_s] of x_dtype, then its row maps). */
+size_t moe_shared_workspace_size(int T, int I_s, int x_dtype);
+
+/*
+ * moe_shared_expert - an always-active (shared) expert added to the layer output.
+ *
+ * Defined by: "PagedAttention, speculative decoding, MoE and Blackwell", MoE
+ * list, the bullet on shared experts: besides the routed experts a model may
+ * keep a few experts that process every token.  Reading taken: each shared
+ * expert is a SwiGLU FFN of the routed experts' form and its output is added
+ * to the token's output with weight 1 (no gate); several shared experts are
+ * one FFN whose intermediate is their intermediates side by side (the sum of
+ * SwiGLU FFNs equals that FFN exactly).
+ *
+ *   y[t,:] += W_d h_t,  h_t = silu(W_g x_t) * (W_u x_t)   for every t < T
+ * with x [T,H] (bf16 or fp32), w_gate_up [2*I_s, H] (rows 0..I_s-1 gate,
+ * I_s..2*I_s-1 up), w_down [H, I_s], element types and fp8 scales
+ * (s_gate_up [2*I_s], s_down [H]) as in moe_grouped_ffn, and h rounded to bf16
+ * for bf16 activations.  y [T,H] fp32 accumulates: call it after
+ * moe_grouped_ffn's fused combine or moe_combine on the same stream, or pass
+ * MOE_FFN_ZERO_Y (the only flag) for the shared expert alone.  For T > 128
+ * each element of y receives one fp32 add; for T <= 128 (bf16 activations)
+ * the contraction is split over many workgroups to keep HBM busy, so G, U and
+ * y receive several fp32 adds of partial sums in no fixed order (run-to-run
+ * rounding differences).  H and I_s multiples of 64; pointers 16-byte
+ * aligned, workspace at least moe_shared_workspace_size(T, I_s, x_dtype)
+ * bytes, 256-byte aligned.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE,
+ * MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_shared_expert(const void *x, int x_dtype, int T, int H, int I_s, const void *w_gate_up, const void *w_down,
+                      int w_dtype, const float *s_gate_up, const float *s_down, float *y, void *workspace,
+                      size_t workspace_bytes, unsigned flags, void *stream);
 
 #ifdef __cplusplus
 }

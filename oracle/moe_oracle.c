@@ -47,6 +47,11 @@
  *      ties to the even code, magnitudes above 448 saturate to 448, the sign
  *      bit is kept.  In the W8A8 layer x is quantised per token row, h from
  *      its fp32 value per row, and the weights arrive already quantised.
+ *   R10 a shared expert ("PagedAttention, speculative decoding, MoE and
+ *      Blackwell", MoE list, shared-experts bullet) is an FFN of the R5 form
+ *      that every token passes through; its output is added to the token's
+ *      output with weight 1, and several shared experts are one FFN whose
+ *      intermediate is theirs side by side.
  *
  * Everything else accumulates in fp64 over the exact stored input values.
  */
@@ -454,6 +459,51 @@ void oracle_h_mx(const int32_t *row_token, const int32_t *row_expert, int R, con
         free(xq);
         free(xv);
         free(hv);
+    }
+}
+
+/* R10 (with R5's h rounding), token-major: the shared expert's contribution
+ * W_d (silu(W_g x_t) * (W_u x_t)) for the listed tokens (y_out [n_tok, H], fp64
+ * stored fp32).  w_gate_up [2*I_s, H] (rows 0..I_s-1 gate), w_down [H, I_s];
+ * s_gate_up [2*I_s], s_down [H] per-output-channel scales for e4m3 weights. */
+void oracle_shared_tokens(const int32_t *tokens, int n_tok, const void *x, int x_dt, int H, int I_s,
+                          const void *w_gate_up, const void *w_down, int w_dt, const float *s_gate_up,
+                          const float *s_down, int round_h, float *y_out)
+{
+#pragma omp parallel
+    {
+        double *xt = (double *)malloc(sizeof(double) * (size_t)H);
+        double *hb = (double *)malloc(sizeof(double) * (size_t)I_s);
+#pragma omp for schedule(dynamic, 1)
+        for (int q = 0; q < n_tok; q++) {
+            int t = tokens[q];
+            for (int n = 0; n < H; n++)
+                xt[n] = elem(x, x_dt, (size_t)t * H + n);
+            for (int i = 0; i < I_s; i++) {
+                double G = 0.0, U = 0.0;
+                size_t rg = (size_t)i * H, ru = (size_t)(I_s + i) * H;
+                for (int h = 0; h < H; h++) {
+                    G += xt[h] * elem(w_gate_up, w_dt, rg + h);
+                    U += xt[h] * elem(w_gate_up, w_dt, ru + h);
+                }
+                if (w_dt == ODT_E4M3) {
+                    G *= (double)s_gate_up[i];
+                    U *= (double)s_gate_up[I_s + i];
+                }
+                float hf = (float)(G / (1.0 + exp(-G)) * U);
+                hb[i] = round_h ? (double)bf16_bits_to_float(oracle_bf16_round(hf)) : (double)hf;
+            }
+            for (int n = 0; n < H; n++) {
+                double o = 0.0;
+                for (int i = 0; i < I_s; i++)
+                    o += hb[i] * elem(w_down, w_dt, (size_t)n * I_s + i);
+                if (w_dt == ODT_E4M3)
+                    o *= (double)s_down[n];
+                y_out[(size_t)q * H + n] = (float)o;
+            }
+        }
+        free(xt);
+        free(hb);
     }
 }
 

@@ -71,6 +71,7 @@ def lib():
         L.oracle_mx_quantize.argtypes = [P, i, i, i, P, P]
         L.oracle_layer_tokens_mx.argtypes = [P, i, P, i, P, P, i, i, i, i, i, P, P, P, P, P]
         L.oracle_h_mx.argtypes = [P, P, i, P, i, i, i, P, P, P, P]
+        L.oracle_shared_tokens.argtypes = [P, i, P, i, i, i, P, P, i, P, P, i, P]
         _lib = L
     return _lib
 
@@ -162,6 +163,25 @@ def layer_tokens(tokens, x, topk_ids, topk_w, e_begin: int, e_end: int, w_gate_u
     y = np.empty((len(tok), H), dtype=np.float32)
     lib().oracle_layer_tokens(_p(tok), len(tok), _p(x), _dt_of(x), _p(ids), _p(w), T, H, k, e_begin, e_end, I,
                               _p(wgu), _p(wd), _dt_of(wgu), _p(sgu), _p(sd), 1 if round_h else 0, _p(y))
+    return y
+
+
+def shared_tokens(tokens, x, w_gate_up, w_down, s_gate_up=None, s_down=None, round_h: bool = True) -> np.ndarray:
+    """R10: the shared expert's contribution (fp32 [len(tokens), H]) for the listed tokens."""
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    x = np.ascontiguousarray(x)
+    wgu = np.ascontiguousarray(w_gate_up)
+    wd = np.ascontiguousarray(w_down)
+    T, H = x.shape
+    I_s = wd.shape[1]
+    assert wgu.shape == (2 * I_s, H) and wd.shape == (H, I_s) and wgu.dtype == wd.dtype
+    sgu = None if s_gate_up is None else np.ascontiguousarray(s_gate_up, dtype=np.float32)
+    sd = None if s_down is None else np.ascontiguousarray(s_down, dtype=np.float32)
+    if _dt_of(wgu) == 2:
+        assert sgu is not None and sd is not None
+    y = np.empty((len(tok), H), dtype=np.float32)
+    lib().oracle_shared_tokens(_p(tok), len(tok), _p(x), _dt_of(x), H, I_s, _p(wgu), _p(wd), _dt_of(wgu), _p(sgu),
+                               _p(sd), 1 if round_h else 0, _p(y))
     return y
 
 

@@ -122,6 +122,21 @@ def test_quantize_mx_validation(kw, code):
     assert moe.lib().moe_quantize_mx(a["x"], a["xd"], a["rows"], a["K"], a["q"], a["s"], None) == code
 
 
+def shared(x=FAKE, xd=1, T=8, H=64, I_s=64, wgu=FAKE, wd=FAKE, wdt=1, sgu=None, sd=None, y=FAKE, ws=FAKE,
+           wsb=1 << 20, flags=0):
+    return moe.lib().moe_shared_expert(x, xd, T, H, I_s, wgu, wd, wdt, sgu, sd, y, ws, wsb, flags, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=96), -2), (dict(I_s=32), -2), (dict(T=-1), -2), (dict(T=1 << 20, H=2048), -2), (dict(flags=1), -2),
+    (dict(xd=0), -3), (dict(wdt=3), -3), (dict(x=None), -1), (dict(y=None), -1), (dict(wd=None), -1),
+    (dict(wdt=2), -1), (dict(ws=None), -4), (dict(wsb=64), -4), (dict(y=FAKE_ODD), -6), (dict(T=0), 0),
+])
+def test_shared_expert_validation(kw, code):
+    # every case is rejected (or is empty) on the host before anything is launched
+    assert shared(**kw) == code
+
+
 def test_workspace_size():
     L = moe.lib()
     # per-chunk (1024 assignments) expert counts
@@ -134,6 +149,9 @@ def test_workspace_size():
     # h as MXFP8: codes [R_cap, I] and scales [R_cap, I/32], each 256-byte aligned
     ws = L.moe_ffn_mx_workspace_size(48000, 1536)
     assert ws >= 48000 * 1536 + 48000 * 48 and ws % 256 == 0
+    # shared expert: h [T, I_s] plus its row maps (offsets, row_token, row_w)
+    ws = L.moe_shared_workspace_size(6000, 1536, 1)
+    assert ws >= 6000 * 1536 * 2 + 8 + 2 * 6000 * 4 and ws % 256 == 0
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -349,7 +349,7 @@ def sample_tokens(cfg, ids, n=24):
     return np.array(sorted(pick), dtype=np.int32)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "ep_share"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "ep_share", "decode_shared", "prefill_shared"])
 def test_full_workload_layer(name):
     cfg = CONFIGS[name]
     inp = host_inputs(cfg)
@@ -368,6 +368,9 @@ def test_full_workload_layer(name):
     say(f"full layer {name}: oracle on {len(toks)} sampled tokens")
     y_o = O.layer_tokens(toks, inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"], inp["s_gate_up"],
                          inp["s_down"])
+    if cfg.I_s > 0:
+        y_o = y_o.astype(np.float64) + O.shared_tokens(toks, inp["x"], inp["ws_gate_up"], inp["ws_down"],
+                                                       inp["ss_gate_up"], inp["ss_down"])
     yg = y.cpu().numpy()
     check_y(yg[toks], y_o, name)
     # a second call reuses the buffers and gives the same routing and (up to atomic order) the same y
@@ -375,6 +378,59 @@ def test_full_workload_layer(name):
     check_y(y2[toks], y_o, name + " (repeat)")
     del dev, bufs
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# shared expert: standalone against the oracle, and added to the routed layer
+# ----------------------------------------------------------------------------
+SHARED_CASES = [
+    # T <= 128: weight-streaming kernel; larger T: tile kernels (bf16 DMA, fp8 register-staged); fp32 model
+    LayerConfig("sh_decode", T=64, H=256, E=4, k=2, I=64, seed=401, w_std=0.05, I_s=384),
+    LayerConfig("sh_tail", T=129, H=384, E=4, k=2, I=64, seed=402, w_std=0.05, I_s=320),
+    LayerConfig("sh_prefill", T=700, H=384, E=4, k=2, I=64, seed=403, w_std=0.05, I_s=448),
+    LayerConfig("sh_fp8", T=300, H=256, E=4, k=2, I=64, wdt="fp8", seed=404, w_std=0.05, I_s=256),
+    LayerConfig("sh_fp8_small", T=40, H=256, E=4, k=2, I=64, wdt="fp8", seed=405, w_std=0.05, I_s=192),
+    LayerConfig("sh_f32", T=50, H=128, E=4, k=2, I=64, act="f32", wdt="f32", init="fan_in", seed=406, I_s=128),
+]
+
+
+@pytest.mark.parametrize("cfg", SHARED_CASES, ids=lambda c: c.name)
+def test_shared_expert_matches_oracle(cfg):
+    inp = host_inputs(cfg)
+    dev = L.to_device(inp)
+    say(f"shared expert {cfg.name}: T={cfg.T} H={cfg.H} I_s={cfg.I_s} {cfg.wdt}")
+    y = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], y, dev["ss_gate_up"], dev["ss_down"],
+                          zero_y=True)
+    torch.cuda.synchronize()
+    y_o = O.shared_tokens(np.arange(cfg.T), inp["x"], inp["ws_gate_up"], inp["ws_down"], inp["ss_gate_up"],
+                          inp["ss_down"], round_h=cfg.act != "f32")
+    check_y(y.cpu().numpy(), y_o, cfg.name)
+    # accumulating onto an existing y adds the same contribution: bit for bit when every element
+    # gets one add (T > 128), within fp32 rounding of the split-K partial sums otherwise
+    base = torch.randn((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+    y2 = base.clone()
+    moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], y2, dev["ss_gate_up"], dev["ss_down"])
+    torch.cuda.synchronize()
+    if cfg.T > 128 or cfg.act == "f32":
+        assert torch.equal(y2, base + y)
+    else:
+        check_y((y2 - base).cpu().numpy(), y_o, cfg.name + " (accumulated)")
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "combine"])
+@pytest.mark.parametrize("cfg", [SHARED_CASES[0], SHARED_CASES[2], SHARED_CASES[3]], ids=lambda c: c.name)
+def test_layer_with_shared_expert_matches_oracle(cfg, fused):
+    inp = host_inputs(cfg)
+    dev = L.to_device(inp)
+    bufs = L.LayerBuffers(cfg, fused=fused)
+    say(f"layer + shared expert {cfg.name} fused={fused}")
+    y = L.run_layer(dev, bufs).cpu().numpy()
+    r = O.layer(inp)
+    assert np.array_equal(bufs.topk_ids.cpu().numpy(), r["topk_ids"])
+    y_o = r["y"].astype(np.float64) + O.shared_tokens(np.arange(cfg.T), inp["x"], inp["ws_gate_up"],
+                                                      inp["ws_down"], inp["ss_gate_up"], inp["ss_down"])
+    check_y(y, y_o, cfg.name + " + shared")
 
 
 # ----------------------------------------------------------------------------

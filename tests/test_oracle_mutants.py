@@ -50,6 +50,12 @@ MUTANTS = {
                            "hq[32 * b + i] = hv[32 * b + i];"),
     "mx_weight_scale_wrong_block": ("return ldexp(oracle_e4m3_value(codes[row * (size_t)K + i]), (int)scales[row * (size_t)(K / 32) + i / 32] - 127);",
                                     "return ldexp(oracle_e4m3_value(codes[row * (size_t)K + i]), (int)scales[row * (size_t)(K / 32) + (i / 32 + 1) % (K / 32)] - 127);"),
+    "shared_up_rows_misplaced": ("size_t rg = (size_t)i * H, ru = (size_t)(I_s + i) * H;",
+                                 "size_t rg = (size_t)i * H, ru = (size_t)(I_s / 2 + i) * H;"),
+    "shared_silu_dropped": ("float hf = (float)(G / (1.0 + exp(-G)) * U);", "float hf = (float)(G * U);"),
+    "shared_fp8_down_scale_dropped": ("o *= (double)s_down[n];", "o *= 1.0;"),
+    "shared_down_row_stride": ("o += hb[i] * elem(w_down, w_dt, (size_t)n * I_s + i);",
+                               "o += hb[i] * elem(w_down, w_dt, (size_t)i * H + n);"),
     "combine_gate_added_not_multiplied": ("acc += (double)topk_w[(size_t)t * k + j] * (double)y_perm[(size_t)r * H + n];",
                                           "acc += (double)topk_w[(size_t)t * k + j] + (double)y_perm[(size_t)r * H + n];"),
 }

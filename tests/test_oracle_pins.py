@@ -563,3 +563,63 @@ def test_h_mx_rows_match_dense_numpy_formulation():
         h = (silu(gu[:I]) * gu[I:]).astype(np.float32)[None, :]
         q, s = O.mx_quantize(h)
         assert np.array_equal(hq[r], q[0]) and np.array_equal(hs[r], s[0])
+
+
+# ----------------------------------------------------------------------------
+# shared expert (R10)
+# ----------------------------------------------------------------------------
+SHARED = [
+    LayerConfig("sh_f32", T=20, H=64, E=4, k=2, I=32, act="f32", wdt="f32", init="fan_in", seed=41, I_s=96),
+    LayerConfig("sh_bf16", T=18, H=64, E=4, k=2, I=32, act="bf16", wdt="bf16", seed=42, w_std=0.1, I_s=64),
+    LayerConfig("sh_fp8", T=16, H=128, E=4, k=2, I=32, act="bf16", wdt="fp8", seed=43, w_std=0.1, I_s=96),
+]
+
+
+@pytest.mark.parametrize("cfg", SHARED, ids=lambda c: c.name)
+def test_shared_expert_matches_dense_numpy_formulation(cfg):
+    # numpy matmuls over all tokens at once: x W_gu^T, SwiGLU, (bf16 h), h W_d^T
+    inp = synth.make_inputs(cfg)
+    x = decode_w(inp["x"], cfg.act) if cfg.act == "bf16" else inp["x"].astype(np.float64)
+    wgu = decode_w(inp["ws_gate_up"], cfg.wdt)
+    wd = decode_w(inp["ws_down"], cfg.wdt)
+    if cfg.wdt == "fp8":
+        wgu = wgu * inp["ss_gate_up"][:, None].astype(np.float64)
+        wd = wd * inp["ss_down"][:, None].astype(np.float64)
+    gu = x @ wgu.T
+    h = (silu(gu[:, :cfg.I_s]) * gu[:, cfg.I_s:]).astype(np.float32)
+    if cfg.act != "f32":
+        h = bf16_bits_to_f32(torch_bf16_bits(h))
+    ref = h.astype(np.float64) @ wd.T
+    y = O.shared_tokens(np.arange(cfg.T), inp["x"], inp["ws_gate_up"], inp["ws_down"], inp["ss_gate_up"],
+                        inp["ss_down"], round_h=cfg.act != "f32")
+    rms = np.sqrt((ref ** 2).mean())
+    assert rms > 0
+    assert np.max(np.abs(y - ref)) <= 1e-5 * np.max(np.abs(ref)) + 1e-3 * rms
+
+
+def test_shared_expert_is_the_sum_of_its_halves():
+    # two shared experts of intermediate m side by side are one of intermediate 2m: the
+    # output of the whole equals the sum of the outputs of the halves (fp32 h, no rounding)
+    cfg = SHARED[0]
+    inp = synth.make_inputs(cfg)
+    m = cfg.I_s // 2
+    gu, dn = inp["ws_gate_up"], inp["ws_down"]
+    I_s = cfg.I_s
+    halves = []
+    for a, b in ((0, m), (m, I_s)):
+        gu_h = np.concatenate([gu[a:b], gu[I_s + a:I_s + b]])
+        halves.append(O.shared_tokens(np.arange(cfg.T), inp["x"], gu_h, np.ascontiguousarray(dn[:, a:b]),
+                                      round_h=False).astype(np.float64))
+    whole = O.shared_tokens(np.arange(cfg.T), inp["x"], gu, dn, round_h=False).astype(np.float64)
+    assert np.allclose(whole, halves[0] + halves[1], rtol=1e-5, atol=1e-6 * np.abs(whole).max())
+
+
+def test_shared_expert_equals_a_one_expert_top1_layer_bit_exact():
+    # a shared expert is a routed expert with gate 1 that every token selects
+    cfg = SHARED[1]
+    inp = synth.make_inputs(cfg)
+    ids = np.zeros((cfg.T, 1), dtype=np.int32)
+    w = np.ones((cfg.T, 1), dtype=np.float32)
+    routed = O.layer_tokens(np.arange(cfg.T), inp["x"], ids, w, 0, 1, inp["ws_gate_up"][None], inp["ws_down"][None])
+    shared = O.shared_tokens(np.arange(cfg.T), inp["x"], inp["ws_gate_up"], inp["ws_down"])
+    assert np.array_equal(routed, shared)
