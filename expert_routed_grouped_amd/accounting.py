@@ -11,7 +11,10 @@ tests can pin them to the book's worked numbers:
 * rows a grouped GEMM executes when every expert is padded to a tile
   (section 9.4.3, local counts [32,16,8,4,2,1,1,0]);
 * expert skew s = max_j m_j / (n*k/R) (section 9.4.2 equations);
-* rows on the card that holds a hot expert (section 9.4.1).
+* rows on the card that holds a hot expert (section 9.4.1);
+* replica-aware load: rows per card when hot experts have replicas that
+  share their assignments, and when a replica's copy cost is paid back
+  (section 9.4.2, Example 9.6: N_min = floor(T_copy / dt) + 1).
 """
 from __future__ import annotations
 
@@ -89,6 +92,44 @@ def hot_expert_card_rows(n: int, k: int, E: int, hot_rows: float, groups: int) -
     rest = (n * k - hot_rows) / (E - 1)
     per_card = E // groups
     return hot_rows + (per_card - 1) * rest
+
+
+def replica_card_rows(counts: Sequence[int], placement: Sequence[Sequence[int]]) -> np.ndarray:
+    """Rows each card multiplies when the assignments of an expert are split evenly over its
+    replicas.  ``placement[c]`` lists the experts card c holds (an expert on several cards has
+    that many replicas); an expert's m rows go m // r to each of its r replicas, the remainder
+    one row each to its first replicas in card order.  Every expert with rows must be placed."""
+    counts = [int(c) for c in counts]
+    holders = {}
+    for c, experts in enumerate(placement):
+        for e in experts:
+            holders.setdefault(int(e), []).append(c)
+    rows = np.zeros(len(placement), dtype=np.int64)
+    for e, m in enumerate(counts):
+        if m == 0:
+            continue
+        cards = holders.get(e)
+        if not cards:
+            raise ValueError(f"expert {e} has {m} rows but no card holds it")
+        q, rem = divmod(m, len(cards))
+        for i, c in enumerate(cards):
+            rows[c] += q + (1 if i < rem else 0)
+    return rows
+
+
+def replica_break_even(t_copy: float, dt: float) -> int:
+    """Smallest number of batches N with N * dt > t_copy: floor(t_copy / dt) + 1."""
+    return int(math.floor(t_copy / dt)) + 1
+
+
+def replica_net_saving(batches: int, t_copy: float, dt: float) -> float:
+    """Time saved by a replica over ``batches`` batches after paying its copy once."""
+    return batches * dt - t_copy
+
+
+def replica_memory_bytes(expert_bytes_: int, layers: int, replicas_per_layer: int = 1) -> int:
+    """HBM one card gives up for ``replicas_per_layer`` extra experts in each of ``layers`` layers."""
+    return expert_bytes_ * layers * replicas_per_layer
 
 
 def layer_hbm_bytes(counts: Iterable[int], T: int, H: int, I: int, E: int, act_bytes: int,

@@ -623,3 +623,50 @@ def test_shared_expert_equals_a_one_expert_top1_layer_bit_exact():
     routed = O.layer_tokens(np.arange(cfg.T), inp["x"], ids, w, 0, 1, inp["ws_gate_up"][None], inp["ws_down"][None])
     shared = O.shared_tokens(np.arange(cfg.T), inp["x"], inp["ws_gate_up"], inp["ws_down"])
     assert np.array_equal(routed, shared)
+
+
+def test_replica_accounting_matches_example_9_6():
+    from expert_routed_grouped_amd import accounting as A
+    g = GOLD["replica_break_even"]
+    # 128 tokens pick the same 8 hot experts, all on card 0: 1024 assignments
+    counts = [g["tokens"]] * g["hot_experts"]
+    alone = A.replica_card_rows(counts, [list(range(8))] + [[] for _ in range(g["cards"] - 1)])
+    assert alone.tolist() == [1024] + [0] * 7
+    # one replica of seven of them on cards 1..7 (7 x 36 MiB = 252 MiB copied)
+    assert g["replicated"] * g["expert_mib"] == g["copy_mib"]
+    placed = A.replica_card_rows(counts, [list(range(8))] + [[e] for e in range(1, 8)])
+    assert placed.tolist() == [128 + 7 * 64] + [64] * 7
+    # card 0 streams its rows' traffic: the time falls with its row count
+    after = g["card0_ms_before"] * placed[0] / alone[0]
+    assert round(after, 3) == g["card0_ms_after"]
+    dt = g["card0_ms_before"] - after
+    assert round(dt, 2) == round(g["saving_ms_per_batch"], 2)
+    assert A.replica_break_even(g["copy_ms_intra"], dt) == g["n_min_intra"]
+    assert A.replica_break_even(g["copy_ms_inter"], dt) == g["n_min_inter"]
+    for n, v in g["net_ms_intra"].items():
+        assert round(A.replica_net_saving(int(n), g["copy_ms_intra"], dt), 1) == v
+    for n, v in g["net_ms_inter"].items():
+        assert round(A.replica_net_saving(int(n), g["copy_ms_inter"], dt), 1) == v
+    m = GOLD["replica_memory"]
+    mib = 1 << 20
+    assert A.replica_memory_bytes(m["expert_mib"] * mib, m["layers"]) == m["all_layers_mib"] * mib
+    assert round(A.gib(A.replica_memory_bytes(m["expert_mib"] * mib, m["layers"])), 2) == m["all_layers_gib"]
+    assert A.replica_memory_bytes(m["expert_mib"] * mib, m["hot_layers"]) == m["hot_layers_mib"] * mib
+
+
+def test_replica_rows_conserve_assignments_and_split_evenly():
+    from expert_routed_grouped_amd import accounting as A
+    rng = np.random.default_rng(5)
+    counts = rng.integers(0, 50, size=16).tolist()
+    placement = [[e for e in range(16) if e % 4 == c] for c in range(4)]
+    placement[1].append(0)  # expert 0 gets a replica on card 1
+    placement[2].append(0)  # and one on card 2
+    rows = A.replica_card_rows(counts, placement)
+    assert rows.sum() == sum(counts)
+    base = A.replica_card_rows(counts, [[e for e in range(16) if e % 4 == c] for c in range(4)])
+    q, r = divmod(counts[0], 3)
+    assert rows[0] == base[0] - counts[0] + q + (1 if r > 0 else 0)
+    assert rows[1] == base[1] + q + (1 if r > 1 else 0)
+    assert rows[2] == base[2] + q
+    with pytest.raises(ValueError):
+        A.replica_card_rows([1, 2], [[0]])
