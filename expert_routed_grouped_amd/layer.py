@@ -15,7 +15,7 @@ from . import moe
 
 # Above this many (row x hidden) outputs the fused epilogue's fp32 atomics cost more
 # than writing per-row outputs and reducing them with moe_combine (measured on MI355X:
-# ~0.34 G atomic adds/s against ~6-7 TB/s of streaming stores).
+# ~0.33 T atomic adds/s against ~6-7 TB/s of streaming stores).
 FUSED_COMBINE_MAX_ELEMS = 16 * 1024 * 1024
 
 
