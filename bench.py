@@ -178,14 +178,19 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=stream)
-        moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=p, stream=stream)
+        if bufs.rd_ws is not None:  # decode: route + dispatch (+ zeroing of y) in one launch
+            moe.moe_route_dispatch(dev["x"], dev["w_router"], dev["bias"], cfg.k, cfg.E, cfg.lo, cfg.hi, bufs.rd_ws,
+                                   bufs.topk_ids, bufs.topk_w, p, y_zero=bufs.y if bufs.fused else None,
+                                   stream=stream)
+        else:
+            moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=stream)
+            moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=p, stream=stream)
         if mx:
             moe.moe_quantize_mx(dev["x"], xq, xs, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         common = dict(workspace=bufs.workspace, gather=True, stream=stream)
-        outs = dict(y=bufs.y, zero_y=True) if bufs.fused else dict(y_perm=bufs.y_perm, zero_y=False)
+        outs = (dict(y=bufs.y, zero_y=bufs.rd_ws is None) if bufs.fused else dict(y_perm=bufs.y_perm, zero_y=False))
         ffn_half("gate_up", outs, common)
         if ev is not None:
             ev[2].record(stream)
@@ -301,7 +306,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "T": T, "H": H, "E": cfg.E, "k": cfg.k, "I": I,
                    "local_experts": [cfg.lo, cfg.hi], "parallelism": "none (one GPU)",
-                   "combine": "fused atomic epilogue" if bufs.fused else "per-row outputs + moe_combine"},
+                   "combine": "fused atomic epilogue" if bufs.fused else "per-row outputs + moe_combine",
+                   "dispatch": "route + dispatch in one launch" if bufs.rd_ws is not None else "moe_route + moe_permute"},
         "roofline": roof,
         "layer": {"ms_p50": round(float(np.median(layer_ms)), 4), "ms_p10": round(float(np.percentile(layer_ms, 10)), 4),
                   "ms_p90": round(float(np.percentile(layer_ms, 90)), 4),

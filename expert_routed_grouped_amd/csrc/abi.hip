@@ -41,6 +41,27 @@ int moe_route(const void *x, int x_dtype, const void *w_router, int w_dtype, con
                                  topk_w, (hipStream_t)stream));
 }
 
+size_t moe_route_dispatch_workspace_size(void) { return 256; }
+
+int moe_route_dispatch(const void *x, int x_dtype, const void *w_router, int w_dtype, const float *bias, int T, int H,
+                       int E, int k, int e_begin, int e_end, int32_t *topk_ids, float *topk_w, int32_t *counts,
+                       int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row, float *y_zero,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  if (T < 0 || H < 1 || E < 1 || E > 512 || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
+  if (e_begin < 0 || e_end <= e_begin || e_end > E) return MOE_ERR_SHAPE;
+  if ((x_dtype != MOE_F32 && x_dtype != MOE_BF16) || (w_dtype != MOE_F32 && w_dtype != MOE_BF16)) return MOE_ERR_DTYPE;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (T > 0 && (!x || !w_router || !topk_ids || !topk_w || !row_token || !row_w || !token_row)) return MOE_ERR_NULL;
+  if (T > 0 && !route_dispatch_fits(T, H, E, k, x, w_router)) return MOE_ERR_SHAPE;
+  if (y_zero && (H % 4 != 0 || !aligned16(y_zero))) return MOE_ERR_ALIGN;
+  if (!workspace || workspace_bytes < moe_route_dispatch_workspace_size()) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return MOE_ERR_ALIGN;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_route_dispatch(x, x_dtype == MOE_BF16, w_router, w_dtype == MOE_BF16, bias, T, H, E, k,
+                                          e_begin, e_end - e_begin, topk_ids, topk_w, counts, offsets, row_token,
+                                          row_w, token_row, y_zero, (uint32_t *)workspace, (hipStream_t)stream));
+}
+
 int moe_permute(const int32_t *topk_ids, const float *topk_w, int T, int k, int E, int e_begin, int e_end,
                 int32_t *counts, int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
                 const void *x, int x_dtype, int H, void *x_perm, void *workspace, size_t workspace_bytes,

@@ -65,6 +65,17 @@ hipError_t launch_combine(const float *y_perm, const int32_t *token_row, const f
 
 hipError_t launch_zero_f32(float *p, size_t n, hipStream_t s);
 
+// Decode route + local dispatch (+ zeroing of the fused-combine target) in one launch.
+// Fits for T <= kRouteDispatchMaxT, T*k <= 8192, E <= 256, H % 8 == 0 (H <= 16384) and
+// 16-byte aligned x and router weight.  ``ticket`` is a device counter that must be zero
+// before the first launch; every launch leaves it zero.
+constexpr int kRouteDispatchMaxT = 512;
+bool route_dispatch_fits(int T, int H, int E, int k, const void *x, const void *w);
+hipError_t launch_route_dispatch(const void *x, int x_bf16, const void *w, int w_bf16, const float *bias, int T, int H,
+                                 int E, int k, int lo, int El, int32_t *ids, float *gates, int32_t *counts,
+                                 int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
+                                 float *y_zero, uint32_t *ticket, hipStream_t s);
+
 // Row maps of one group holding every token once, in order: offsets = {0, T},
 // row_token[i] = i, row_w[i] = 1 (the shared expert as a one-expert grouped FFN).
 hipError_t launch_identity_rows(int T, int32_t *offsets, int32_t *row_token, float *row_w, hipStream_t s);

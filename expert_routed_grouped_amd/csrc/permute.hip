@@ -17,101 +17,19 @@
 // batches run in one workgroup of 16 waves; large ones in chunks of 1024
 // assignments (count kernel, one-workgroup scan of the chunk counts, assign
 // kernel), the chunk counts living in the caller's workspace.
-#include "common.h"
+#include "permute_dev.h"
 
 namespace {
 
+using perm::kUnroll;
+using perm::wave_count;
+using perm::wave_assign;
+using perm::wave_exclusive_scan;
+using perm::match_lanes;
+using perm::lanemask_lt;
+
 constexpr int kPermWaves = 16;
 constexpr int kPermThreads = kPermWaves * 64;
-constexpr int kUnroll = 8;  // loads in flight per lane before the batch is processed
-
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
-
-// Lanes whose ``key`` equals this lane's key, among lanes with ``active`` set.
-__device__ __forceinline__ uint64_t match_lanes(int key, bool active, int nbits) {
-  uint64_t m = __ballot(active);
-  for (int b = 0; b < nbits; b++) {
-    bool bit = (key >> b) & 1;
-    uint64_t ones = __ballot(active && bit);
-    m &= bit ? ones : ~ones;
-  }
-  return m;
-}
-
-// Count, per expert, the local assignments a in [a0, a1) of one wave into cnt[] (LDS).
-__device__ __forceinline__ void wave_count(const int32_t *__restrict__ ids, int a0, int a1, int lo, int El, int nbits,
-                                           int *cnt, int lane) {
-  for (int base = a0; base < a1; base += 64 * kUnroll) {
-    int ev[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
-      int a = base + u * 64 + lane;
-      ev[u] = a < a1 ? ids[a] - lo : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
-      if (base + u * 64 >= a1) break;
-      bool local = (unsigned)ev[u] < (unsigned)El;
-      uint64_t peers = match_lanes(ev[u], local, nbits);
-      if (local && (peers & lanemask_lt(lane)) == 0) cnt[ev[u]] += __popcll(peers);
-    }
-  }
-}
-
-// Give rows to the assignments a in [a0, a1) of one wave, in order; next[e] (LDS)
-// holds this wave's next free row of expert e and is advanced.
-__device__ __forceinline__ void wave_assign(const int32_t *__restrict__ ids, const float *__restrict__ w, int a0,
-                                            int a1, int k, int lo, int El, int nbits, int R_cap, int *next, int lane,
-                                            int32_t *__restrict__ row_token, float *__restrict__ row_w,
-                                            int32_t *__restrict__ token_row) {
-  for (int base = a0; base < a1; base += 64 * kUnroll) {
-    int ev[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
-      int a = base + u * 64 + lane;
-      ev[u] = a < a1 ? ids[a] - lo : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
-      const int a = base + u * 64 + lane;
-      if (base + u * 64 >= a1) break;
-      const bool valid = a < a1;
-      const bool local = (unsigned)ev[u] < (unsigned)El;
-      uint64_t peers = match_lanes(ev[u], local, nbits);
-      int rank = __popcll(peers & lanemask_lt(lane));
-      int r = -1;
-      if (local) {
-        int first = next[ev[u]];
-        r = first + rank;
-        if (rank == 0) next[ev[u]] = first + __popcll(peers);
-        if (r < R_cap) {  // always true for distinct experts per token; guards bad input
-          row_token[r] = a / k;
-          row_w[r] = w[a];
-        }
-      }
-      if (valid) token_row[a] = r < R_cap ? r : -1;
-    }
-  }
-}
-
-// Exclusive scan of v[0..El) in place by one wave; returns the total.
-__device__ __forceinline__ int wave_exclusive_scan(int *v, int El, int lane) {
-  int carry = 0;
-  for (int b = 0; b < El; b += 64) {
-    int e = b + lane;
-    int x = e < El ? v[e] : 0;
-    int incl = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      int o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    if (e < El) v[e] = carry + incl - x;
-    carry += __shfl(incl, 63, 64);
-  }
-  return carry;
-}
-
 // Small batches: the whole problem in one workgroup of 16 waves.
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__restrict__ ids,
                                                               const float *__restrict__ w, int N, int k, int lo,
@@ -122,39 +40,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
                                                               float *__restrict__ row_w,
                                                               int32_t *__restrict__ token_row) {
   extern __shared__ int smem[];
-  int *cnt = smem;                     // [kPermWaves][El]: per-wave counts, then per-wave next row
-  int *scan = smem + kPermWaves * El;  // [El]
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < kPermWaves * El; i += kPermThreads) cnt[i] = 0;
-  __syncthreads();
-  const int per = ((N + kPermThreads - 1) / kPermThreads) * 64;  // multiple of 64
-  const int a0 = min(N, wave * per), a1 = min(N, a0 + per);
-  wave_count(ids, a0, a1, lo, El, nbits, cnt + wave * El, lane);
-  __syncthreads();
-  for (int e = threadIdx.x; e < El; e += kPermThreads) {
-    int s = 0;
-    for (int v = 0; v < kPermWaves; v++) s += cnt[v * El + e];
-    scan[e] = s;
-    counts[e] = s;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int total = wave_exclusive_scan(scan, El, lane);
-    if (lane == 0) offsets[El] = total;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < El; e += kPermThreads) {
-    int run = scan[e];
-    offsets[e] = run;
-    for (int v = 0; v < kPermWaves; v++) {
-      int c = cnt[v * El + e];
-      cnt[v * El + e] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  wave_assign(ids, w, a0, a1, k, lo, El, nbits, R_cap, cnt + wave * El, lane, row_token, row_w, token_row);
+  perm::permute_block<kPermWaves>(ids, w, N, k, lo, El, nbits, R_cap, counts, offsets, row_token, row_w, token_row,
+                                  smem);
 }
 
 // Large batches: chunks of kChunk assignments, one 4-wave workgroup each.

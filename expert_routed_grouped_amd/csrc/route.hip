@@ -8,7 +8,7 @@
 // through scalar loads.  Top-k is k rounds of a wave-wide max over 64-bit keys
 // (orderable logit bits, inverted expert id), so equal logits go to the lower
 // expert index; the gates are a softmax over the k selected logits.
-#include "common.h"
+#include "permute_dev.h"
 
 namespace {
 
@@ -66,9 +66,9 @@ __device__ __forceinline__ float load1(const void *p, size_t i) {
 // Block = EC waves (wave c owns experts 64c .. 64c+63), TT tokens per block.
 // VEC: H % 8 == 0 and 16-byte aligned rows (8-wide loads); otherwise one h at a time.
 template <int TT, int EC, bool XB, bool WB, bool VEC>
-__global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__ x, const void *__restrict__ w,
-                                                        const float *__restrict__ bias, int T, int H, int E, int k,
-                                                        int32_t *__restrict__ ids, float *__restrict__ gates) {
+__device__ __forceinline__ void route_tokens(const void *__restrict__ x, const void *__restrict__ w,
+                                             const float *__restrict__ bias, int T, int H, int E, int k,
+                                             int32_t *__restrict__ ids, float *__restrict__ gates) {
   __shared__ float lg[TT][64 * EC];
   const int lane = threadIdx.x & 63;
   const int c = threadIdx.x >> 6;
@@ -220,6 +220,50 @@ __global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__
       gates[(size_t)t * k + lane] = u / sum;
     }
   }
+}
+
+template <int TT, int EC, bool XB, bool WB, bool VEC>
+__global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__ x, const void *__restrict__ w,
+                                                        const float *__restrict__ bias, int T, int H, int E, int k,
+                                                        int32_t *__restrict__ ids, float *__restrict__ gates) {
+  route_tokens<TT, EC, XB, WB, VEC>(x, w, bias, T, H, E, k, ids, gates);
+}
+
+// Decode route + local dispatch in one launch: block t routes token t (as route_kernel with one
+// token per block) and zeroes row t of the fused-combine target; the last block to finish --
+// found with a ticket counter, each block publishing its routing before it takes a ticket --
+// groups the assignments by expert (the single-workgroup permutation) and resets the ticket.
+// No block ever waits for another, so no co-residency is assumed.
+template <int EC, bool XB, bool WB>
+__global__ __launch_bounds__(64 * EC) void route_dispatch_kernel(const void *__restrict__ x, const void *__restrict__ w,
+                                                                 const float *__restrict__ bias, int T, int H, int E,
+                                                                 int k, int lo, int El, int nbits,
+                                                                 int32_t *__restrict__ ids, float *__restrict__ gates,
+                                                                 int32_t *__restrict__ counts,
+                                                                 int32_t *__restrict__ offsets,
+                                                                 int32_t *__restrict__ row_token,
+                                                                 float *__restrict__ row_w,
+                                                                 int32_t *__restrict__ token_row,
+                                                                 float *__restrict__ y_zero,
+                                                                 uint32_t *__restrict__ ticket) {
+  __shared__ int last;
+  if (y_zero != nullptr) {
+    f32x4_t *row = (f32x4_t *)(y_zero + (size_t)blockIdx.x * H);
+    for (int i = threadIdx.x; i < H / 4; i += blockDim.x) row[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  route_tokens<1, EC, XB, WB, true>(x, w, bias, T, H, E, k, ids, gates);
+  __threadfence();  // this block's ids and gates are visible device-wide before its ticket
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(ticket, 1u) == (uint32_t)gridDim.x - 1u;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();  // acquire: every other block's routing
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  const int N = T * k;
+  const int R_cap = T * (k < El ? k : El);
+  perm::permute_block<EC>(ids, gates, N, k, lo, El, nbits, R_cap, counts, offsets, row_token, row_w, token_row,
+                          (int *)dyn);
+  if (threadIdx.x == 0) atomicExch(ticket, 0u);
 }
 
 // Top-k + gates of one token from its logits in LDS (wave-wide; every lane of the
@@ -423,6 +467,48 @@ hipError_t launch_ec(const void *x, int xb, const void *w, int wb, const float *
 }
 
 }  // namespace
+
+namespace {
+
+template <int EC>
+hipError_t launch_rd(const void *x, int xb, const void *w, int wb, const float *bias, int T, int H, int E, int k, int lo,
+                     int El, int32_t *ids, float *gates, int32_t *counts, int32_t *offsets, int32_t *row_token,
+                     float *row_w, int32_t *token_row, float *y_zero, uint32_t *ticket, hipStream_t s) {
+  int nbits = 0;
+  while ((1 << nbits) < El) nbits++;
+  const size_t xs_bytes = sizeof(float) * (size_t)H, perm_bytes = sizeof(int) * (size_t)(EC + 1) * El;
+  const size_t shm = xs_bytes > perm_bytes ? xs_bytes : perm_bytes;
+#define RD_CASE(XB, WB)                                                                                          \
+  if (xb == XB && wb == WB) {                                                                                    \
+    hipLaunchKernelGGL((route_dispatch_kernel<EC, XB, WB>), dim3(T), dim3(64 * EC), shm, s, x, w, bias, T, H, E, k, \
+                       lo, El, nbits, ids, gates, counts, offsets, row_token, row_w, token_row, y_zero, ticket);   \
+    return hipGetLastError();                                                                                    \
+  }
+  RD_CASE(true, true) RD_CASE(false, false) RD_CASE(true, false) RD_CASE(false, true)
+#undef RD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool route_dispatch_fits(int T, int H, int E, int k, const void *x, const void *w) {
+  return T >= 1 && T <= kRouteDispatchMaxT && (long long)T * k <= 8192 && E <= 256 && H % 8 == 0 &&
+         H * sizeof(float) <= 65536 && (((uintptr_t)x | (uintptr_t)w) % 16 == 0);
+}
+
+hipError_t launch_route_dispatch(const void *x, int x_bf16, const void *w, int w_bf16, const float *bias, int T, int H,
+                                 int E, int k, int lo, int El, int32_t *ids, float *gates, int32_t *counts,
+                                 int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
+                                 float *y_zero, uint32_t *ticket, hipStream_t s) {
+  if (E <= 64)
+    return launch_rd<1>(x, x_bf16, w, w_bf16, bias, T, H, E, k, lo, El, ids, gates, counts, offsets, row_token, row_w,
+                        token_row, y_zero, ticket, s);
+  if (E <= 128)
+    return launch_rd<2>(x, x_bf16, w, w_bf16, bias, T, H, E, k, lo, El, ids, gates, counts, offsets, row_token, row_w,
+                        token_row, y_zero, ticket, s);
+  return launch_rd<4>(x, x_bf16, w, w_bf16, bias, T, H, E, k, lo, El, ids, gates, counts, offsets, row_token, row_w,
+                      token_row, y_zero, ticket, s);
+}
 
 hipError_t launch_route(const void *x, int x_bf16, const void *w, int w_bf16, const float *bias, int T, int H, int E,
                         int k, int32_t *ids, float *gates, hipStream_t s) {

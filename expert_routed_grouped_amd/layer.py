@@ -50,7 +50,7 @@ def to_device(inputs: dict, device="cuda") -> dict:
 class LayerBuffers:
     """Device buffers of one layer shape, reused across calls."""
 
-    def __init__(self, cfg, device="cuda", fused: Optional[bool] = None):
+    def __init__(self, cfg, device="cuda", fused: Optional[bool] = None, use_route_dispatch: bool = True):
         T, k, El, H, I = cfg.T, cfg.k, cfg.E_loc, cfg.H, cfg.I
         self.cfg = cfg
         self.R_cap = T * min(k, El)
@@ -71,17 +71,26 @@ class LayerBuffers:
         self.y_perm = None if self.fused else torch.empty((max(self.R_cap, 1), H), dtype=torch.float32, **d)
         self.shared_ws = (torch.empty(moe.moe_shared_workspace_size(T, cfg.I_s, adt), dtype=torch.uint8, **d)
                           if cfg.I_s > 0 else None)
+        # decode-sized batches route and dispatch in one launch (its ticket workspace starts zeroed)
+        fits = 1 <= T <= 512 and T * k <= 8192 and cfg.E <= 256 and H % 8 == 0 and H <= 16384
+        self.rd_ws = moe.moe_route_dispatch_workspace(device) if (fits and use_route_dispatch) else None
 
 
 def run_layer(dev: dict, bufs: LayerBuffers, stream=None) -> torch.Tensor:
     """route -> permute -> grouped FFN (-> combine) (-> shared expert).  Returns y [T,H] fp32."""
     cfg = bufs.cfg
-    moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=stream)
-    p = moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=bufs.perm, stream=stream)
+    p = bufs.perm
+    if bufs.rd_ws is not None:  # one launch: route, dispatch and (fused combine) the zeroing of y
+        moe.moe_route_dispatch(dev["x"], dev["w_router"], dev["bias"], cfg.k, cfg.E, cfg.lo, cfg.hi, bufs.rd_ws,
+                               bufs.topk_ids, bufs.topk_w, p, y_zero=bufs.y if bufs.fused else None, stream=stream)
+    else:
+        moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=stream)
+        moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=p, stream=stream)
     if bufs.fused:
         moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
                             dev["w_gate_up"], dev["w_down"], dev.get("s_gate_up"), dev.get("s_down"),
-                            y=bufs.y, workspace=bufs.workspace, gather=True, zero_y=True, stream=stream)
+                            y=bufs.y, workspace=bufs.workspace, gather=True, zero_y=bufs.rd_ws is None,
+                            stream=stream)
     else:
         moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
                             dev["w_gate_up"], dev["w_down"], dev.get("s_gate_up"), dev.get("s_down"),

@@ -24,7 +24,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTY
 # Every symbol moe.h declares (checked by the CPU test suite).
 EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_permute_workspace_size",
            "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_quantize_mx", "moe_ffn_mx_workspace_size",
-           "moe_grouped_ffn_mx", "moe_shared_workspace_size", "moe_shared_expert")
+           "moe_grouped_ffn_mx", "moe_shared_workspace_size", "moe_shared_expert", "moe_route_dispatch_workspace_size",
+           "moe_route_dispatch")
 
 
 class MoEError(RuntimeError):
@@ -70,6 +71,10 @@ def lib():
         L.moe_shared_workspace_size.argtypes = [I, I, I]
         L.moe_shared_expert.restype = I
         L.moe_shared_expert.argtypes = [P, I, I, I, I, P, P, I, P, P, P, P, Z, ctypes.c_uint, P]
+        L.moe_route_dispatch_workspace_size.restype = Z
+        L.moe_route_dispatch_workspace_size.argtypes = []
+        L.moe_route_dispatch.restype = I
+        L.moe_route_dispatch.argtypes = [P, I, P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
         _lib = L
     return _lib
 
@@ -255,3 +260,22 @@ def moe_shared_expert(x: torch.Tensor, w_gate_up: torch.Tensor, w_down: torch.Te
         _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(), MOE_FFN_ZERO_Y if zero_y else 0,
         _stream(stream)))
     return y
+
+
+def moe_route_dispatch_workspace(device="cuda") -> torch.Tensor:
+    """A zeroed workspace for moe_route_dispatch (its ticket counter starts at zero)."""
+    return torch.zeros(int(lib().moe_route_dispatch_workspace_size()), dtype=torch.uint8, device=device)
+
+
+def moe_route_dispatch(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor], k: int, E: int,
+                       e_begin: int, e_end: int, workspace: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                       out: dict, y_zero: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Route + local dispatch of a decode batch in one launch; ``out`` holds counts, offsets,
+    row_token, row_w, token_row (as from moe_permute); zeroes ``y_zero`` when given."""
+    T, H = x.shape
+    _check("moe_route_dispatch", lib().moe_route_dispatch(
+        _ptr(x), _dtype(x), _ptr(w_router), _dtype(w_router), _ptr(bias), T, H, E, k, e_begin, e_end, _ptr(topk_ids),
+        _ptr(topk_w), _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["row_token"]), _ptr(out["row_w"]),
+        _ptr(out["token_row"]), _ptr(y_zero), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out

@@ -10,7 +10,8 @@
  *                    down-projection epilogue (or per-row outputs for moe_combine)
  *   moe_combine      gate-weighted gather-sum of per-row outputs to token order
  *
- * plus moe_shared_expert (an always-active expert added to y) and the W8A8
+ * plus moe_route_dispatch (the first two calls of a decode batch in one
+ * launch), moe_shared_expert (an always-active expert added to y) and the W8A8
  * MXFP8 variant of the expert FFN (moe_quantize_mx, moe_grouped_ffn_mx).
  *
  * The method follows three pages: "AI-infra book, ch. 9 Distributed inference"
@@ -261,6 +262,37 @@ int moe_grouped_ffn_mx(const uint8_t *a_codes, const uint8_t *a_scales, const in
  */
 int moe_combine(const float *y_perm, const int32_t *token_row, const float *topk_w, int T, int k, int H,
                 float *y, void *stream);
+
+/* Bytes of workspace moe_route_dispatch needs (one ticket counter). */
+size_t moe_route_dispatch_workspace_size(void);
+
+/*
+ * moe_route_dispatch - moe_route and moe_permute of a decode batch in one launch.
+ *
+ * Defined by: "Hosting Qwen on Blackwell", section "MoE Dispatch - Combine":
+ * for decoding the dispatch work (routing information aggregated, each local
+ * expert's tokens grouped for its GEMM) runs as one kernel, where prefill
+ * splits it into several because the routing step needs fewer blocks.
+ *
+ * Results are exactly those of moe_route (topk_ids, topk_w) followed by
+ * moe_permute without the x_perm gather (counts, offsets, row_token, row_w,
+ * token_row), same layouts and sizes.  If y_zero is not NULL, y_zero [T,H]
+ * fp32 is also zeroed in the same launch (the target of moe_grouped_ffn's
+ * fused combine, which then runs without MOE_FFN_ZERO_Y).  Each block routes
+ * one token; the last block to finish groups the assignments, so no block
+ * ever waits on another.  Supported sizes: 1 <= T <= 512, T*k <= 8192,
+ * E <= 256, H a multiple of 8 and at most 16384, x and w_router 16-byte
+ * aligned (else MOE_ERR_SHAPE: use moe_route + moe_permute).  The workspace
+ * (moe_route_dispatch_workspace_size() bytes, 256-byte aligned) holds a
+ * ticket counter that must be zero before the first call (zero it once when
+ * allocating); every call leaves it zero.  Calls that share a workspace must
+ * not overlap (run them on one stream).  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE,
+ * MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_route_dispatch(const void *x, int x_dtype, const void *w_router, int w_dtype, const float *bias, int T, int H,
+                       int E, int k, int e_begin, int e_end, int32_t *topk_ids, float *topk_w, int32_t *counts,
+                       int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row, float *y_zero,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace moe_shared_expert needs (h [T, I_s] of x_dtype, then its row maps). */
 size_t moe_shared_workspace_size(int T, int I_s, int x_dtype);

@@ -137,6 +137,23 @@ def test_shared_expert_validation(kw, code):
     assert shared(**kw) == code
 
 
+def route_dispatch(x=FAKE, xd=1, w=FAKE, wd=1, T=64, H=256, E=16, k=4, lo=0, hi=16, ids=FAKE, g=FAKE, c=FAKE,
+                   o=FAKE, rt=FAKE, rw=FAKE, tr=FAKE, y=None, ws=FAKE, wsb=256):
+    return moe.lib().moe_route_dispatch(x, xd, w, wd, None, T, H, E, k, lo, hi, ids, g, c, o, rt, rw, tr, y, ws, wsb,
+                                        None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=513), -2), (dict(T=300, k=32, E=64, hi=64), -2), (dict(E=257, hi=257), -2), (dict(H=100), -2),
+    (dict(k=17, E=16), -2), (dict(lo=4, hi=4), -2), (dict(hi=17), -2), (dict(x=FAKE_ODD), -2), (dict(xd=2), -3),
+    (dict(x=None), -1), (dict(c=None), -1), (dict(rt=None), -1), (dict(ws=None), -4), (dict(wsb=16), -4),
+    (dict(y=FAKE_ODD), -6), (dict(T=0, x=None), 0),
+])
+def test_route_dispatch_validation(kw, code):
+    # every case is rejected (or is empty) on the host before anything is launched
+    assert route_dispatch(**kw) == code
+
+
 def test_workspace_size():
     L = moe.lib()
     # per-chunk (1024 assignments) expert counts
@@ -149,6 +166,7 @@ def test_workspace_size():
     # h as MXFP8: codes [R_cap, I] and scales [R_cap, I/32], each 256-byte aligned
     ws = L.moe_ffn_mx_workspace_size(48000, 1536)
     assert ws >= 48000 * 1536 + 48000 * 48 and ws % 256 == 0
+    assert L.moe_route_dispatch_workspace_size() == 256
     # shared expert: h [T, I_s] plus its row maps (offsets, row_token, row_w)
     ws = L.moe_shared_workspace_size(6000, 1536, 1)
     assert ws >= 6000 * 1536 * 2 + 8 + 2 * 6000 * 4 and ws % 256 == 0

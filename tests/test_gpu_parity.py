@@ -381,6 +381,56 @@ def test_full_workload_layer(name):
 
 
 # ----------------------------------------------------------------------------
+# decode route + dispatch in one launch: bit-identical to moe_route + moe_permute
+# ----------------------------------------------------------------------------
+RD_CASES = [
+    CONFIGS["decode"],
+    LayerConfig("rd_t1", T=1, H=256, E=16, k=4, I=64, seed=501),
+    LayerConfig("rd_max", T=512, H=512, E=128, k=16, I=64, seed=502, w_std=0.05),     # T*k = 8192
+    LayerConfig("rd_e256", T=100, H=256, E=256, k=8, I=64, seed=503, w_std=0.05),    # four waves per block
+    LayerConfig("rd_e40_local", T=77, H=128, E=40, k=3, I=64, e_begin=5, e_end=30, seed=504),  # one wave
+    LayerConfig("rd_f32", T=33, H=64, E=8, k=2, I=64, act="f32", wdt="f32", init="fan_in", seed=505),
+    LayerConfig("rd_zipf", T=200, H=256, E=64, k=8, I=64, bias="zipf", seed=506, w_std=0.05),
+]
+
+
+@pytest.mark.parametrize("cfg", RD_CASES, ids=lambda c: c.name)
+def test_route_dispatch_matches_route_then_permute(cfg):
+    inp = synth.make_inputs(cfg, with_weights=False)
+    dev = L.to_device(inp)
+    say(f"route+dispatch {cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} local [{cfg.lo},{cfg.hi})")
+    ids, w = moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k)
+    p = moe.moe_permute(ids, w, cfg.E, cfg.lo, cfg.hi)
+    torch.cuda.synchronize()
+    ids_o, w_o, _ = O.route(inp["x"], inp["w_router"], inp["bias"], cfg.k)
+    p_o = O.permute(ids_o, w_o, cfg.lo, cfg.hi)
+    R = int(p_o["R"])
+    ws = moe.moe_route_dispatch_workspace()
+    El = cfg.hi - cfg.lo
+    for rep in range(3):  # the ticket counter must come back to zero after every call
+        out = dict(counts=torch.full((El,), -7, dtype=torch.int32, device="cuda"),
+                   offsets=torch.full((El + 1,), -7, dtype=torch.int32, device="cuda"),
+                   row_token=torch.full((max(p["R_cap"], 1),), -7, dtype=torch.int32, device="cuda"),
+                   row_w=torch.full((max(p["R_cap"], 1),), -7.0, dtype=torch.float32, device="cuda"),
+                   token_row=torch.full((cfg.T, cfg.k), -7, dtype=torch.int32, device="cuda"))
+        ids2 = torch.full_like(ids, -7)
+        w2 = torch.full_like(w, -7.0)
+        y = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.float32, device="cuda")
+        moe.moe_route_dispatch(dev["x"], dev["w_router"], dev["bias"], cfg.k, cfg.E, cfg.lo, cfg.hi, ws, ids2, w2,
+                               out, y_zero=y)
+        torch.cuda.synchronize()
+        assert torch.equal(ids2, ids) and torch.equal(w2.view(torch.int32), w.view(torch.int32))
+        assert np.array_equal(ids2.cpu().numpy(), ids_o)
+        for key in ("counts", "offsets", "token_row"):
+            assert torch.equal(out[key], p[key]), key
+        assert torch.equal(out["row_token"][:R], p["row_token"][:R])
+        assert torch.equal(out["row_w"][:R].view(torch.int32), p["row_w"][:R].view(torch.int32))
+        assert np.array_equal(out["row_token"][:R].cpu().numpy(), p_o["row_token"])
+        assert torch.all(y == 0)
+        assert torch.all(ws == 0)
+
+
+# ----------------------------------------------------------------------------
 # shared expert: standalone against the oracle, and added to the routed layer
 # ----------------------------------------------------------------------------
 SHARED_CASES = [
