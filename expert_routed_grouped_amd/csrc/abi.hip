@@ -250,6 +250,7 @@ int moe_quantize_mx(const void *x, int x_dtype, int rows, int K, uint8_t *codes,
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (rows == 0) return MOE_OK;
   if (!x || !codes || !scales) return MOE_ERR_NULL;
+  if (!aligned16(x) || ((uintptr_t)codes & 7u) != 0) return MOE_ERR_ALIGN;  // 16-byte loads, 8-byte stores
   return hip_status(launch_quantize_mx(x, x_dtype == MOE_BF16, rows, K, codes, scales, (hipStream_t)stream));
 }
 

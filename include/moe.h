@@ -211,8 +211,9 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
  *   scales[r, b] = s;  codes[r, 32b+i] = E4M3 code nearest to v_i / 2^(s-127),
  *   ties to the even code, magnitudes >= 448 saturate to 448, sign bit kept.
  * x: rows x K, MOE_F32 or MOE_BF16; codes [rows, K] uint8; scales [rows, K/32]
- * uint8.  K must be a multiple of 32 and rows >= 0.  Errors: MOE_ERR_NULL,
- * MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_HIP.
+ * uint8.  K must be a multiple of 32 and rows >= 0; x 16-byte aligned, codes
+ * 8-byte aligned.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE,
+ * MOE_ERR_ALIGN, MOE_ERR_HIP.
  */
 int moe_quantize_mx(const void *x, int x_dtype, int rows, int K, uint8_t *codes, uint8_t *scales, void *stream);
 

@@ -114,7 +114,7 @@ def test_ffn_mx_validation(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(K=48), -2), (dict(K=0), -2), (dict(rows=-1), -2), (dict(xd=2), -3), (dict(x=None), -1),
-    (dict(q=None), -1), (dict(rows=0), 0),
+    (dict(q=None), -1), (dict(rows=0), 0), (dict(x=FAKE_ODD), -6), (dict(q=FAKE_ODD), -6),
 ])
 def test_quantize_mx_validation(kw, code):
     a = dict(x=FAKE, xd=1, rows=4, K=64, q=FAKE, s=FAKE)

@@ -486,10 +486,12 @@ def test_layer_with_shared_expert_matches_oracle(cfg, fused):
 # ----------------------------------------------------------------------------
 # W8A8 MXFP8: quantisation (bit-exact) and the MX grouped FFN against the MX oracle
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f32", "bf16_large"])
 def test_quantize_mx_matches_oracle(dt):
     rng = np.random.default_rng(301)
     rows, K = 333, 384
+    if dt == "bf16_large":  # more 8-value vectors than lanes in the grid: the grid-stride loop runs twice
+        rows, K, dt = 2100, 4096, "bf16"
     x32 = (rng.standard_normal((rows, K)) * np.exp2(rng.integers(-20, 20, (rows, 1)))).astype(np.float32)
     x32[0, :32] = 0.0                                  # all-zero block
     x32[1, :32] = -0.0                                 # negative zeros keep their sign bit
