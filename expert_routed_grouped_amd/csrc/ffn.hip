@@ -349,7 +349,8 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
   const long long mt1 = ((long long)a.R_cap + (long long)a.El * (TBM - 1)) / TBM;
   const long long mt2 = (long long)a.El * ceil_div_i(a.T, TBM);
   const long long max_mt = mt1 < mt2 ? mt1 : mt2;
-  const bool fp8 = a.w_dt == 2;
+  // only fp8 weights get here (bf16 weights take the direct-to-LDS kernel above)
+  if (a.w_dt != 2) return hipErrorInvalidValue;
   TileParams tp{};
   tp.offsets = a.offsets;
   tp.row_token = a.row_token;
@@ -364,8 +365,7 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
     tp.scale = a.s_gu;
     tp.out = a.h;
     const int grid = (int)(max_mt * ceil_div_i(a.I, 128));
-    if (fp8) err = a.gather ? launch_big<0, true, true, false>(tp, grid, s) : launch_big<0, true, false, false>(tp, grid, s);
-    else err = a.gather ? launch_big<0, false, true, false>(tp, grid, s) : launch_big<0, false, false, false>(tp, grid, s);
+    err = a.gather ? launch_big<0, true, true, false>(tp, grid, s) : launch_big<0, true, false, false>(tp, grid, s);
     if (err != hipSuccess) return err;
   }
   if (!second) return hipSuccess;
@@ -375,8 +375,6 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
   const bool atomic = a.y != nullptr;
   tp.out = atomic ? (void *)a.y : (void *)a.y_perm;
   const int grid = (int)(max_mt * ceil_div_i(a.H, big::BN));
-  if (fp8) err = atomic ? launch_big<1, true, false, true>(tp, grid, s) : launch_big<1, true, false, false>(tp, grid, s);
-  else err = atomic ? launch_big<1, false, false, true>(tp, grid, s) : launch_big<1, false, false, false>(tp, grid, s);
-  return err;
+  return atomic ? launch_big<1, true, false, true>(tp, grid, s) : launch_big<1, true, false, false>(tp, grid, s);
 }
 

@@ -116,7 +116,8 @@ __device__ __forceinline__ void route_tokens(const void *__restrict__ x, const v
     // 32 h per step; a ring of ROUTE_NS register sets keeps the weight pieces of
     // the next ROUTE_NS-1 steps in flight while a step computes (each lane reads
     // its own expert row, so only prefetch depth hides the L2 latency)
-    constexpr int HS = 32, P = HS * (WB ? 2 : 4) / 16, NS = ROUTE_NS;
+    // fp32 weights take twice the registers per step: half the ring depth
+    constexpr int HS = 32, P = HS * (WB ? 2 : 4) / 16, NS = WB ? ROUTE_NS : ROUTE_NS / 2;
     const int nsteps = H / HS;
     u32x4_t ring[NS][P];
     auto wload = [&](u32x4_t(&b)[P], int st) __attribute__((always_inline)) {

@@ -441,6 +441,7 @@ SHARED_CASES = [
     LayerConfig("sh_fp8", T=300, H=256, E=4, k=2, I=64, wdt="fp8", seed=404, w_std=0.05, I_s=256),
     LayerConfig("sh_fp8_small", T=40, H=256, E=4, k=2, I=64, wdt="fp8", seed=405, w_std=0.05, I_s=192),
     LayerConfig("sh_f32", T=50, H=128, E=4, k=2, I=64, act="f32", wdt="f32", init="fan_in", seed=406, I_s=128),
+    LayerConfig("sh_t1", T=1, H=4096, E=4, k=2, I=64, seed=407, w_std=0.02, I_s=1536),  # one token, split K
 ]
 
 
