@@ -333,6 +333,39 @@ def test_ffn_empty_batch_zeroes_y():
 
 
 # ----------------------------------------------------------------------------
+# the decode layer under HIP graph capture: every replay against the oracle
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "combine"])
+def test_layer_graph_replay_matches_oracle(fused):
+    # every step of the layer is a kernel of the library (zeroing included), so the whole call
+    # can be captured once and replayed; eager work runs between the replays
+    cfg = LayerConfig("graph", T=64, H=512, E=32, k=4, I=256, seed=601, w_std=0.05)
+    inp = host_inputs(cfg)
+    dev = L.to_device(inp)
+    bufs = L.LayerBuffers(cfg, fused=fused)
+    r = O.layer(inp)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        L.run_layer(dev, bufs, stream=s)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        L.run_layer(dev, bufs, stream=s)
+    for rep in range(4):
+        bufs.y.fill_(float("nan"))
+        bufs.topk_ids.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bufs.topk_ids.cpu().numpy(), r["topk_ids"]), f"replay {rep}"
+        check_y(bufs.y.cpu().numpy(), r["y"], f"graph replay {rep} fused={fused}")
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between the replays
+        torch.cuda.synchronize()
+        del junk
+
+
+# ----------------------------------------------------------------------------
 # full workload shapes, benchmark launch configuration, sampled tokens
 # ----------------------------------------------------------------------------
 def sample_tokens(cfg, ids, n=24):
