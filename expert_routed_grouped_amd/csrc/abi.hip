@@ -56,7 +56,9 @@ int moe_route_dispatch(const void *x, int x_dtype, const void *w_router, int w_d
   if (y_zero && (H % 4 != 0 || !aligned16(y_zero))) return MOE_ERR_ALIGN;
   if (!workspace || workspace_bytes < moe_route_dispatch_workspace_size()) return MOE_ERR_WORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return MOE_ERR_ALIGN;
-  if (T == 0) return MOE_OK;
+  if (T == 0)  // nothing to route: zero counts and offsets as moe_permute does
+    return hip_status(launch_permute(nullptr, nullptr, 0, k, e_begin, e_end - e_begin, counts, offsets, row_token,
+                                     row_w, token_row, nullptr, (hipStream_t)stream));
   return hip_status(launch_route_dispatch(x, x_dtype == MOE_BF16, w_router, w_dtype == MOE_BF16, bias, T, H, E, k,
                                           e_begin, e_end - e_begin, topk_ids, topk_w, counts, offsets, row_token,
                                           row_w, token_row, y_zero, (uint32_t *)workspace, (hipStream_t)stream));

@@ -277,7 +277,8 @@ size_t moe_route_dispatch_workspace_size(void);
  *
  * Results are exactly those of moe_route (topk_ids, topk_w) followed by
  * moe_permute without the x_perm gather (counts, offsets, row_token, row_w,
- * token_row), same layouts and sizes.  If y_zero is not NULL, y_zero [T,H]
+ * token_row), same layouts and sizes (T = 0 zeroes counts and offsets).  If
+ * y_zero is not NULL, y_zero [T,H]
  * fp32 is also zeroed in the same launch (the target of moe_grouped_ffn's
  * fused combine, which then runs without MOE_FFN_ZERO_Y).  Each block routes
  * one token; the last block to finish groups the assignments, so no block

@@ -147,7 +147,7 @@ def route_dispatch(x=FAKE, xd=1, w=FAKE, wd=1, T=64, H=256, E=16, k=4, lo=0, hi=
     (dict(T=513), -2), (dict(T=300, k=32, E=64, hi=64), -2), (dict(E=257, hi=257), -2), (dict(H=100), -2),
     (dict(k=17, E=16), -2), (dict(lo=4, hi=4), -2), (dict(hi=17), -2), (dict(x=FAKE_ODD), -2), (dict(xd=2), -3),
     (dict(x=None), -1), (dict(c=None), -1), (dict(rt=None), -1), (dict(ws=None), -4), (dict(wsb=16), -4),
-    (dict(y=FAKE_ODD), -6), (dict(T=0, x=None), 0),
+    (dict(y=FAKE_ODD), -6),
 ])
 def test_route_dispatch_validation(kw, code):
     # every case is rejected (or is empty) on the host before anything is launched

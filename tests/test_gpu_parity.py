@@ -463,6 +463,21 @@ def test_route_dispatch_matches_route_then_permute(cfg):
         assert torch.all(ws == 0)
 
 
+def test_route_dispatch_empty_batch_zeroes_counts():
+    ws = moe.moe_route_dispatch_workspace()
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    wr = torch.zeros((16, 256), dtype=torch.bfloat16, device="cuda")
+    out = dict(counts=torch.full((8,), -7, dtype=torch.int32, device="cuda"),
+               offsets=torch.full((9,), -7, dtype=torch.int32, device="cuda"),
+               row_token=torch.empty(1, dtype=torch.int32, device="cuda"),
+               row_w=torch.empty(1, dtype=torch.float32, device="cuda"),
+               token_row=torch.empty((0, 4), dtype=torch.int32, device="cuda"))
+    moe.moe_route_dispatch(x, wr, None, 4, 16, 4, 12, ws, torch.empty((0, 4), dtype=torch.int32, device="cuda"),
+                           torch.empty((0, 4), dtype=torch.float32, device="cuda"), out)
+    torch.cuda.synchronize()
+    assert torch.all(out["counts"] == 0) and torch.all(out["offsets"] == 0)
+
+
 # ----------------------------------------------------------------------------
 # shared expert: standalone against the oracle, and added to the routed layer
 # ----------------------------------------------------------------------------
