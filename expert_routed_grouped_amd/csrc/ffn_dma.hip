@@ -156,7 +156,7 @@ __device__ __forceinline__ void dma_body(const TileParams &p, const char *abase,
             if (m < mvalid) {
               const int row = rbase + m;
               if constexpr (ATOMIC) atomicAdd(out + (size_t)p.row_token[row] * p.H + n, p.row_w[row] * acc[i][j][r]);
-              else __builtin_nontemporal_store(acc[i][j][r], out + (size_t)row * p.H + n);  // read once, by the combine
+              else out[(size_t)row * p.H + n] = acc[i][j][r];
             }
           }
       }
