@@ -89,6 +89,8 @@ def _ptr(t: Optional[torch.Tensor]):
         return None
     if not t.is_contiguous():
         raise ValueError("tensors passed to the MoE library must be contiguous")
+    if not t.is_cuda:  # every array of the ABI is device memory; a host pointer would fault the GPU
+        raise ValueError("tensors passed to the MoE library must be on the GPU")
     return ctypes.c_void_p(t.data_ptr())
 
 

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from expert_routed_grouped_amd import moe
 
@@ -186,3 +187,13 @@ def test_python_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         moe.lib()
+
+
+def test_binding_rejects_host_and_strided_tensors():
+    # a host pointer handed to a kernel would fault the GPU: the binding refuses it first
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    wr = torch.zeros((8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="on the GPU"):
+        moe.moe_route(x, wr, None, 2, torch.zeros((4, 2), dtype=torch.int32), torch.zeros((4, 2)))
+    with pytest.raises(ValueError, match="contiguous"):
+        moe.moe_quantize_mx(torch.zeros((64, 64)).t())
