@@ -53,14 +53,18 @@ def parse():
     ap.add_argument("--flush-steps", type=int, default=20,
                     help="extra steps, each after writing a 1 GiB scratch buffer (cold L2 and Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weights", default="packed", choices=["packed", "row-major"],
+                    help="layout of the resident bf16/fp8 expert weights (packed once with moe_pack_weights "
+                         "before timing; MXFP8 and fp32 weights are always row-major)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch from a committed counter summary, or None when there is none or the kernel's
-    sources changed since the counters were taken (the summary records their SHA-256)."""
+def measured_traffic(kernel, workload, weights):
+    """HBM bytes per launch from a committed counter summary, or None when there is none, it was taken
+    with the other weight layout, or the kernel's sources changed since the counters were taken (the
+    summary records their SHA-256)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
@@ -75,7 +79,7 @@ def measured_traffic(kernel, workload):
         for src in fields["kernel_sources"].split():
             with open(os.path.join(ROOT, src), "rb") as f:
                 h.update(f.read())
-        if h.hexdigest() != fields["source_sha256"]:
+        if h.hexdigest() != fields["source_sha256"] or fields.get("weights", "row-major") != weights:
             return None
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, OSError, ValueError):
@@ -155,6 +159,9 @@ def main():
     print(f"[bench] generating {args.config} inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg)
     dev = L.to_device(inp)
+    if args.weights == "packed":
+        L.pack_weights(dev)  # one-time layout change of the resident weights, like loading them
+    packed = bool(dev.get("packed", False))
     bufs = L.LayerBuffers(cfg)
     stream = torch.cuda.current_stream()
     p = bufs.perm
@@ -173,7 +180,7 @@ def main():
         else:
             moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
                                 dev["w_gate_up"], dev["w_down"], dev["s_gate_up"], dev["s_down"], phase=phase,
-                                **outs, **common)
+                                packed=packed, **outs, **common)
 
     def step(ev=None):
         if ev is not None:
@@ -204,7 +211,7 @@ def main():
 
     def shared():
         moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], bufs.y, dev.get("ss_gate_up"),
-                              dev.get("ss_down"), workspace=bufs.shared_ws, stream=stream)
+                              dev.get("ss_down"), workspace=bufs.shared_ws, packed=packed, stream=stream)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -270,7 +277,8 @@ def main():
         layer_flops += A.useful_flops(T, H, cfg.I_s)
         layer_bytes += A.expert_bytes(H, cfg.I_s, wbytes, cfg.wdt == "fp8")
     gu_s = float(np.mean(gu_ms)) * 1e-3
-    if args.config == "decode":
+    hbm_bound = args.config.startswith("decode")  # a few rows per expert: the weight stream bounds the kernel
+    if hbm_bound:
         achieved = gu_bytes / gu_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
@@ -282,13 +290,13 @@ def main():
     kernel = ("ffn_mx_kernel" if mx else
               ("ffn_stream_kernel" if bufs.R_cap <= 48 * cfg.E_loc else
                ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel")))
-    roof["traffic"] = measured_traffic(kernel, args.config)
+    roof["traffic"] = measured_traffic(kernel, args.config, "packed" if packed else "row-major")
     # rows the grouped GEMM actually multiplies, by the tiling of the kernel in use
     padded = (A.padded_rows(counts, 64) if kernel == "ffn_stream_kernel" else
               (A.split_padded_rows(counts, 256, 64) if kernel == "ffn_dma_kernel" else
                (A.split_padded_rows(counts, 192, 64) if kernel == "ffn_mx_kernel" else A.padded_rows(counts, 256))))
     roof.update({"kernel": f"{kernel} (gate/up + SwiGLU half, one launch)", "avg_ms": round(float(np.mean(gu_ms)), 4),
-                 "algorithmic_per_launch": gu_bytes if args.config == "decode" else gu_flops})
+                 "algorithmic_per_launch": gu_bytes if hbm_bound else gu_flops})
     layer_s = ms_per_step * 1e-3
     res = {
         "metric": METRIC,
@@ -307,7 +315,8 @@ def main():
         "config": {"workload": WORKLOADS[args.config], "T": T, "H": H, "E": cfg.E, "k": cfg.k, "I": I,
                    "local_experts": [cfg.lo, cfg.hi], "parallelism": "none (one GPU)",
                    "combine": "fused atomic epilogue" if bufs.fused else "per-row outputs + moe_combine",
-                   "dispatch": "route + dispatch in one launch" if bufs.rd_ws is not None else "moe_route + moe_permute"},
+                   "dispatch": "route + dispatch in one launch" if bufs.rd_ws is not None else "moe_route + moe_permute",
+                   "weights": "packed 32x64 blocks (moe_pack_weights, once before timing)" if packed else "row-major"},
         "roofline": roof,
         "layer": {"ms_p50": round(float(np.median(layer_ms)), 4), "ms_p10": round(float(np.percentile(layer_ms, 10)), 4),
                   "ms_p90": round(float(np.percentile(layer_ms, 90)), 4),

@@ -132,6 +132,11 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
     return MOE_ERR_ALIGN;
   const unsigned only = flags & (MOE_FFN_ONLY_GATE_UP | MOE_FFN_ONLY_DOWN);
   if (only == (MOE_FFN_ONLY_GATE_UP | MOE_FFN_ONLY_DOWN)) return MOE_ERR_SHAPE;
+  if ((flags & ~(MOE_FFN_GATHER | MOE_FFN_ZERO_Y | MOE_FFN_ONLY_GATE_UP | MOE_FFN_ONLY_DOWN |
+                 MOE_FFN_PACKED_WEIGHTS)) != 0)
+    return MOE_ERR_SHAPE;
+  const bool packed = (flags & MOE_FFN_PACKED_WEIGHTS) != 0;
+  if (packed && w_dtype == MOE_F32) return MOE_ERR_DTYPE;
   hipStream_t s = (hipStream_t)stream;
   if (y && (flags & MOE_FFN_ZERO_Y) && only != MOE_FFN_ONLY_GATE_UP) {
     hipError_t err = launch_zero_f32(y, (size_t)T * H, s);
@@ -158,7 +163,20 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
   fa.y_perm = y_perm;
   fa.h = workspace;
   fa.phase = only == MOE_FFN_ONLY_GATE_UP ? 1 : (only == MOE_FFN_ONLY_DOWN ? 2 : 3);
+  fa.wpacked = packed;
   return hip_status(launch_ffn(fa, s));
+}
+
+int moe_pack_weights(const void *w, int w_dtype, int E, int N, int K, void *packed, void *stream) {
+  if (w_dtype != MOE_BF16 && w_dtype != MOE_FP8_E4M3) return MOE_ERR_DTYPE;
+  if (E < 1 || N < 32 || K < 64 || N % 32 != 0 || K % 64 != 0) return MOE_ERR_SHAPE;
+  if (!w || !packed) return MOE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(packed)) return MOE_ERR_ALIGN;
+  const int esz = w_dtype == MOE_BF16 ? 2 : 1;
+  const size_t bytes = (size_t)E * (size_t)N * (size_t)K * (size_t)esz;
+  const uintptr_t a0 = (uintptr_t)w, b0 = (uintptr_t)packed;
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return MOE_ERR_SHAPE;  // the two buffers overlap
+  return hip_status(launch_pack_weights(w, esz, E, N, K, packed, (hipStream_t)stream));
 }
 
 // Up to this many tokens the shared expert streams its weights (every token in one or two 64-row
@@ -183,7 +201,8 @@ int moe_shared_expert(const void *x, int x_dtype, int T, int H, int I_s, const v
   const bool bf16_path = x_dtype == MOE_BF16 && (w_dtype == MOE_BF16 || w_dtype == MOE_FP8_E4M3);
   const bool f32_path = x_dtype == MOE_F32 && w_dtype == MOE_F32;
   if (!bf16_path && !f32_path) return MOE_ERR_DTYPE;
-  if ((flags & ~MOE_FFN_ZERO_Y) != 0) return MOE_ERR_SHAPE;
+  if ((flags & ~(MOE_FFN_ZERO_Y | MOE_FFN_PACKED_WEIGHTS)) != 0) return MOE_ERR_SHAPE;
+  if ((flags & MOE_FFN_PACKED_WEIGHTS) && w_dtype == MOE_F32) return MOE_ERR_DTYPE;
   if (T == 0) return MOE_OK;
   if (!x || !w_gate_up || !w_down || !y) return MOE_ERR_NULL;
   if (w_dtype == MOE_FP8_E4M3 && (!s_gate_up || !s_down)) return MOE_ERR_NULL;
@@ -223,6 +242,7 @@ int moe_shared_expert(const void *x, int x_dtype, int T, int H, int I_s, const v
   fa.h = workspace;
   fa.phase = 3;
   fa.kernel = T <= SHARED_STREAM_ROWS ? 1 : 2;
+  fa.wpacked = (flags & MOE_FFN_PACKED_WEIGHTS) != 0;
   if (T <= SHARED_STREAM_ROWS && x_dtype == MOE_BF16) {
     // one expert gives only I_s / 128 gate/up workgroups per 64-row tile: split K over up to half
     // the 64-wide chunks so that about a thousand workgroups stream the weights
@@ -271,6 +291,7 @@ int moe_grouped_ffn_mx(const uint8_t *a_codes, const uint8_t *a_scales, const in
   if ((long long)R_cap > (long long)T * E_loc) return MOE_ERR_SHAPE;
   if ((long long)(T > R_cap ? T : R_cap) * (H > I ? H : I) >= (1LL << 30) || (long long)H * I >= (1LL << 30))
     return MOE_ERR_SHAPE;
+  if (flags & MOE_FFN_PACKED_WEIGHTS) return MOE_ERR_DTYPE;  // MX weights are row-major only
   if ((y == nullptr) == (y_perm == nullptr)) return MOE_ERR_NULL;
   const bool gather = (flags & MOE_FFN_GATHER) != 0;
   if (!a_codes || !a_scales || !offsets || !wgu_codes || !wgu_scales || !wd_codes || !wd_scales) return MOE_ERR_NULL;

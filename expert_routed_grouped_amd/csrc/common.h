@@ -98,11 +98,16 @@ struct FfnArgs {
   void *h;                // intermediate
   int phase;              // bit 0: gate/up half, bit 1: down half
   int kernel;             // bf16 / fp8 weights: 0 pick by rows per expert, 1 weight streaming, 2 tiles
+  int wpacked;            // both weight tensors in the packed block layout (moe_pack_weights)
   int ksplit;             // weight streaming only: split K over this many workgroups per tile (needs y and
   float *gu32;            // gu32, an fp32 [R_cap, 2I] scratch for the G and U partial sums)
 };
 
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t s);
+
+// Repack row-major weights [E, N, K] (esz-byte elements, N % 32 == 0, K % 64 == 0) into the
+// packed block layout read by the FFN kernels when FfnArgs::wpacked is set.
+hipError_t launch_pack_weights(const void *w, int esz, int E, int N, int K, void *packed, hipStream_t s);
 
 // MXFP8 quantisation of rows x K values (K % 32 == 0).
 hipError_t launch_quantize_mx(const void *x, int x_bf16, int rows, int K, uint8_t *codes, uint8_t *scales,

@@ -61,6 +61,7 @@ struct BigLoads {
   const char *bbase[BQ];                  // uniform per piece (bf16) / this expert's weights (fp8)
   uint32_t aoff[4];                       // per thread
   uint32_t boff[FP8 ? BQ : 1];            // per thread (bf16: one offset shared by every piece)
+  uint32_t bstep;                         // weight bytes from one K step to the next (row-major or packed)
 };
 
 template <bool FP8>
@@ -76,7 +77,7 @@ __device__ __forceinline__ void big_kloop(const BigLoads<FP8> &ld, int K, int ti
     for (int q = 0; q < 4; q++) ra[q] = *(const u32x4_t *)(a + ld.aoff[q]);
 #pragma unroll
     for (int q = 0; q < BQ; q++) {
-      const char *b = ld.bbase[q] + (size_t)k0 * (FP8 ? 1 : 2);
+      const char *b = ld.bbase[q] + (size_t)(k0 / BK) * ld.bstep;
       rb[q] = *(const u32x4_t *)(b + ld.boff[FP8 ? q : 0]);
     }
   };
@@ -176,13 +177,15 @@ __global__ __launch_bounds__(big::NTHR, 1) void ffn_big_kernel(TileParams p) {
       if constexpr (MODE == 0) wrow = ((rho >> 5) & 1) * p.I + min(nt * 128 + (rho >> 6) * 32 + (rho & 31), p.I - 1);
       else wrow = min(nt * BN + rho, p.H - 1);
       ld.bbase[q] = wexp;
-      ld.boff[q] = (uint32_t)wrow * (uint32_t)K + (uint32_t)(tid & 3) * 16u;
+      ld.boff[q] = (uint32_t)ffn::w_row_off(p.wpacked, (size_t)wrow, K, 1) + (uint32_t)(tid & 3) * 16u;
     }
+    ld.bstep = (uint32_t)ffn::w_chunk_step(p.wpacked, 1);
   } else {
     // piece q of thread tid is tile row (tid >> 3) + 64q, chunk tid & 7.  Gate/up: tile rows
     // [64q, 64q+64) are the gate then up rows of intermediate columns nt*128 + 32q + [0, 32);
     // down: weight rows nt*256 + 64q + [0, 64).  A piece group past the end re-reads group 0.
     const int t8 = tid >> 3;
+    ld.bstep = big::BK * 2;  // row-major only (bf16 weights take the direct-to-LDS kernel)
     if constexpr (MODE == 0) {
       ld.boff[0] = (uint32_t)((((t8 >> 5) & 1) * p.I + (t8 & 31)) * K) * 2u + (uint32_t)(tid & 7) * 16u;
 #pragma unroll
@@ -313,6 +316,34 @@ __global__ __launch_bounds__(64) void down_f32_kernel(const float *__restrict__ 
 
 }  // namespace
 
+namespace {
+
+// One thread moves one 16-byte piece of a weight row to its place in the packed layout.
+__global__ void pack_weights_kernel(const char *__restrict__ w, int esz, size_t rows, int K, char *__restrict__ out) {
+  const size_t per_row = (size_t)K * esz / 16;
+  const size_t n = rows * per_row;
+  for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < n; u += (size_t)gridDim.x * blockDim.x) {
+    const size_t row = u / per_row;
+    const int kb = (int)(u - row * per_row) * 16;  // byte offset inside the row-major row
+    const int k = kb / esz;
+    const size_t dst =
+        ffn::w_row_off(1, row, K, esz) + (size_t)(k >> 6) * ffn::w_chunk_step(1, esz) + (size_t)(kb % (64 * esz));
+    *(u32x4_t *)(out + dst) = *(const u32x4_t *)(w + row * (size_t)K * esz + kb);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_weights(const void *w, int esz, int E, int N, int K, void *packed, hipStream_t s) {
+  const size_t rows = (size_t)E * N;
+  const size_t n = rows * ((size_t)K * esz / 16);
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(blocks < 8192 ? (unsigned)blocks : 8192u), dim3(256), 0, s,
+                     (const char *)w, esz, rows, K, (char *)packed);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
   hipError_t err;
   if (a.R_cap == 0 || a.T == 0) return hipSuccess;
@@ -342,6 +373,7 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
     base.H = a.H;
     base.I = a.I;
     base.R_cap = a.R_cap;
+    base.wpacked = a.wpacked;
     return stream ? launch_ffn_stream(base, a, s) : launch_ffn_dma(base, a, s);
   }
   // worst-case M-tiles: sum_e ceil(c_e/BM) <= (R + El*(BM-1))/BM and <= El*ceil(T/BM)
@@ -359,6 +391,7 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
   tp.H = a.H;
   tp.I = a.I;
   tp.R_cap = a.R_cap;
+  tp.wpacked = a.wpacked;
   if (first) {
     tp.a = a.a;
     tp.w = a.w_gu;

@@ -16,7 +16,16 @@ struct TileParams {
   int R_cap;              // rows past R_cap are never touched, whatever the offsets say
   int ksplit;             // weight-streaming kernel: K slices per tile (0 or 1: none)
   float *gu32;            // with ksplit > 1: fp32 G and U partial sums [R_cap, 2I], zeroed beforehand
+  int wpacked;            // weights in 32-row x 64-k blocks (moe_pack_weights) instead of row-major
 };
+
+// Byte offset of weight row ``row`` (counted over all experts of the tensor) at k = 0, and the
+// byte step from one 64-wide K chunk to the next, for row-major or packed weights of esz bytes.
+// Packed: every 32 rows form K/64 consecutive blocks of 32 x 64 values, row-major inside.
+__device__ __forceinline__ size_t w_row_off(int packed, size_t row, int K, int esz) {
+  return packed ? ((row >> 5) * 32 * (size_t)K + (row & 31) * 64) * esz : row * (size_t)K * esz;
+}
+__device__ __forceinline__ size_t w_chunk_step(int packed, int esz) { return (size_t)(packed ? 32 * 64 : 64) * esz; }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll

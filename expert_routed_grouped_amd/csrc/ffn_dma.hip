@@ -49,6 +49,7 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 
 struct DmaSrc {
   uint32_t aoff[4], boff[4];  // byte offsets of this lane's A and B segments at K step 0
+  uint32_t bstep;             // bytes from one K step of the weights to the next (row-major or packed)
 };
 
 template <int NMB>
@@ -65,7 +66,7 @@ __device__ __forceinline__ void dma_kloop(const char *abase, const char *bbase, 
                                        (lds_void *)(lds + (kt & 1) * A_BYTES + (wave + 8 * u) * 1024), 16, 0, 0);
   };
   auto loadB = [&](int kt, int u) __attribute__((always_inline)) {
-    __builtin_amdgcn_global_load_lds((const void *)(bbase + (size_t)kt * BK * 2 + src.boff[u]),
+    __builtin_amdgcn_global_load_lds((const void *)(bbase + (size_t)kt * src.bstep + src.boff[u]),
                                      (lds_void *)(lds + 2 * A_BYTES + (kt % 3) * B_BYTES + (wave + 8 * u) * 1024), 16, 0,
                                      0);
   };
@@ -205,8 +206,9 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_dma_kernel(TileParams p) {
     int wrow;
     if constexpr (MODE == 0) wrow = ((row >> 5) & 1) * p.I + min(nt * 128 + (row >> 6) * 32 + (row & 31), p.I - 1);
     else wrow = min(nt * BN + row, p.H - 1);
-    src.boff[u] = (uint32_t)wrow * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
+    src.boff[u] = (uint32_t)ffn::w_row_off(p.wpacked, (size_t)wrow, K, 2) + (uint32_t)chunk * 16u;
   }
+  src.bstep = (uint32_t)ffn::w_chunk_step(p.wpacked, 2);
   const int arow0 = wm * half;
   const int rbase = r0 + arow0;
 #define DMA_BODY(n) dma_body<MODE, ATOMIC, n>(p, abase, bbase, src, nA, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)

@@ -75,12 +75,12 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
   // weight rows of this lane (k offset 32g inside every 64-wide chunk)
   const size_t wesz = FP8 ? 1 : 2;
   const char *wrow[NB];
-  if constexpr (MODE == 0) {
-    wrow[0] = (const char *)p.w + (((size_t)e * Nw + c0 + n) * K + 32 * g) * wesz;
-    wrow[1] = (const char *)p.w + (((size_t)e * Nw + p.I + c0 + n) * K + 32 * g) * wesz;
-  } else {
-    wrow[0] = (const char *)p.w + (((size_t)e * Nw + c0 + n) * K + 32 * g) * wesz;
-    wrow[1] = (const char *)p.w + (((size_t)e * Nw + c0 + 32 + n) * K + 32 * g) * wesz;
+  const size_t cstep = ffn::w_chunk_step(p.wpacked, (int)wesz);  // bytes from one 64-wide k chunk to the next
+  {
+    const size_t r0w = (size_t)e * Nw + c0 + n;                 // this lane's first weight row
+    const size_t r1w = MODE == 0 ? r0w + p.I : r0w + 32;        // up row / second down block
+    wrow[0] = (const char *)p.w + ffn::w_row_off(p.wpacked, r0w, K, (int)wesz) + 32 * g * wesz;
+    wrow[1] = (const char *)p.w + ffn::w_row_off(p.wpacked, r1w, K, (int)wesz) + 32 * g * wesz;
   }
   // activation rows (two 32-row blocks; rows past the end repeat the last valid row)
   const uint16_t *arow[SMB];
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
 #pragma unroll
     for (int b = 0; b < NB; b++)
 #pragma unroll
-      for (int q = 0; q < WQ; q++) wq[buf][b][q] = *(const u32x4_t *)(wrow[b] + (size_t)k0 * wesz + 16 * q);
+      for (int q = 0; q < WQ; q++) wq[buf][b][q] = *(const u32x4_t *)(wrow[b] + (size_t)(k0 >> 6) * cstep + 16 * q);
 #pragma unroll
     for (int q = 0; q < 4; q++) aq[buf][0][q] = *(const u32x4_t *)(arow[0] + k0 + 8 * q);
     if constexpr (SMB > 1) {
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
   const int kb = ks * (K / 64) / KS;
   const int KC = (ks + 1) * (K / 64) / KS - kb;
 #pragma unroll
-  for (int b = 0; b < NB; b++) wrow[b] += (size_t)kb * 64 * wesz;
+  for (int b = 0; b < NB; b++) wrow[b] += (size_t)kb * cstep;
 #pragma unroll
   for (int mb = 0; mb < SMB; mb++) arow[mb] += (size_t)kb * 64;
   if (KC > 0) load(0, 0);

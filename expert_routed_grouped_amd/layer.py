@@ -47,6 +47,19 @@ def to_device(inputs: dict, device="cuda") -> dict:
     return out
 
 
+def pack_weights(dev: dict) -> dict:
+    """Replace the bf16 / fp8 expert weights of ``dev`` (routed and shared) by copies in the packed
+    block layout (``moe_pack_weights``); later calls pass ``packed=True``.  fp32 weights stay
+    row-major.  Done once, outside any timed region, like loading the weights."""
+    if dev["cfg"].wdt not in ("bf16", "fp8") or dev.get("packed"):
+        return dev
+    for key in ("w_gate_up", "w_down", "ws_gate_up", "ws_down"):
+        if dev.get(key) is not None:
+            dev[key] = moe.moe_pack_weights(dev[key])
+    dev["packed"] = True
+    return dev
+
+
 class LayerBuffers:
     """Device buffers of one layer shape, reused across calls."""
 
@@ -80,6 +93,7 @@ def run_layer(dev: dict, bufs: LayerBuffers, stream=None) -> torch.Tensor:
     """route -> permute -> grouped FFN (-> combine) (-> shared expert).  Returns y [T,H] fp32."""
     cfg = bufs.cfg
     p = bufs.perm
+    packed = bool(dev.get("packed", False))
     if bufs.rd_ws is not None:  # one launch: route, dispatch and (fused combine) the zeroing of y
         moe.moe_route_dispatch(dev["x"], dev["w_router"], dev["bias"], cfg.k, cfg.E, cfg.lo, cfg.hi, bufs.rd_ws,
                                bufs.topk_ids, bufs.topk_w, p, y_zero=bufs.y if bufs.fused else None, stream=stream)
@@ -90,13 +104,13 @@ def run_layer(dev: dict, bufs: LayerBuffers, stream=None) -> torch.Tensor:
         moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
                             dev["w_gate_up"], dev["w_down"], dev.get("s_gate_up"), dev.get("s_down"),
                             y=bufs.y, workspace=bufs.workspace, gather=True, zero_y=bufs.rd_ws is None,
-                            stream=stream)
+                            packed=packed, stream=stream)
     else:
         moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
                             dev["w_gate_up"], dev["w_down"], dev.get("s_gate_up"), dev.get("s_down"),
-                            y_perm=bufs.y_perm, workspace=bufs.workspace, gather=True, stream=stream)
+                            y_perm=bufs.y_perm, workspace=bufs.workspace, gather=True, packed=packed, stream=stream)
         moe.moe_combine(bufs.y_perm, p["token_row"], bufs.topk_w, y=bufs.y, stream=stream)
     if bufs.shared_ws is not None:
         moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], bufs.y, dev.get("ss_gate_up"),
-                              dev.get("ss_down"), workspace=bufs.shared_ws, stream=stream)
+                              dev.get("ss_down"), workspace=bufs.shared_ws, packed=packed, stream=stream)
     return bufs.y

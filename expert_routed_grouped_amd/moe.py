@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP8 = 0, 1, 2, 3
 MOE_FFN_GATHER, MOE_FFN_ZERO_Y, MOE_FFN_ONLY_GATE_UP, MOE_FFN_ONLY_DOWN = 1, 2, 4, 8
+MOE_FFN_PACKED_WEIGHTS = 16
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE", -4: "MOE_ERR_WORKSPACE",
           -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIGN"}
 
@@ -25,7 +26,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTY
 EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_permute_workspace_size",
            "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_quantize_mx", "moe_ffn_mx_workspace_size",
            "moe_grouped_ffn_mx", "moe_shared_workspace_size", "moe_shared_expert", "moe_route_dispatch_workspace_size",
-           "moe_route_dispatch")
+           "moe_route_dispatch", "moe_pack_weights")
 
 
 class MoEError(RuntimeError):
@@ -75,6 +76,8 @@ def lib():
         L.moe_route_dispatch_workspace_size.argtypes = []
         L.moe_route_dispatch.restype = I
         L.moe_route_dispatch.argtypes = [P, I, P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
+        L.moe_pack_weights.restype = I
+        L.moe_pack_weights.argtypes = [P, I, I, I, I, P, P]
         _lib = L
     return _lib
 
@@ -176,10 +179,11 @@ def moe_grouped_ffn(a: torch.Tensor, offsets: torch.Tensor, row_token: torch.Ten
                     s_gate_up: Optional[torch.Tensor] = None, s_down: Optional[torch.Tensor] = None,
                     y: Optional[torch.Tensor] = None, y_perm: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, gather: bool = True, zero_y: bool = True,
-                    phase: str = "both", stream=None):
+                    phase: str = "both", packed: bool = False, stream=None):
     """SwiGLU expert FFN over the grouped rows.  With ``y`` the gate-weighted combine is
     fused (y accumulates; zeroed first when ``zero_y``); otherwise writes ``y_perm``.
-    ``phase``: "both", "gate_up" or "down" (the two halves, same arguments and workspace)."""
+    ``phase``: "both", "gate_up" or "down" (the two halves, same arguments and workspace).
+    ``packed``: both weight tensors come from moe_pack_weights."""
     El, twoI, H = w_gate_up.shape
     I = twoI // 2
     adt = _dtype(a)
@@ -188,6 +192,7 @@ def moe_grouped_ffn(a: torch.Tensor, offsets: torch.Tensor, row_token: torch.Ten
         workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
     flags = (MOE_FFN_GATHER if gather else 0) | (MOE_FFN_ZERO_Y if zero_y else 0)
     flags |= {"both": 0, "gate_up": MOE_FFN_ONLY_GATE_UP, "down": MOE_FFN_ONLY_DOWN}[phase]
+    flags |= MOE_FFN_PACKED_WEIGHTS if packed else 0
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(
         _ptr(a), adt, _ptr(offsets), _ptr(row_token), _ptr(row_w), El, T, R_cap, H, I, _ptr(w_gate_up),
         _ptr(w_down), _dtype(w_gate_up), _ptr(s_gate_up), _ptr(s_down), _ptr(y), _ptr(y_perm), _ptr(workspace),
@@ -249,8 +254,10 @@ def moe_shared_workspace_size(T: int, I_s: int, x_dtype: int) -> int:
 
 def moe_shared_expert(x: torch.Tensor, w_gate_up: torch.Tensor, w_down: torch.Tensor, y: torch.Tensor,
                       s_gate_up: Optional[torch.Tensor] = None, s_down: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None, zero_y: bool = False, stream=None):
-    """y += shared-expert SwiGLU FFN of x (every token, weight 1); ``zero_y`` zeroes y first."""
+                      workspace: Optional[torch.Tensor] = None, zero_y: bool = False, packed: bool = False,
+                      stream=None):
+    """y += shared-expert SwiGLU FFN of x (every token, weight 1); ``zero_y`` zeroes y first;
+    ``packed``: both weight tensors come from moe_pack_weights."""
     T, H = x.shape
     I_s = w_gate_up.shape[0] // 2
     xdt = _dtype(x)
@@ -259,9 +266,21 @@ def moe_shared_expert(x: torch.Tensor, w_gate_up: torch.Tensor, w_down: torch.Te
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     _check("moe_shared_expert", lib().moe_shared_expert(
         _ptr(x), xdt, T, H, I_s, _ptr(w_gate_up), _ptr(w_down), _dtype(w_gate_up), _ptr(s_gate_up), _ptr(s_down),
-        _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(), MOE_FFN_ZERO_Y if zero_y else 0,
-        _stream(stream)))
+        _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        (MOE_FFN_ZERO_Y if zero_y else 0) | (MOE_FFN_PACKED_WEIGHTS if packed else 0), _stream(stream)))
     return y
+
+
+def moe_pack_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Weights [E, N, K] (or [N, K], one expert) in the packed block layout, as a tensor of the
+    same shape and dtype (pass it with ``packed=True``)."""
+    E, N, K = (1, *w.shape) if w.dim() == 2 else w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    if out.shape != w.shape or out.dtype != w.dtype:
+        raise ValueError("out must have the shape and dtype of w")
+    _check("moe_pack_weights", lib().moe_pack_weights(_ptr(w), _dtype(w), E, N, K, _ptr(out), _stream(stream)))
+    return out
 
 
 def moe_route_dispatch_workspace(device="cuda") -> torch.Tensor:

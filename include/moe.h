@@ -11,8 +11,9 @@
  *   moe_combine      gate-weighted gather-sum of per-row outputs to token order
  *
  * plus moe_route_dispatch (the first two calls of a decode batch in one
- * launch), moe_shared_expert (an always-active expert added to y) and the W8A8
- * MXFP8 variant of the expert FFN (moe_quantize_mx, moe_grouped_ffn_mx).
+ * launch), moe_shared_expert (an always-active expert added to y), the W8A8
+ * MXFP8 variant of the expert FFN (moe_quantize_mx, moe_grouped_ffn_mx) and
+ * moe_pack_weights (a one-time reordering of resident weights for faster reads).
  *
  * The method follows three pages: "AI-infra book, ch. 9 Distributed inference"
  * (section 9.3.4, Fig. 9-16: route, group rows by expert, expert GEMMs, weighted
@@ -82,6 +83,8 @@ extern "C" {
 #define MOE_FFN_ONLY_GATE_UP 4u /* run only the first half: gate/up + SwiGLU into the workspace's h */
 #define MOE_FFN_ONLY_DOWN 8u    /* run only the second half: down + combine from the workspace's h, which a
                                    preceding MOE_FFN_ONLY_GATE_UP call with the same arguments filled */
+#define MOE_FFN_PACKED_WEIGHTS 16u /* w_gate_up and w_down are in the packed block layout that
+                                      moe_pack_weights writes (bf16 and fp8 weights only) */
 
 /* Library version (major*10000 + minor*100 + patch). */
 int moe_version(void);
@@ -189,7 +192,10 @@ size_t moe_ffn_workspace_size(int R_cap, int E_loc, int H, int I, int a_dtype);
  * MOE_FFN_ONLY_GATE_UP / MOE_FFN_ONLY_DOWN split the call into its two halves
  * (same arguments, same workspace, same stream, in that order), e.g. to place
  * other work between them; setting both is MOE_ERR_SHAPE.  MOE_FFN_ZERO_Y is
- * honoured by the call that runs the down half.
+ * honoured by the call that runs the down half.  MOE_FFN_PACKED_WEIGHTS: both
+ * weight tensors come from moe_pack_weights (MOE_ERR_DTYPE with fp32 weights);
+ * the results are bit-identical to those with row-major weights.  An unknown
+ * flag bit is MOE_ERR_SHAPE.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE,
  * MOE_ERR_ALIGN, MOE_ERR_HIP.  R_cap == 0 or T == 0 only zeroes y (if asked).
  */
@@ -198,6 +204,33 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
                     const void *w_gate_up, const void *w_down, int w_dtype,
                     const float *s_gate_up, const float *s_down, float *y, float *y_perm,
                     void *workspace, size_t workspace_bytes, unsigned flags, void *stream);
+
+/*
+ * moe_pack_weights - copy expert weights into the packed block layout.
+ *
+ * Same values, another order in memory; it changes no result.  The
+ * expert-parallel layer keeps every local expert's weights resident and reads
+ * them all once per call (section "Expert Parallelism" of "Hosting Qwen on
+ * Blackwell"; the weight bytes that section 9.3.2 of the AI-infra book counts
+ * per expert); the layout only makes that read more sequential: a workgroup
+ * that streams 32 weight rows reads one contiguous 32 x 64-value block per
+ * 64-wide step of the contraction instead of 32 rows far apart.
+ *
+ * w: [E, N, K] row-major, MOE_BF16 or MOE_FP8_E4M3 (w_dtype); packed: the same
+ * number of bytes, written as, for every group of 32 rows (row = e*N + n over
+ * all experts) and every 64-wide K chunk c, the 32 x 64 block of those rows and
+ * columns [64c, 64c+64), row-major, with the blocks of a row group in order of
+ * c and the row groups in order.  Element (row, k) is at
+ *   ((row / 32) * 32 * K + (row % 32) * 64 + (k / 64) * 2048 + k % 64).
+ * Pass the packed w_gate_up ([E_loc, 2I, H]: N = 2I, K = H) and w_down
+ * ([E_loc, H, I]: N = H, K = I) to moe_grouped_ffn or moe_shared_expert (E = 1)
+ * with MOE_FFN_PACKED_WEIGHTS; fp8 scales stay as they are.  N a multiple of 32,
+ * K of 64; both pointers 16-byte aligned, the buffers must not overlap (the
+ * call does not pack in place).  Runs asynchronously on ``stream``.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (also for overlapping buffers),
+ * MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_pack_weights(const void *w, int w_dtype, int E, int N, int K, void *packed, void *stream);
 
 /*
  * moe_quantize_mx - MXFP8 quantisation of a row-major matrix along its rows.
@@ -235,11 +268,12 @@ size_t moe_ffn_mx_workspace_size(int R_cap, int I);
  * exact E4M3 products times their two block scales in fp32 on the fp8 matrix
  * cores; h_r = silu(G) * U in fp32 is quantised per row with the rule of
  * moe_quantize_mx (blocks of 32 along I) into the workspace before the down
- * projection.  Outputs, flags and the combine are those of moe_grouped_ffn.
+ * projection.  Outputs, flags and the combine are those of moe_grouped_ffn
+ * (MX weights are row-major only: MOE_FFN_PACKED_WEIGHTS is MOE_ERR_DTYPE).
  * H and I must be multiples of 128; pointers 16-byte aligned (scale arrays
  * 4-byte aligned); workspace at least moe_ffn_mx_workspace_size(R_cap, I)
  * bytes, 256-byte aligned.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE,
- * MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ * MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP.
  */
 int moe_grouped_ffn_mx(const uint8_t *a_codes, const uint8_t *a_scales, const int32_t *offsets,
                        const int32_t *row_token, const float *row_w, int E_loc, int T, int R_cap, int H, int I,
@@ -316,7 +350,9 @@ size_t moe_shared_workspace_size(int T, int I_s, int x_dtype);
  * (s_gate_up [2*I_s], s_down [H]) as in moe_grouped_ffn, and h rounded to bf16
  * for bf16 activations.  y [T,H] fp32 accumulates: call it after
  * moe_grouped_ffn's fused combine or moe_combine on the same stream, or pass
- * MOE_FFN_ZERO_Y (the only flag) for the shared expert alone.  For T > 128
+ * MOE_FFN_ZERO_Y for the shared expert alone; MOE_FFN_PACKED_WEIGHTS (bf16 and
+ * fp8 weights) reads weights packed by moe_pack_weights with E = 1; any other
+ * flag bit is MOE_ERR_SHAPE.  For T > 128
  * each element of y receives one fp32 add; for T <= 128 (bf16 activations)
  * the contraction is split over many workgroups to keep HBM busy, so G, U and
  * y receive several fp32 adds of partial sums in no fixed order (run-to-run

@@ -88,7 +88,7 @@ def ffn(**kw):
     (dict(ad=0), -3), (dict(wdt=0), -3), (dict(ad=2, wdt=2), -3),
     (dict(y=None), -1), (dict(yp=FAKE), -1), (dict(wdt=2), -1), (dict(rt=None), -1), (dict(rw=None), -1),
     (dict(ws=None), -4), (dict(wsb=10), -4), (dict(a=FAKE_ODD), -6), (dict(ws=P(0x1010)), -6),
-    (dict(T=1 << 20, R=1 << 20, H=1024), -2),
+    (dict(T=1 << 20, R=1 << 20, H=1024), -2), (dict(flags=3 | 32), -2), (dict(ad=0, wdt=0, flags=3 | 16), -3),
 ])
 def test_ffn_validation(kw, code):
     assert ffn(**kw) == code
@@ -107,7 +107,7 @@ def ffn_mx(**kw):
     (dict(H=192), -2), (dict(I=64), -2), (dict(El=0), -2), (dict(R=16 * 8 + 1), -2), (dict(T=1 << 20, R=1 << 20, H=1024), -2),
     (dict(y=None), -1), (dict(yp=FAKE), -1), (dict(as_=None), -1), (dict(wds=None), -1), (dict(rt=None), -1),
     (dict(ws=None), -4), (dict(wsb=10), -4), (dict(a=FAKE_ODD), -6), (dict(as_=P(0x1002)), -6),
-    (dict(ws=P(0x1010)), -6), (dict(flags=3 | 4 | 8), -2),
+    (dict(ws=P(0x1010)), -6), (dict(flags=3 | 4 | 8), -2), (dict(flags=3 | 16), -3),
 ])
 def test_ffn_mx_validation(kw, code):
     assert ffn_mx(**kw) == code
@@ -132,10 +132,23 @@ def shared(x=FAKE, xd=1, T=8, H=64, I_s=64, wgu=FAKE, wd=FAKE, wdt=1, sgu=None, 
     (dict(H=96), -2), (dict(I_s=32), -2), (dict(T=-1), -2), (dict(T=1 << 20, H=2048), -2), (dict(flags=1), -2),
     (dict(xd=0), -3), (dict(wdt=3), -3), (dict(x=None), -1), (dict(y=None), -1), (dict(wd=None), -1),
     (dict(wdt=2), -1), (dict(ws=None), -4), (dict(wsb=64), -4), (dict(y=FAKE_ODD), -6), (dict(T=0), 0),
+    (dict(flags=16 | 1), -2), (dict(flags=32), -2), (dict(xd=0, wdt=0, flags=16), -3), (dict(T=0, flags=16 | 2), 0),
 ])
 def test_shared_expert_validation(kw, code):
     # every case is rejected (or is empty) on the host before anything is launched
     assert shared(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=0), -3), (dict(dt=3), -3), (dict(E=0), -2), (dict(N=48), -2), (dict(N=0), -2), (dict(K=96), -2),
+    (dict(K=32), -2), (dict(w=None), -1), (dict(out=None), -1), (dict(w=FAKE_ODD), -6), (dict(out=P(0x9008)), -6),
+    (dict(out=P(0x1000 + 4096 - 16)), -2), (dict(out=FAKE), -2), (dict(w=P(0x1000 + 2048), out=FAKE, dt=2, K=128), -2),
+])
+def test_pack_weights_validation(kw, code):
+    # every case is rejected on the host before anything is launched (the last three overlap)
+    a = dict(w=FAKE, dt=1, E=1, N=32, K=64, out=P(0x9000))
+    a.update(kw)
+    assert moe.lib().moe_pack_weights(a["w"], a["dt"], a["E"], a["N"], a["K"], a["out"], None) == code
 
 
 def route_dispatch(x=FAKE, xd=1, w=FAKE, wd=1, T=64, H=256, E=16, k=4, lo=0, hi=16, ids=FAKE, g=FAKE, c=FAKE,

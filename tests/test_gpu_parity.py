@@ -382,14 +382,20 @@ def sample_tokens(cfg, ids, n=24):
     return np.array(sorted(pick), dtype=np.int32)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "ep_share", "decode_shared", "prefill_shared"])
-def test_full_workload_layer(name):
+FULL_CASES = [(n, False) for n in ["decode", "prefill", "skew", "ep_share", "decode_shared", "prefill_shared"]]
+FULL_CASES += [(n, True) for n in ["decode", "prefill", "ep_share", "decode_shared"]]
+
+
+@pytest.mark.parametrize("name,packed", FULL_CASES, ids=[f"{n}{'_packed' if p else ''}" for n, p in FULL_CASES])
+def test_full_workload_layer(name, packed):
     cfg = CONFIGS[name]
     inp = host_inputs(cfg)
     say(f"full layer {name}: generating / uploading")
     dev = L.to_device(inp)
+    if packed:
+        L.pack_weights(dev)
     bufs = L.LayerBuffers(cfg)
-    say(f"full layer {name}: run_layer fused={bufs.fused} R_cap={bufs.R_cap}")
+    say(f"full layer {name}: run_layer fused={bufs.fused} R_cap={bufs.R_cap} packed={packed}")
     y = L.run_layer(dev, bufs)
     torch.cuda.synchronize()
     ids, w = oracle_routing(cfg)
@@ -726,3 +732,103 @@ def test_full_workload_layer_mx():
     y, p, h = mx_layer(dev, cfg, ids_d, w_d, fused=False)
     assert len(used) > 0
     check_mx_layer(cfg, inp, ids, w, y, h, tokens=toks)
+
+
+# ----------------------------------------------------------------------------
+# packed weight layout: the reorder itself, and bit-identical FFN outputs
+# ----------------------------------------------------------------------------
+def np_packed(w):
+    """The packed block layout written with numpy: 32-row groups, 64-wide K chunks, row-major blocks."""
+    E, N, K = w.shape
+    return np.ascontiguousarray(w.reshape(E * N // 32, 32, K // 64, 64).transpose(0, 2, 1, 3)).reshape(E, N, K)
+
+
+@pytest.mark.parametrize("dt,shape", [("bf16", (3, 96, 192)), ("fp8", (2, 64, 320)), ("bf16", (64, 128)),
+                                      ("fp8", (5, 32, 64))])
+def test_pack_weights_layout(dt, shape):
+    rng = np.random.default_rng(501)
+    if dt == "bf16":
+        w = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+        wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        w = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        wd = torch.from_numpy(w).cuda()
+    out = moe.moe_pack_weights(wd)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else out.cpu().numpy()
+    ref = np_packed(w.reshape((1,) + shape if len(shape) == 2 else shape)).reshape(shape)
+    assert np.array_equal(got, ref)
+    src = wd.cpu().view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else wd.cpu().numpy()
+    assert np.array_equal(src, w)  # the source is left as it was
+
+
+def ffn_rows(dev, cfg, ids_d, w_d, packed):
+    """Per-row outputs y_perm (one plain store per element: deterministic) of the grouped FFN."""
+    p = moe.moe_permute(ids_d, w_d, cfg.E, cfg.lo, cfg.hi)
+    yp = torch.full((max(p["R_cap"], 1), cfg.H), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, p["R_cap"], dev["w_gate_up"],
+                        dev["w_down"], dev["s_gate_up"], dev["s_down"], y_perm=yp, packed=packed)
+    torch.cuda.synchronize()
+    return yp, p
+
+
+PACKED_CASES = ["stream_bf16", "stream_fp8_local", "stream_hot", "ffn_bf16", "ffn_fp8_local", "ffn_skew_empty",
+                "tiles_fp8"]
+
+
+@pytest.mark.parametrize("name", PACKED_CASES)
+def test_ffn_packed_weights_bit_identical(name):
+    """Weight streaming (bf16, fp8), direct-to-LDS tiles (bf16) and register-staged tiles (fp8)
+    read packed weights to the same bits as row-major ones; the fused combine matches the oracle."""
+    if name == "tiles_fp8":
+        cfg = LayerConfig("tiles_fp8", T=1000, H=320, E=len(TILE_COUNTS), k=5, I=192, wdt="fp8", seed=210,
+                          w_std=0.05)
+        ids, w = constructed_routing(TILE_COUNTS, cfg.T, cfg.k, seed=211)
+    else:
+        cfg = next(c for c in FFN_CASES if c.name == name)
+        ids, w = oracle_routing(cfg)
+    inp = host_inputs(cfg)
+    dev = L.to_device(inp)
+    ids_d, w_d = to_dev_routing(ids, w)
+    say(f"packed weights {name}: T={cfg.T} H={cfg.H} E_loc={cfg.E_loc} I={cfg.I} {cfg.wdt}")
+    y_row, p = ffn_rows(dev, cfg, ids_d, w_d, packed=False)
+    L.pack_weights(dev)
+    y_pk, _ = ffn_rows(dev, cfg, ids_d, w_d, packed=True)
+    R = int(p["offsets"][-1])  # rows of local assignments (rows past them up to R_cap stay unwritten)
+    assert R > 0 and torch.equal(y_pk[:R], y_row[:R])
+    y, _ = gpu_layer_packed(dev, cfg, ids_d, w_d)
+    y_o = O.layer_tokens(np.arange(cfg.T), inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"],
+                         inp["s_gate_up"], inp["s_down"], round_h=True)
+    check_y(y, y_o, name + " packed fused")
+
+
+def gpu_layer_packed(dev, cfg, ids_d, w_d):
+    p = moe.moe_permute(ids_d, w_d, cfg.E, cfg.lo, cfg.hi)
+    y = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, p["R_cap"], dev["w_gate_up"],
+                        dev["w_down"], dev["s_gate_up"], dev["s_down"], y=y, zero_y=True, packed=True)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), p
+
+
+@pytest.mark.parametrize("cfg", [SHARED_CASES[0], SHARED_CASES[2], SHARED_CASES[3], SHARED_CASES[4], SHARED_CASES[6]],
+                         ids=lambda c: c.name)
+def test_shared_expert_packed_weights(cfg):
+    """Packed shared-expert weights: the same bits where every element of y gets one add (T > 128),
+    the oracle's result within tolerance on the split-K path."""
+    inp = host_inputs(cfg)
+    dev = L.to_device(inp)
+    say(f"shared expert packed {cfg.name}: T={cfg.T} H={cfg.H} I_s={cfg.I_s} {cfg.wdt}")
+    y_row = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+    moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], y_row, dev["ss_gate_up"], dev["ss_down"],
+                          zero_y=True)
+    L.pack_weights(dev)
+    y_pk = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], y_pk, dev["ss_gate_up"], dev["ss_down"],
+                          zero_y=True, packed=True)
+    torch.cuda.synchronize()
+    if cfg.T > 128:
+        assert torch.equal(y_pk, y_row)
+    y_o = O.shared_tokens(np.arange(cfg.T), inp["x"], inp["ws_gate_up"], inp["ws_down"], inp["ss_gate_up"],
+                          inp["ss_down"], round_h=True)
+    check_y(y_pk.cpu().numpy(), y_o, cfg.name + " packed")
