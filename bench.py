@@ -37,6 +37,7 @@ WORKLOADS = {
     "skew": "skewed prefill MoE layer: T=6000, top-8 of 128, logit bias 2*ln Zipf(1.2), H=4096, I=1536, bf16",
     "ep_share": "EP=4 share: T=8192 routed over 128 experts, local experts 0-31, fp8 e4m3 weights, H=4096, I=1536",
     "prefill_mx": "W8A8 MXFP8 prefill MoE layer: T=6000 tokens x top-8 of E=128 experts, H=4096, SwiGLU I=1536",
+    "decode_mx": "W8A8 MXFP8 decode MoE layer: T=64 tokens x top-8 of E=128 experts, H=4096, SwiGLU I=1536",
     "decode_shared": "decode MoE layer (T=64, top-8 of 128, H=4096, I=1536, bf16) plus one shared expert (I_s=1536)",
     "prefill_shared": "prefill MoE layer (T=6000, top-8 of 128, H=4096, I=1536, bf16) plus one shared expert "
                       "(I_s=1536)",
@@ -287,12 +288,14 @@ def main():
         peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None}
-    kernel = ("ffn_mx_kernel" if mx else
-              ("ffn_stream_kernel" if bufs.R_cap <= 48 * cfg.E_loc else
+    streaming = bufs.R_cap <= 48 * cfg.E_loc
+    kernel = (("ffn_mx_stream_kernel" if streaming else "ffn_mx_kernel") if mx else
+              ("ffn_stream_kernel" if streaming else
                ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel")))
     roof["traffic"] = measured_traffic(kernel, args.config, "packed" if packed else "row-major")
     # rows the grouped GEMM actually multiplies, by the tiling of the kernel in use
     padded = (A.padded_rows(counts, 64) if kernel == "ffn_stream_kernel" else
+              A.padded_rows(counts, 32 if bufs.R_cap <= 16 * cfg.E_loc else 64) if kernel == "ffn_mx_stream_kernel" else
               (A.split_padded_rows(counts, 256, 64) if kernel == "ffn_dma_kernel" else
                (A.split_padded_rows(counts, 192, 64) if kernel == "ffn_mx_kernel" else A.padded_rows(counts, 256))))
     roof.update({"kernel": f"{kernel} (gate/up + SwiGLU half, one launch)", "avg_ms": round(float(np.mean(gu_ms)), 4),

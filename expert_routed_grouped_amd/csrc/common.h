@@ -127,6 +127,9 @@ struct FfnMxArgs {
   float *y, *y_perm;
   void *ws;
   int phase;                   // bit 0: gate/up half, bit 1: down half
+  int kernel;                  // 0 pick by rows per expert, 1 weight streaming, 2 tiles
 };
 size_t ffn_mx_h_bytes(int R_cap, int I);
 hipError_t launch_ffn_mx(const FfnMxArgs &a, hipStream_t s);
+// Weight-streaming W8A8 path for small batches (ffn_mx_stream.hip).
+hipError_t launch_ffn_mx_stream(const FfnMxArgs &a, hipStream_t s);

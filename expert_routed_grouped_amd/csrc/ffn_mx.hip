@@ -283,6 +283,8 @@ size_t ffn_mx_h_bytes(int R_cap, int I) { return align_up((size_t)R_cap * (size_
 
 hipError_t launch_ffn_mx(const FfnMxArgs &a, hipStream_t s) {
   if (a.R_cap == 0 || a.T == 0) return hipSuccess;
+  // few rows per expert on average: stream the weights (HBM bound), as for bf16 weights
+  if (a.kernel == 1 || (a.kernel == 0 && (long long)a.R_cap <= 48LL * a.El)) return launch_ffn_mx_stream(a, s);
   hipError_t err = hipSuccess;
   const long long mt1 = ((long long)a.R_cap + (long long)a.El * (BM - 1)) / BM;
   const long long mt2 = (long long)a.El * ceil_div_i(a.T, BM);

@@ -96,6 +96,7 @@ CONFIGS = {
     "ep_share": LayerConfig("ep_share", T=8192, H=4096, E=128, k=8, I=1536, wdt="fp8", e_begin=0, e_end=32, seed=5),
     # W8A8 MXFP8 variant of the prefill layer (weights converted offline, activations on the fly)
     "prefill_mx": LayerConfig("prefill_mx", T=6000, H=4096, E=128, k=8, I=1536, wdt="mxfp8", seed=6),
+    "decode_mx": LayerConfig("decode_mx", T=64, H=4096, E=128, k=8, I=1536, wdt="mxfp8", seed=9),
     # the decode and prefill layers with one always-active shared expert of a routed expert's shape
     "decode_shared": LayerConfig("decode_shared", T=64, H=4096, E=128, k=8, I=1536, seed=7, I_s=1536),
     "prefill_shared": LayerConfig("prefill_shared", T=6000, H=4096, E=128, k=8, I=1536, seed=8, I_s=1536),

@@ -692,6 +692,14 @@ MX_CASES = [
     # several M and N tiles with ragged expert counts; N tail of the down projection (H % 256 == 128)
     LayerConfig("mx_small", T=700, H=384, E=6, k=3, I=256, wdt="mxfp8", seed=302, w_std=0.05),
     LayerConfig("mx_local", T=500, H=256, E=8, k=2, I=384, wdt="mxfp8", e_begin=2, e_end=6, seed=303, w_std=0.05),
+    # few rows per expert: the weight-streaming kernel with 32-row tiles (down N tail: H % 256 == 128),
+    # with 64-row tiles (more than 16 rows per local expert on average), one hot expert over many tiles
+    LayerConfig("mx_stream", T=64, H=384, E=16, k=4, I=256, wdt="mxfp8", seed=306, w_std=0.05),
+    LayerConfig("mx_stream_local", T=48, H=512, E=16, k=4, I=384, wdt="mxfp8", e_begin=4, e_end=12, seed=307,
+                w_std=0.05),
+    # K a multiple of 512 in both halves: scales read four K steps at a time
+    LayerConfig("mx_stream_s4", T=64, H=512, E=16, k=4, I=512, wdt="mxfp8", seed=309, w_std=0.05),
+    LayerConfig("mx_stream_hot", T=120, H=256, E=16, k=2, I=256, wdt="mxfp8", bias="zipf", seed=308, w_std=0.05),
 ]
 
 
@@ -720,8 +728,9 @@ def test_layer_mx_tile_boundaries(fused):
     check_mx_layer(cfg, inp, ids, w, y, h)
 
 
-def test_full_workload_layer_mx():
-    cfg = CONFIGS["prefill_mx"]
+@pytest.mark.parametrize("name,fused", [("prefill_mx", False), ("decode_mx", True), ("decode_mx", False)])
+def test_full_workload_layer_mx(name, fused):
+    cfg = CONFIGS[name]
     ids, w = oracle_routing(cfg)
     toks = sample_tokens(cfg, ids)
     used = sorted(set(int(e) for e in ids[toks].ravel()))
@@ -729,7 +738,7 @@ def test_full_workload_layer_mx():
     dev = mx_dev(inp)
     say(f"full MX layer {cfg.name}: T={cfg.T}, sampled tokens {toks.tolist()}")
     ids_d, w_d = to_dev_routing(ids, w)
-    y, p, h = mx_layer(dev, cfg, ids_d, w_d, fused=False)
+    y, p, h = mx_layer(dev, cfg, ids_d, w_d, fused=fused)
     assert len(used) > 0
     check_mx_layer(cfg, inp, ids, w, y, h, tokens=toks)
 
