@@ -118,7 +118,7 @@ __device__ __forceinline__ void route_tokens(const void *__restrict__ x, const v
     // its own expert row, so only prefetch depth hides the L2 latency)
     // fp32 weights take twice the registers per step: half the ring depth
     constexpr int HS = 32, P = HS * (WB ? 2 : 4) / 16, NS = WB ? ROUTE_NS : ROUTE_NS / 2;
-    const int nsteps = H / HS;
+    const int nsteps = H / (HS * NS) * NS;  // whole rounds of the ring; the rest runs below
     u32x4_t ring[NS][P];
     auto wload = [&](u32x4_t(&b)[P], int st) __attribute__((always_inline)) {
 #pragma unroll
@@ -149,15 +149,23 @@ __device__ __forceinline__ void route_tokens(const void *__restrict__ x, const v
         }
       }
     };
+    // The ring runs whole rounds with unconditional loads (steps past the end re-read the last
+    // step, which is in bounds) and no exit inside a round, and a compiler barrier keeps every
+    // load where it is issued: the number of loads issued after any slot is then fixed, so the
+    // wait before a step covers only that step's slot.  A conditional load or an early exit makes
+    // the compiler wait for every load in flight, and without the barrier it moves the loads next
+    // to their use; either way a step then costs one memory round trip.
+    if (nsteps > 0) {
 #pragma unroll
-    for (int q = 0; q < NS - 1; q++)
-      if (q < nsteps) wload(ring[q], q);
+      for (int q = 0; q < NS - 1; q++) wload(ring[q], q);
+      asm volatile("" ::: "memory");
+    }
     for (int st0 = 0; st0 < nsteps; st0 += NS) {
 #pragma unroll
       for (int q = 0; q < NS; q++) {
         const int st = st0 + q;
-        if (st >= nsteps) break;
-        if (st + NS - 1 < nsteps) wload(ring[(q + NS - 1) % NS], st + NS - 1);
+        wload(ring[(q + NS - 1) % NS], min(st + NS - 1, nsteps - 1));
+        asm volatile("" ::: "memory");
         wstep(ring[q], st);
       }
     }

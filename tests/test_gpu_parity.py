@@ -430,6 +430,8 @@ RD_CASES = [
     LayerConfig("rd_e40_local", T=77, H=128, E=40, k=3, I=64, e_begin=5, e_end=30, seed=504),  # one wave
     LayerConfig("rd_f32", T=33, H=64, E=8, k=2, I=64, act="f32", wdt="f32", init="fan_in", seed=505),
     LayerConfig("rd_zipf", T=200, H=256, E=64, k=8, I=64, bias="zipf", seed=506, w_std=0.05),
+    # ragged: H = 264 leaves 8 h after the whole rounds of the router's load ring; E, T odd sizes
+    LayerConfig("rd_ragged", T=70, H=264, E=21, k=5, I=64, seed=507, w_std=0.05),
 ]
 
 
