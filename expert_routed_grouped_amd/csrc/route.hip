@@ -5,9 +5,9 @@
 // fused-multiply-add chain over h in ascending order; this fixed order is the
 // library's contract, so the chain is computed as is: one lane owns one expert
 // and walks h upward, the token's activations are wave-uniform and come in
-// through scalar loads.  Top-k is k rounds of a wave-wide max over 64-bit keys
-// (orderable logit bits, inverted expert id), so equal logits go to the lower
-// expert index; the gates are a softmax over the k selected logits.
+// through scalar loads.  Top-k is k rounds of a wave-wide max (DPP) over 64-bit
+// keys (orderable logit bits, inverted expert id), so equal logits go to the
+// lower expert index; the gates are a softmax over the k selected logits.
 #include "permute_dev.h"
 
 namespace {
@@ -23,21 +23,46 @@ __device__ __forceinline__ float ord_val(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// Wave-wide reductions on DPP (data-parallel primitives: a VALU operand taken from another lane
+// of the same row of 16, or broadcast from the last lane of the previous row or pair of rows).
+// Row shifts by 1, 2, 4 and 8 leave in lane 15 of every row the reduction of that row; the row
+// broadcasts of lanes 15 and 31 then carry it across rows, so lane 63 holds the reduction of the
+// whole wave, which readlane makes wave-uniform.  A lane a shift leaves without a source reads 0,
+// the identity of both the unsigned maximum and the sum.  No LDS traffic is involved.
+enum : int { kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118, kDppBcast15 = 0x142,
+             kDppBcast31 = 0x143 };
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppShr1, 0xf, 0xf, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppShr2, 0xf, 0xf, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppShr4, 0xf, 0xf, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppShr8, 0xf, 0xf, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppBcast15, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppBcast31, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Largest 64-bit key of the wave: the largest high word, then the largest low word among the
+// lanes that hold it (lexicographic, i.e. the unsigned 64-bit maximum).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int CTRL, int ROWS, bool BOUND>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, BOUND));
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v += dpp_f32<kDppShr1, 0xf, true>(v);
+  v += dpp_f32<kDppShr2, 0xf, true>(v);
+  v += dpp_f32<kDppShr4, 0xf, true>(v);
+  v += dpp_f32<kDppShr8, 0xf, true>(v);
+  v += dpp_f32<kDppBcast15, 0xa, false>(v);
+  v += dpp_f32<kDppBcast31, 0xc, false>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Load 8 consecutive elements starting at p (16-byte aligned) as fp32.
