@@ -4,8 +4,10 @@
 // MoE list; AI-infra book, section 9.3.4).  The logit of (t, e) is an fp32
 // fused-multiply-add chain over h in ascending order; this fixed order is the
 // library's contract, so the chain is computed as is: one lane owns one expert
-// and walks h upward, the token's activations are wave-uniform and come in
-// through scalar loads.  Top-k is k rounds of a wave-wide max (DPP) over 64-bit
+// and walks h upward; the token's activations are staged in LDS as fp32 and
+// every lane reads them at one address (broadcast).  With few tokens the time
+// is that of one wave issuing the chain (about 2.3 instructions per h), not
+// memory.  Top-k is k rounds of a wave-wide max (DPP) over 64-bit
 // keys (orderable logit bits, inverted expert id), so equal logits go to the
 // lower expert index; the gates are a softmax over the k selected logits.
 #include "permute_dev.h"
