@@ -53,10 +53,15 @@ __device__ __forceinline__ v8i_t frag(const u32x4_t &lo, const u32x4_t &hi) {
 // blocks per M tile (1 keeps the registers of two waves per SIMD; 2 streams the weights once per
 // 64 rows of an expert at one wave per SIMD).  S4: K is a multiple of 512 and the scale arrays
 // are 16-byte aligned, so each row's scales are read 16 bytes (four K steps) at a time instead of
-// one dword per step (a quarter of the scale requests).
-template <int MODE, int XMB, bool S4, bool GATHER, bool ATOMIC>
+// one dword per step (a quarter of the scale requests).  WLDS (K <= 4096): the wave first copies
+// the scale rows of its 64 weight rows (at most 128 bytes, one line, each) into its own part of
+// LDS and reads each step's scale dword there, so every scale line leaves HBM once; read from
+// memory step by step, a row's scale line is usually evicted from L2 between two steps.
+template <int MODE, int XMB, bool S4, bool WLDS, bool GATHER, bool ATOMIC>
 __global__ __launch_bounds__(64 * XWAVES) void ffn_mx_stream_kernel(MxsParams mp) {
   constexpr int XBM = 32 * XMB;  // rows per M tile
+  constexpr int WSTRIDE = 33;    // LDS dwords per weight row's scales (K <= 4096, one pad dword)
+  __shared__ uint32_t wsl[WLDS ? XWAVES : 1][2][32][WLDS ? WSTRIDE : 1];
   const TileParams &p = mp.tp;
   const int K = MODE == 0 ? p.H : p.I;
   const int Ncols = MODE == 0 ? p.I : p.H;
@@ -111,7 +116,9 @@ __global__ __launch_bounds__(64 * XWAVES) void ffn_mx_stream_kernel(MxsParams mp
     for (int b = 0; b < 2; b++) {
 #pragma unroll
       for (int q = 0; q < 4; q++) wq[buf][b][q] = *(const u32x4_t *)(wrow[b] + k0 + 32 * q);
-      if constexpr (S4) {
+      if constexpr (WLDS) {
+        // the weight scales are in LDS
+      } else if constexpr (S4) {
         if ((s & 3) == 0) wnxt[b] = *(const u32x4_t *)(wsrow[b] + 4 * s);  // s is uniform
       } else {
         wsc[buf][b] = *(const uint32_t *)(wsrow[b] + 4 * s);
@@ -134,8 +141,10 @@ __global__ __launch_bounds__(64 * XWAVES) void ffn_mx_stream_kernel(MxsParams mp
     uint32_t sb[2], sa[XMB];
     if constexpr (S4) {
       if ((s & 3) == 0) {
+        if constexpr (!WLDS) {
 #pragma unroll
-        for (int b = 0; b < 2; b++) wcur[b] = wnxt[b];
+          for (int b = 0; b < 2; b++) wcur[b] = wnxt[b];
+        }
 #pragma unroll
         for (int mb = 0; mb < XMB; mb++) acur[mb] = anxt[mb];
       }
@@ -143,15 +152,23 @@ __global__ __launch_bounds__(64 * XWAVES) void ffn_mx_stream_kernel(MxsParams mp
       auto pick = [&](const u32x4_t &v) {
         return buf == 0 ? (hi2 ? v.z : v.x) : (hi2 ? v.w : v.y);
       };
+      if constexpr (!WLDS) {
 #pragma unroll
-      for (int b = 0; b < 2; b++) sb[b] = pick(wcur[b]) >> (8 * h);
+        for (int b = 0; b < 2; b++) sb[b] = pick(wcur[b]) >> (8 * h);
+      }
 #pragma unroll
       for (int mb = 0; mb < XMB; mb++) sa[mb] = pick(acur[mb]) >> (8 * h);
     } else {
+      if constexpr (!WLDS) {
 #pragma unroll
-      for (int b = 0; b < 2; b++) sb[b] = wsc[buf][b] >> (8 * h);
+        for (int b = 0; b < 2; b++) sb[b] = wsc[buf][b] >> (8 * h);
+      }
 #pragma unroll
       for (int mb = 0; mb < XMB; mb++) sa[mb] = asc[buf][mb] >> (8 * h);
+    }
+    if constexpr (WLDS) {
+#pragma unroll
+      for (int b = 0; b < 2; b++) sb[b] = wsl[wave][b][n][s] >> (8 * h);
     }
     // instruction j: pieces 2j, 2j+1 of the lane's loads, blocks 2j (half 0) and 2j+1 (half 1)
     auto pair = [&](auto JC) __attribute__((always_inline)) {
@@ -179,6 +196,15 @@ __global__ __launch_bounds__(64 * XWAVES) void ffn_mx_stream_kernel(MxsParams mp
   };
   const int KT = K / 128;  // with S4 a multiple of 4
   load(0, 0);
+  if constexpr (WLDS) {
+    // lane (n, h) copies its half of the scale dwords of row n of both weight blocks; only this
+    // wave reads them, and LDS operations of one wave are done in order, so no barrier is needed
+    const int kd = kb / 4, half = (kd + 1) / 2;
+    const int i0 = h * half, i1 = min(kd, i0 + half);
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+      for (int i = i0; i < i1; i++) wsl[wave][b][n][i] = *(const uint32_t *)(wsrow[b] + 4 * i);
+  }
   int s = 0;
   for (; s + 2 <= KT; s += 2) {
     load(1, s + 1);
@@ -235,12 +261,17 @@ hipError_t launch_xs(const MxsParams &mp, int xmb, long long max_mt, int ntiles,
   const int grid = (int)(max_mt * ntiles);
   const int K = MODE == 0 ? mp.tp.H : mp.tp.I;
   const bool s4 = K % 512 == 0 && (((uintptr_t)mp.a_scales | (uintptr_t)mp.w_scales) & 15u) == 0;
+  const bool wl = K <= 4096;  // a row's scale dwords fit the LDS row of ffn_mx_stream_kernel
   dim3 g(grid), b(64 * XWAVES);
-  if (xmb == 1 && s4) hipLaunchKernelGGL((ffn_mx_stream_kernel<MODE, 1, true, GATHER, ATOMIC>), g, b, 0, s, mp);
-  else if (xmb == 1) hipLaunchKernelGGL((ffn_mx_stream_kernel<MODE, 1, false, GATHER, ATOMIC>), g, b, 0, s, mp);
-  else if (s4) hipLaunchKernelGGL((ffn_mx_stream_kernel<MODE, 2, true, GATHER, ATOMIC>), g, b, 0, s, mp);
-  else hipLaunchKernelGGL((ffn_mx_stream_kernel<MODE, 2, false, GATHER, ATOMIC>), g, b, 0, s, mp);
-  return hipGetLastError();
+#define XS_CASE(XMB, S4, WL)                                                                      \
+  if (xmb == XMB && s4 == S4 && wl == WL) {                                                      \
+    hipLaunchKernelGGL((ffn_mx_stream_kernel<MODE, XMB, S4, WL, GATHER, ATOMIC>), g, b, 0, s, mp); \
+    return hipGetLastError();                                                                    \
+  }
+  XS_CASE(1, true, true) XS_CASE(1, false, true) XS_CASE(2, true, true) XS_CASE(2, false, true)
+  XS_CASE(1, true, false) XS_CASE(1, false, false) XS_CASE(2, true, false) XS_CASE(2, false, false)
+#undef XS_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
