@@ -177,7 +177,7 @@ def main():
         if mx:
             moe.moe_grouped_ffn_mx(xq, xs, p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
                                    dev["w_gate_up"], dev["s_gate_up"], dev["w_down"], dev["s_down"], phase=phase,
-                                   **outs, **common)
+                                   packed=packed, **outs, **common)
         else:
             moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
                                 dev["w_gate_up"], dev["w_down"], dev["s_gate_up"], dev["s_down"], phase=phase,

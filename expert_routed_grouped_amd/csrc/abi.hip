@@ -291,7 +291,6 @@ int moe_grouped_ffn_mx(const uint8_t *a_codes, const uint8_t *a_scales, const in
   if ((long long)R_cap > (long long)T * E_loc) return MOE_ERR_SHAPE;
   if ((long long)(T > R_cap ? T : R_cap) * (H > I ? H : I) >= (1LL << 30) || (long long)H * I >= (1LL << 30))
     return MOE_ERR_SHAPE;
-  if (flags & MOE_FFN_PACKED_WEIGHTS) return MOE_ERR_DTYPE;  // MX weights are row-major only
   if ((y == nullptr) == (y_perm == nullptr)) return MOE_ERR_NULL;
   const bool gather = (flags & MOE_FFN_GATHER) != 0;
   if (!a_codes || !a_scales || !offsets || !wgu_codes || !wgu_scales || !wd_codes || !wd_scales) return MOE_ERR_NULL;
@@ -310,6 +309,7 @@ int moe_grouped_ffn_mx(const uint8_t *a_codes, const uint8_t *a_scales, const in
     if (launch_zero_f32(y, (size_t)T * H, s) != hipSuccess) return MOE_ERR_HIP;
   }
   FfnMxArgs fa{};
+  fa.wpacked = (flags & MOE_FFN_PACKED_WEIGHTS) ? 1 : 0;
   fa.a = a_codes;
   fa.a_s = a_scales;
   fa.gather = gather;

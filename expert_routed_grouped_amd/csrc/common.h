@@ -128,6 +128,7 @@ struct FfnMxArgs {
   void *ws;
   int phase;                   // bit 0: gate/up half, bit 1: down half
   int kernel;                  // 0 pick by rows per expert, 1 weight streaming, 2 tiles
+  int wpacked;                 // weight codes in the packed block layout (moe_pack_weights)
 };
 size_t ffn_mx_h_bytes(int R_cap, int I);
 hipError_t launch_ffn_mx(const FfnMxArgs &a, hipStream_t s);

@@ -62,6 +62,7 @@ struct MxParams {
 
 struct Src {
   uint32_t aoff[3], boff[4];   // byte offsets of this lane's A / B segment chunks at K step 0
+  uint32_t bstep;              // bytes from one K step of the weight codes to the next (row-major or packed)
   const uint8_t *sptr;         // this lane's scale dword at K step 0: A row (lanes < 32) or B row
 };
 
@@ -77,7 +78,7 @@ __device__ __forceinline__ void kloop(const char *abase, const char *bbase, cons
                                      (lds_void *)(lds + (kt & 1) * A_BYTES + (wave + 8 * u) * 1024), 16, 0, 0);
   };
   auto loadB = [&](int kt, int u) __attribute__((always_inline)) {
-    __builtin_amdgcn_global_load_lds((const void *)(bbase + (size_t)min(kt, KT - 1) * BK + src.boff[u]),
+    __builtin_amdgcn_global_load_lds((const void *)(bbase + (size_t)min(kt, KT - 1) * src.bstep + src.boff[u]),
                                      (lds_void *)(lds + OFF_B + (kt % 3) * BSLOT + (wave + 8 * u) * 1024), 16, 0, 0);
   };
   auto loadS = [&](int kt) __attribute__((always_inline)) {  // four scale bytes per row and K step
@@ -253,8 +254,14 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
     const int row = (wave + 8 * u) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     if (u < 3) src.aoff[u] = a_row(row) * (uint32_t)K + (uint32_t)chunk * 16u;
-    src.boff[u] = (uint32_t)w_row(row) * (uint32_t)K + (uint32_t)chunk * 16u;
+    // 16-byte chunk c of a 128-value step: row-major at 16c; packed in the 64-value chunk c / 4
+    // of the row's 32-row block, at 16 (c % 4) inside its 64-byte piece
+    const uint32_t wr = (uint32_t)w_row(row);
+    src.boff[u] = p.wpacked ? (wr >> 5) * 32u * (uint32_t)K + (wr & 31u) * 64u + (uint32_t)(chunk >> 2) * 2048u +
+                                  (uint32_t)(chunk & 3) * 16u
+                            : wr * (uint32_t)K + (uint32_t)chunk * 16u;
   }
+  src.bstep = p.wpacked ? 2u * 2048u : (uint32_t)BK;
   {
     const int row = wave * 32 + (lane & 31);
     src.sptr = lane < 32 ? asb + (size_t)a_row(row) * kb : bsb + (size_t)w_row(row) * kb;
@@ -299,6 +306,7 @@ hipError_t launch_ffn_mx(const FfnMxArgs &a, hipStream_t s) {
   mp.tp.H = a.H;
   mp.tp.I = a.I;
   mp.tp.R_cap = a.R_cap;
+  mp.tp.wpacked = a.wpacked;
   if (a.phase & 1) {
     MxParams m = mp;
     m.tp.a = a.a;

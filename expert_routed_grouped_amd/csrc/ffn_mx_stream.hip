@@ -80,11 +80,14 @@ __global__ __launch_bounds__(64 * XWAVES) void ffn_mx_stream_kernel(MxsParams mp
   // this lane's weight rows (gate + up, or two down blocks) and activation rows; activation
   // rows past the end repeat the last valid row (their results are never stored)
   const uint8_t *wrow[2], *wsrow[2], *arow[XMB], *asrow[XMB];
+  // codes of one K step (128 values): two 64-wide chunks, cstep bytes apart (64 row-major, 2048
+  // in the packed 32-row x 64-value blocks)
+  const size_t cstep = ffn::w_chunk_step(p.wpacked, 1);
   {
     const size_t r0w = (size_t)e * Nw + c0 + n;
     const size_t r1w = MODE == 0 ? r0w + p.I : r0w + 32;
-    wrow[0] = (const uint8_t *)p.w + r0w * K + 16 * h;
-    wrow[1] = (const uint8_t *)p.w + r1w * K + 16 * h;
+    wrow[0] = (const uint8_t *)p.w + ffn::w_row_off(p.wpacked, r0w, K, 1) + 16 * h;
+    wrow[1] = (const uint8_t *)p.w + ffn::w_row_off(p.wpacked, r1w, K, 1) + 16 * h;
     wsrow[0] = mp.w_scales + r0w * kb;
     wsrow[1] = mp.w_scales + r1w * kb;
   }
@@ -111,11 +114,11 @@ __global__ __launch_bounds__(64 * XWAVES) void ffn_mx_stream_kernel(MxsParams mp
   uint32_t wsc[2][2], asc[2][XMB];
   u32x4_t wnxt[2], anxt[XMB], wcur[2], acur[XMB];
   auto load = [&](int buf, int s) __attribute__((always_inline)) {
-    const size_t k0 = (size_t)s * 128;
+    const size_t k0 = (size_t)s * 128, w0 = (size_t)s * 2 * cstep;
 #pragma unroll
     for (int b = 0; b < 2; b++) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) wq[buf][b][q] = *(const u32x4_t *)(wrow[b] + k0 + 32 * q);
+      for (int q = 0; q < 4; q++) wq[buf][b][q] = *(const u32x4_t *)(wrow[b] + w0 + (q >> 1) * cstep + 32 * (q & 1));
       if constexpr (WLDS) {
         // the weight scales are in LDS
       } else if constexpr (S4) {
@@ -296,6 +299,7 @@ hipError_t launch_ffn_mx_stream(const FfnMxArgs &a, hipStream_t s) {
   mp.tp.H = a.H;
   mp.tp.I = a.I;
   mp.tp.R_cap = a.R_cap;
+  mp.tp.wpacked = a.wpacked;
   if (a.phase & 1) {
     MxsParams m = mp;
     m.tp.a = a.a;

@@ -48,10 +48,11 @@ def to_device(inputs: dict, device="cuda") -> dict:
 
 
 def pack_weights(dev: dict) -> dict:
-    """Replace the bf16 / fp8 expert weights of ``dev`` (routed and shared) by copies in the packed
-    block layout (``moe_pack_weights``); later calls pass ``packed=True``.  fp32 weights stay
-    row-major.  Done once, outside any timed region, like loading the weights."""
-    if dev["cfg"].wdt not in ("bf16", "fp8") or dev.get("packed"):
+    """Replace the bf16 / fp8 expert weights (MXFP8: their codes) of ``dev`` (routed and shared) by
+    copies in the packed block layout (``moe_pack_weights``); later calls pass ``packed=True``.
+    fp32 weights and MX scales stay row-major.  Done once, outside any timed region, like loading
+    the weights."""
+    if dev["cfg"].wdt not in ("bf16", "fp8", "mxfp8") or dev.get("packed"):
         return dev
     for key in ("w_gate_up", "w_down", "ws_gate_up", "ws_down"):
         if dev.get(key) is not None:

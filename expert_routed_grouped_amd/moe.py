@@ -221,8 +221,10 @@ def moe_grouped_ffn_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, offsets: t
                        row_w: torch.Tensor, T: int, R_cap: int, wgu_codes: torch.Tensor, wgu_scales: torch.Tensor,
                        wd_codes: torch.Tensor, wd_scales: torch.Tensor, y: Optional[torch.Tensor] = None,
                        y_perm: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                       gather: bool = True, zero_y: bool = True, phase: str = "both", stream=None):
-    """W8A8 MXFP8 SwiGLU expert FFN (activations and weights as MX codes + E8M0 scales)."""
+                       gather: bool = True, zero_y: bool = True, phase: str = "both", packed: bool = False,
+                       stream=None):
+    """W8A8 MXFP8 SwiGLU expert FFN (activations and weights as MX codes + E8M0 scales).  ``packed``:
+    the weight codes are in the packed block layout (moe_pack_weights); scales stay row-major."""
     El, twoI, H = wgu_codes.shape
     I = twoI // 2
     need = moe_ffn_mx_workspace_size(R_cap, I)
@@ -230,6 +232,7 @@ def moe_grouped_ffn_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, offsets: t
         workspace = torch.empty(need, dtype=torch.uint8, device=a_codes.device)
     flags = (MOE_FFN_GATHER if gather else 0) | (MOE_FFN_ZERO_Y if zero_y else 0)
     flags |= {"both": 0, "gate_up": MOE_FFN_ONLY_GATE_UP, "down": MOE_FFN_ONLY_DOWN}[phase]
+    flags |= MOE_FFN_PACKED_WEIGHTS if packed else 0
     _check("moe_grouped_ffn_mx", lib().moe_grouped_ffn_mx(
         _ptr(a_codes), _ptr(a_scales), _ptr(offsets), _ptr(row_token), _ptr(row_w), El, T, R_cap, H, I,
         _ptr(wgu_codes), _ptr(wgu_scales), _ptr(wd_codes), _ptr(wd_scales), _ptr(y), _ptr(y_perm), _ptr(workspace),

@@ -268,8 +268,9 @@ size_t moe_ffn_mx_workspace_size(int R_cap, int I);
  * exact E4M3 products times their two block scales in fp32 on the fp8 matrix
  * cores; h_r = silu(G) * U in fp32 is quantised per row with the rule of
  * moe_quantize_mx (blocks of 32 along I) into the workspace before the down
- * projection.  Outputs, flags and the combine are those of moe_grouped_ffn
- * (MX weights are row-major only: MOE_FFN_PACKED_WEIGHTS is MOE_ERR_DTYPE).
+ * projection.  Outputs, flags and the combine are those of moe_grouped_ffn;
+ * with MOE_FFN_PACKED_WEIGHTS the weight codes are in the packed block layout
+ * of moe_pack_weights (packed as MOE_FP8_E4M3 bytes), the scales stay row-major.
  * H and I must be multiples of 128; pointers 16-byte aligned (scale arrays
  * 4-byte aligned); workspace at least moe_ffn_mx_workspace_size(R_cap, I)
  * bytes, 256-byte aligned.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE,

@@ -107,7 +107,7 @@ def ffn_mx(**kw):
     (dict(H=192), -2), (dict(I=64), -2), (dict(El=0), -2), (dict(R=16 * 8 + 1), -2), (dict(T=1 << 20, R=1 << 20, H=1024), -2),
     (dict(y=None), -1), (dict(yp=FAKE), -1), (dict(as_=None), -1), (dict(wds=None), -1), (dict(rt=None), -1),
     (dict(ws=None), -4), (dict(wsb=10), -4), (dict(a=FAKE_ODD), -6), (dict(as_=P(0x1002)), -6),
-    (dict(ws=P(0x1010)), -6), (dict(flags=3 | 4 | 8), -2), (dict(flags=3 | 16), -3),
+    (dict(ws=P(0x1010)), -6), (dict(flags=3 | 4 | 8), -2),
 ])
 def test_ffn_mx_validation(kw, code):
     assert ffn_mx(**kw) == code

@@ -564,22 +564,28 @@ def test_quantize_mx_matches_oracle(dt):
     assert np.array_equal(codes.cpu().numpy(), oc)
 
 
-def mx_layer(dev, cfg, ids_d, w_d, fused):
-    """The W8A8 layer on the GPU; returns (y, perm dict, MX intermediate (codes, scales) from the workspace)."""
+def mx_layer(dev, cfg, ids_d, w_d, fused, packed=False, y_rows=None):
+    """The W8A8 layer on the GPU; returns (y, perm dict, MX intermediate (codes, scales) from the workspace).
+    ``packed``: the weight codes go in as packed copies (moe_pack_weights).  ``y_rows``: a list that
+    receives the per-row outputs of the unfused path."""
     p = moe.moe_permute(ids_d, w_d, cfg.E, cfg.lo, cfg.hi)
     R_cap = p["R_cap"]
     xq, xs = moe.moe_quantize_mx(dev["x"])
     y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
     ws = torch.empty(moe.moe_ffn_mx_workspace_size(R_cap, cfg.I), dtype=torch.uint8, device="cuda")
-    args = (xq, xs, p["offsets"], p["row_token"], p["row_w"], cfg.T, R_cap, dev["w_gate_up"], dev["s_gate_up"],
-            dev["w_down"], dev["s_down"])
+    wgu, wd = dev["w_gate_up"], dev["w_down"]
+    if packed:
+        wgu, wd = moe.moe_pack_weights(wgu), moe.moe_pack_weights(wd)
+    args = (xq, xs, p["offsets"], p["row_token"], p["row_w"], cfg.T, R_cap, wgu, dev["s_gate_up"], wd, dev["s_down"])
     if fused:
         y.fill_(float("nan"))
-        moe.moe_grouped_ffn_mx(*args, y=y, zero_y=True, workspace=ws)
+        moe.moe_grouped_ffn_mx(*args, y=y, zero_y=True, workspace=ws, packed=packed)
     else:
         yp = torch.empty((max(R_cap, 1), cfg.H), dtype=torch.float32, device="cuda")
-        moe.moe_grouped_ffn_mx(*args, y_perm=yp, workspace=ws)
+        moe.moe_grouped_ffn_mx(*args, y_perm=yp, workspace=ws, packed=packed)
         moe.moe_combine(yp, p["token_row"], w_d, y=y)
+        if y_rows is not None:
+            y_rows.append(yp)
     torch.cuda.synchronize()
     wsn = ws.cpu().numpy()
     hbytes = -(-R_cap * cfg.I // 256) * 256
@@ -727,6 +733,26 @@ def test_layer_mx_tile_boundaries(fused):
     ids_d, w_d = to_dev_routing(ids, w)
     y, p, h = mx_layer(dev, cfg, ids_d, w_d, fused)
     assert p["counts"].cpu().tolist() == counts
+    check_mx_layer(cfg, inp, ids, w, y, h)
+
+
+@pytest.mark.parametrize("cfg", [MX_CASES[0], MX_CASES[2], MX_CASES[3], MX_CASES[4]], ids=lambda c: c.name)
+def test_mx_packed_weights_bit_identical(cfg):
+    """Packed MX weight codes (tile kernel: mx_small; streaming kernel: the others) give the same
+    MX intermediate and per-row outputs, bit for bit, as row-major codes; the fused layer with
+    packed codes passes the oracle check."""
+    inp = host_inputs(cfg)
+    dev = mx_dev(inp)
+    ids, w = oracle_routing(cfg)
+    ids_d, w_d = to_dev_routing(ids, w)
+    say(f"MX packed weights {cfg.name}: T={cfg.T} H={cfg.H} E_loc={cfg.E_loc} I={cfg.I}")
+    rows_rm, rows_pk = [], []
+    _, p, h_rm = mx_layer(dev, cfg, ids_d, w_d, fused=False, y_rows=rows_rm)
+    _, _, h_pk = mx_layer(dev, cfg, ids_d, w_d, fused=False, packed=True, y_rows=rows_pk)
+    R = int(p["offsets"][-1])
+    assert np.array_equal(h_rm[0][:R], h_pk[0][:R]) and np.array_equal(h_rm[1][:R], h_pk[1][:R])
+    assert torch.equal(rows_rm[0][:R].view(torch.int32), rows_pk[0][:R].view(torch.int32))
+    y, _, h = mx_layer(dev, cfg, ids_d, w_d, fused=True, packed=True)
     check_mx_layer(cfg, inp, ids, w, y, h)
 
 
