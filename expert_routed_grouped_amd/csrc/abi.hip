@@ -4,6 +4,10 @@
 #include "../../include/moe.h"
 #include "common.h"
 
+#ifndef SHARED_SPLIT_WG
+#define SHARED_SPLIT_WG 192  // measured on the 64-token decode batch (I_s = 1536): 1024 -> 72 us, 384 -> 72, 192 -> 55, 96 -> 57, 48 -> 74
+#endif
+
 #define MOE_VERSION_NUMBER 100  // 0.1.0
 
 namespace {
@@ -245,9 +249,9 @@ int moe_shared_expert(const void *x, int x_dtype, int T, int H, int I_s, const v
   fa.wpacked = (flags & MOE_FFN_PACKED_WEIGHTS) != 0;
   if (T <= SHARED_STREAM_ROWS && x_dtype == MOE_BF16) {
     // one expert gives only I_s / 128 gate/up workgroups per 64-row tile: split K over up to half
-    // the 64-wide chunks so that about a thousand workgroups stream the weights
+    // the 64-wide chunks so that about SHARED_SPLIT_WG workgroups stream the weights
     const int tiles = (T + 63) / 64 * ((I_s + 127) / 128);
-    int ks = (1024 + tiles - 1) / tiles;
+    int ks = (SHARED_SPLIT_WG + tiles - 1) / tiles;
     if (ks > H / 128) ks = H / 128;
     fa.ksplit = ks > 1 ? ks : 1;
     fa.gu32 = (float *)(maps + 256 + 2 * align_up((size_t)T * 4, 256));
