@@ -469,24 +469,29 @@ hipError_t launch_tt(const void *x, int xb, const void *w, int wb, const float *
   return hipErrorInvalidValue;
 }
 
-#ifndef ROUTE_TR
-#define ROUTE_TR 3
-#endif
-
-template <int EC>
-hipError_t launch_staged(const void *x, int xb, const void *w, int wb, const float *bias, int T, int H, int E, int k,
-                         int32_t *ids, float *gates, hipStream_t s) {
-  constexpr int TB = 4 * ROUTE_TR;
+// Tokens per wave of the staged kernel: 4 (16 per workgroup) while that still gives at least two
+// workgroups per compute unit (512 on MI355X), else 3.  Measured on MI355X, moe_route alone:
+// T = 6000: 3 -> 166 us, 4 -> 186 us (375 workgroups); T = 8192: 3 -> 218 us, 4 -> 196 us.
+template <int TR, int EC>
+hipError_t launch_staged_tr(const void *x, int xb, const void *w, int wb, const float *bias, int T, int H, int E,
+                            int k, int32_t *ids, float *gates, hipStream_t s) {
+  constexpr int TB = 4 * TR;
   dim3 grid(ceil_div_i(T, TB)), block(256);
 #define STAGED_CASE(XB, WB)                                                                                      \
   if (xb == XB && wb == WB) {                                                                                  \
-    hipLaunchKernelGGL((route_staged_kernel<ROUTE_TR, EC, XB, WB>), grid, block, 0, s, x, w, bias, T, H, E, k, ids, \
-                       gates);                                                                                 \
+    hipLaunchKernelGGL((route_staged_kernel<TR, EC, XB, WB>), grid, block, 0, s, x, w, bias, T, H, E, k, ids, gates); \
     return hipGetLastError();                                                                                  \
   }
   STAGED_CASE(true, true) STAGED_CASE(false, false) STAGED_CASE(true, false) STAGED_CASE(false, true)
 #undef STAGED_CASE
   return hipErrorInvalidValue;
+}
+
+template <int EC>
+hipError_t launch_staged(const void *x, int xb, const void *w, int wb, const float *bias, int T, int H, int E, int k,
+                         int32_t *ids, float *gates, hipStream_t s) {
+  if (ceil_div_i(T, 16) >= 512) return launch_staged_tr<4, EC>(x, xb, w, wb, bias, T, H, E, k, ids, gates, s);
+  return launch_staged_tr<3, EC>(x, xb, w, wb, bias, T, H, E, k, ids, gates, s);
 }
 
 template <int EC>

@@ -91,6 +91,8 @@ ROUTE_CASES = [
     LayerConfig("r_E512_k32", T=70, H=256, E=512, k=32, I=64, seed=103, w_std=0.05),
     LayerConfig("r_kE", T=64, H=128, E=16, k=16, I=64, seed=104),
     LayerConfig("r_k1", T=513, H=64, E=64, k=1, I=64, seed=105),
+    # 16 tokens per workgroup (at least 512 workgroups), the last one partly empty
+    LayerConfig("r_tr4_ragged", T=8195, H=256, E=128, k=8, I=64, seed=106, w_std=0.05),
 ]
 
 
