@@ -126,6 +126,53 @@ def test_route_ties_and_zero_router():
     assert np.all(ids == np.arange(8)) and np.all(w == np.float32(0.125))
 
 
+
+@pytest.mark.parametrize("T,path", [(40, "route"), (300, "route"), (8200, "route"), (40, "dispatch"),
+                                    (300, "dispatch")])
+def test_route_ties_every_path(T, path):
+    """Exact ties (duplicated router rows, within one 64-expert half and across halves, one of three)
+    go to the lower expert index on every router path: one token per workgroup (T <= 256), the
+    LDS-staged kernel with 12 and 16 tokens per workgroup, and route + dispatch."""
+    cfg = LayerConfig(f"ties{T}", T=T, H=256, E=128, k=8, I=64, seed=108)
+    inp = synth.make_inputs(cfg, with_weights=False)
+    wr = inp["w_router"].copy()
+    wr[7] = wr[3]
+    wr[100] = wr[3]
+    wr[64] = wr[0]
+    wr[127] = wr[126]
+    dev = L.to_device(dict(inp, w_router=wr))
+    say(f"route ties T={T} via {path}")
+    ids_o, w_o, _ = O.route(inp["x"], wr, None, cfg.k)
+    if path == "route":
+        ids, w = gpu_route(dev, cfg)
+    else:
+        ws = moe.moe_route_dispatch_workspace()
+        out = dict(counts=torch.empty((cfg.E,), dtype=torch.int32, device="cuda"),
+                   offsets=torch.empty((cfg.E + 1,), dtype=torch.int32, device="cuda"),
+                   row_token=torch.empty((T * cfg.k,), dtype=torch.int32, device="cuda"),
+                   row_w=torch.empty((T * cfg.k,), dtype=torch.float32, device="cuda"),
+                   token_row=torch.empty((T, cfg.k), dtype=torch.int32, device="cuda"))
+        ids_d = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+        w_d = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+        moe.moe_route_dispatch(dev["x"], dev["w_router"], None, cfg.k, cfg.E, 0, cfg.E, ws, ids_d, w_d, out)
+        torch.cuda.synchronize()
+        ids, w = ids_d.cpu().numpy(), w_d.cpu().numpy()
+        p_o = O.permute(ids_o, w_o, 0, cfg.E)
+        assert np.array_equal(out["offsets"].cpu().numpy(), p_o["offsets"])
+        assert np.array_equal(out["row_token"].cpu().numpy()[:p_o["R"]], p_o["row_token"])
+    assert np.array_equal(ids, ids_o)
+    assert np.max(np.abs(w - w_o)) <= GATE_TOL
+    # the ties really occur: some token selects both members of a duplicated pair, lower index first
+    both = [(a, b) for a, b in ((3, 7), (3, 100), (0, 64), (126, 127))
+            if np.any(np.isin(ids_o, a).any(1) & np.isin(ids_o, b).any(1))]
+    assert both, "no token selected a tied pair"
+    for a, b in both:
+        rows = np.nonzero(np.isin(ids_o, a).any(1) & np.isin(ids_o, b).any(1))[0]
+        pa = np.argmax(ids_o[rows] == a, axis=1)
+        pb = np.argmax(ids_o[rows] == b, axis=1)
+        assert np.all(pa < pb)
+
+
 def test_route_empty_batch():
     cfg = LayerConfig("empty", T=0, H=64, E=8, k=2, I=64, seed=107)
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
