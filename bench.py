@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--flush-steps", type=int, default=20,
                     help="extra steps, each after writing a 1 GiB scratch buffer (cold L2 and Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--router", default="packed", choices=["packed", "as-stored"],
+                    help="decode-sized batches: read the router weight in the layout of moe_pack_router (exact "
+                         "fp32, packed once before timing; routing is bit-identical)")
     ap.add_argument("--weights", default="packed", choices=["packed", "row-major"],
                     help="layout of the resident bf16/fp8 expert weights (packed once with moe_pack_weights "
                          "before timing; MXFP8 and fp32 weights are always row-major)")
@@ -164,6 +167,9 @@ def main():
         L.pack_weights(dev)  # one-time layout change of the resident weights, like loading them
     packed = bool(dev.get("packed", False))
     bufs = L.LayerBuffers(cfg)
+    if bufs.rd_ws is not None and args.router == "packed":
+        L.pack_router(dev)  # one-time layout change of the resident router weight
+    wrp = dev.get("w_router_packed") if bufs.rd_ws is not None else None
     stream = torch.cuda.current_stream()
     p = bufs.perm
     mx = cfg.wdt == "mxfp8"
@@ -187,8 +193,9 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         if bufs.rd_ws is not None:  # decode: route + dispatch (+ zeroing of y) in one launch
-            moe.moe_route_dispatch(dev["x"], dev["w_router"], dev["bias"], cfg.k, cfg.E, cfg.lo, cfg.hi, bufs.rd_ws,
-                                   bufs.topk_ids, bufs.topk_w, p, y_zero=bufs.y if bufs.fused else None,
+            moe.moe_route_dispatch(dev["x"], dev["w_router"] if wrp is None else wrp, dev["bias"], cfg.k, cfg.E,
+                                   cfg.lo, cfg.hi, bufs.rd_ws, bufs.topk_ids, bufs.topk_w, p,
+                                   y_zero=bufs.y if bufs.fused else None, router_packed=wrp is not None,
                                    stream=stream)
         else:
             moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=stream)
@@ -319,7 +326,9 @@ def main():
                    "local_experts": [cfg.lo, cfg.hi], "parallelism": "none (one GPU)",
                    "combine": "fused atomic epilogue" if bufs.fused else "per-row outputs + moe_combine",
                    "dispatch": "route + dispatch in one launch" if bufs.rd_ws is not None else "moe_route + moe_permute",
-                   "weights": "packed 32x64 blocks (moe_pack_weights, once before timing)" if packed else "row-major"},
+                   "weights": "packed 32x64 blocks (moe_pack_weights, once before timing)" if packed else "row-major",
+                   "router_weight": ("fp32 [H/4, E, 4] (moe_pack_router, once before timing)" if wrp is not None
+                                     else "as stored")},
         "roofline": roof,
         "layer": {"ms_p50": round(float(np.median(layer_ms)), 4), "ms_p10": round(float(np.percentile(layer_ms, 10)), 4),
                   "ms_p90": round(float(np.percentile(layer_ms, 90)), 4),

@@ -17,6 +17,9 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 }  // namespace
 
+// defined in route.hip (C++ linkage, outside the C ABI)
+hipError_t launch_pack_router(const void *w, int w_bf16, int E, int H, float *out, hipStream_t s);  // route.hip
+
 extern "C" {
 
 int moe_version(void) { return MOE_VERSION_NUMBER; }
@@ -47,13 +50,23 @@ int moe_route(const void *x, int x_dtype, const void *w_router, int w_dtype, con
 
 size_t moe_route_dispatch_workspace_size(void) { return 256; }
 
+int moe_pack_router(const void *w_router, int w_dtype, int E, int H, float *out, void *stream) {
+  if (E < 1 || E > 512 || H < 4 || H % 4 != 0) return MOE_ERR_SHAPE;
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!w_router || !out) return MOE_ERR_NULL;
+  if (((uintptr_t)w_router & (w_dtype == MOE_BF16 ? 1u : 3u)) != 0 || !aligned16(out)) return MOE_ERR_ALIGN;
+  return hip_status(launch_pack_router(w_router, w_dtype == MOE_BF16, E, H, out, (hipStream_t)stream));
+}
+
 int moe_route_dispatch(const void *x, int x_dtype, const void *w_router, int w_dtype, const float *bias, int T, int H,
                        int E, int k, int e_begin, int e_end, int32_t *topk_ids, float *topk_w, int32_t *counts,
                        int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row, float *y_zero,
                        void *workspace, size_t workspace_bytes, void *stream) {
   if (T < 0 || H < 1 || E < 1 || E > 512 || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
   if (e_begin < 0 || e_end <= e_begin || e_end > E) return MOE_ERR_SHAPE;
-  if ((x_dtype != MOE_F32 && x_dtype != MOE_BF16) || (w_dtype != MOE_F32 && w_dtype != MOE_BF16)) return MOE_ERR_DTYPE;
+  if ((x_dtype != MOE_F32 && x_dtype != MOE_BF16) ||
+      (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_F32_ROUTER_PACKED))
+    return MOE_ERR_DTYPE;
   if (!counts || !offsets) return MOE_ERR_NULL;
   if (T > 0 && (!x || !w_router || !topk_ids || !topk_w || !row_token || !row_w || !token_row)) return MOE_ERR_NULL;
   if (T > 0 && !route_dispatch_fits(T, H, E, k, x, w_router)) return MOE_ERR_SHAPE;
@@ -63,7 +76,8 @@ int moe_route_dispatch(const void *x, int x_dtype, const void *w_router, int w_d
   if (T == 0)  // nothing to route: zero counts and offsets as moe_permute does
     return hip_status(launch_permute(nullptr, nullptr, 0, k, e_begin, e_end - e_begin, counts, offsets, row_token,
                                      row_w, token_row, nullptr, (hipStream_t)stream));
-  return hip_status(launch_route_dispatch(x, x_dtype == MOE_BF16, w_router, w_dtype == MOE_BF16, bias, T, H, E, k,
+  const int w_mode = w_dtype == MOE_BF16 ? 1 : (w_dtype == MOE_F32_ROUTER_PACKED ? 2 : 0);
+  return hip_status(launch_route_dispatch(x, x_dtype == MOE_BF16, w_router, w_mode, bias, T, H, E, k,
                                           e_begin, e_end - e_begin, topk_ids, topk_w, counts, offsets, row_token,
                                           row_w, token_row, y_zero, (uint32_t *)workspace, (hipStream_t)stream));
 }

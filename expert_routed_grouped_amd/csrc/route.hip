@@ -92,10 +92,14 @@ __device__ __forceinline__ float load1(const void *p, size_t i) {
 
 // Block = EC waves (wave c owns experts 64c .. 64c+63), TT tokens per block.
 // VEC: H % 8 == 0 and 16-byte aligned rows (8-wide loads); otherwise one h at a time.
-template <int TT, int EC, bool XB, bool WB, bool VEC>
+// WP (with VEC, fp32): the router weight in the layout of moe_pack_router, [H/4][E][4] fp32:
+// the 16 bytes of h = 4j .. 4j+3 of expert e at (j E + e) 16, so the 64 lanes of a wave read
+// 1 KB contiguously instead of 64 rows 4H bytes apart, and no element needs unpacking.
+template <int TT, int EC, bool XB, bool WB, bool VEC, bool WP = false>
 __device__ __forceinline__ void route_tokens(const void *__restrict__ x, const void *__restrict__ w,
                                              const float *__restrict__ bias, int T, int H, int E, int k,
                                              int32_t *__restrict__ ids, float *__restrict__ gates) {
+  static_assert(!WP || (VEC && !WB), "the packed router weight is fp32, read 16 bytes at a time");
   __shared__ float lg[TT][64 * EC];
   const int lane = threadIdx.x & 63;
   const int c = threadIdx.x >> 6;
@@ -109,7 +113,8 @@ __device__ __forceinline__ void route_tokens(const void *__restrict__ x, const v
     int t = min(t0 + tt, T - 1);
     xrow[tt] = (const char *)x + (size_t)t * H * esz_x;
   }
-  const char *wrow = (const char *)w + (size_t)(ev ? e : 0) * H * esz_w;
+  const char *wrow = WP ? (const char *)w + (size_t)(ev ? e : 0) * 16 : (const char *)w + (size_t)(ev ? e : 0) * H * esz_w;
+  const size_t wpstep = (size_t)E * 16;  // WP: bytes from one 4-wide h group to the next
   // Every block reads all of W_r, which is usually cold (the expert weights of the previous
   // layer call streamed through L2 since).  Each thread of the grid first touches one
   // distinct 128-byte line of it, so the whole matrix is pulled into L2 in one round trip
@@ -149,7 +154,10 @@ __device__ __forceinline__ void route_tokens(const void *__restrict__ x, const v
     u32x4_t ring[NS][P];
     auto wload = [&](u32x4_t(&b)[P], int st) __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = 0; q < P; q++) b[q] = *(const u32x4_t *)(wrow + (size_t)st * HS * esz_w + 16 * q);
+      for (int q = 0; q < P; q++) {
+        if constexpr (WP) b[q] = *(const u32x4_t *)(wrow + ((size_t)st * (HS / 4) + q) * wpstep);
+        else b[q] = *(const u32x4_t *)(wrow + (size_t)st * HS * esz_w + 16 * q);
+      }
     };
     auto wstep = [&](const u32x4_t(&b)[P], int st) __attribute__((always_inline)) {
       const int h = st * HS;
@@ -198,7 +206,13 @@ __device__ __forceinline__ void route_tokens(const void *__restrict__ x, const v
     }
     for (int h = nsteps * HS; h < H; h += 8) {
       float wf[8];
-      load8<WB>(wrow + (size_t)h * esz_w, wf);
+      if constexpr (WP) {
+        const float4 a = *(const float4 *)(wrow + (size_t)(h / 4) * wpstep);
+        const float4 b = *(const float4 *)(wrow + (size_t)(h / 4 + 1) * wpstep);
+        wf[0] = a.x; wf[1] = a.y; wf[2] = a.z; wf[3] = a.w; wf[4] = b.x; wf[5] = b.y; wf[6] = b.z; wf[7] = b.w;
+      } else {
+        load8<WB>(wrow + (size_t)h * esz_w, wf);
+      }
 #pragma unroll
       for (int tt = 0; tt < TT; tt++) {
         const float *xp = xs + tt * H + h;
@@ -270,7 +284,7 @@ __global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__
 // found with a ticket counter, each block publishing its routing before it takes a ticket --
 // groups the assignments by expert (the single-workgroup permutation) and resets the ticket.
 // No block ever waits for another, so no co-residency is assumed.
-template <int EC, bool XB, bool WB>
+template <int EC, bool XB, bool WB, bool WP>
 __global__ __launch_bounds__(64 * EC) void route_dispatch_kernel(const void *__restrict__ x, const void *__restrict__ w,
                                                                  const float *__restrict__ bias, int T, int H, int E,
                                                                  int k, int lo, int El, int nbits,
@@ -287,7 +301,7 @@ __global__ __launch_bounds__(64 * EC) void route_dispatch_kernel(const void *__r
     f32x4_t *row = (f32x4_t *)(y_zero + (size_t)blockIdx.x * H);
     for (int i = threadIdx.x; i < H / 4; i += blockDim.x) row[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  route_tokens<1, EC, XB, WB, true>(x, w, bias, T, H, E, k, ids, gates);
+  route_tokens<1, EC, XB, WB, true, WP>(x, w, bias, T, H, E, k, ids, gates);
   __threadfence();  // this block's ids and gates are visible device-wide before its ticket
   __syncthreads();
   if (threadIdx.x == 0) last = atomicAdd(ticket, 1u) == (uint32_t)gridDim.x - 1u;
@@ -519,13 +533,15 @@ hipError_t launch_rd(const void *x, int xb, const void *w, int wb, const float *
   while ((1 << nbits) < El) nbits++;
   const size_t xs_bytes = sizeof(float) * (size_t)H, perm_bytes = sizeof(int) * (size_t)(EC + 1) * El;
   const size_t shm = xs_bytes > perm_bytes ? xs_bytes : perm_bytes;
-#define RD_CASE(XB, WB)                                                                                          \
-  if (xb == XB && wb == WB) {                                                                                    \
-    hipLaunchKernelGGL((route_dispatch_kernel<EC, XB, WB>), dim3(T), dim3(64 * EC), shm, s, x, w, bias, T, H, E, k, \
-                       lo, El, nbits, ids, gates, counts, offsets, row_token, row_w, token_row, y_zero, ticket);   \
+  // wb: 0 fp32 row-major, 1 bf16 row-major, 2 fp32 in the layout of moe_pack_router
+#define RD_CASE(XB, WB, WP)                                                                                      \
+  if (xb == XB && wb == (WP ? 2 : (WB ? 1 : 0))) {                                                               \
+    hipLaunchKernelGGL((route_dispatch_kernel<EC, XB, WB, WP>), dim3(T), dim3(64 * EC), shm, s, x, w, bias, T, H, E, \
+                       k, lo, El, nbits, ids, gates, counts, offsets, row_token, row_w, token_row, y_zero, ticket); \
     return hipGetLastError();                                                                                    \
   }
-  RD_CASE(true, true) RD_CASE(false, false) RD_CASE(true, false) RD_CASE(false, true)
+  RD_CASE(true, true, false) RD_CASE(false, false, false) RD_CASE(true, false, false) RD_CASE(false, true, false)
+  RD_CASE(true, false, true) RD_CASE(false, false, true)
 #undef RD_CASE
   return hipErrorInvalidValue;
 }
@@ -562,4 +578,34 @@ hipError_t launch_route(const void *x, int x_bf16, const void *w, int w_bf16, co
     case 4: return launch_ec<4>(x, x_bf16, w, w_bf16, bias, T, H, E, k, ids, gates, s);
     default: return launch_ec<8>(x, x_bf16, w, w_bf16, bias, T, H, E, k, ids, gates, s);
   }
+}
+
+namespace {
+// [E, H] (bf16 or fp32) -> [H/4][E][4] fp32: out[(j E + e) 4 + i] = w[e, 4j + i] (exact for bf16).
+__global__ __launch_bounds__(256) void pack_router_kernel(const void *__restrict__ w, int wbf16, int E, int H,
+                                                          float *__restrict__ out) {
+  const size_t n = (size_t)E * (H / 4);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t j = i / E, e = i - j * E;  // output piece i = j E + e
+    const size_t src = e * (size_t)H + 4 * j;
+    f32x4_t v;
+    if (wbf16) {
+      const uint16_t *b = (const uint16_t *)w + src;
+      v = f32x4_t{bf16_to_f32(b[0]), bf16_to_f32(b[1]), bf16_to_f32(b[2]), bf16_to_f32(b[3])};
+    } else {
+      const float *f = (const float *)w + src;
+      v = f32x4_t{f[0], f[1], f[2], f[3]};
+    }
+    *(f32x4_t *)(out + 4 * i) = v;
+  }
+}
+}  // namespace
+
+hipError_t launch_pack_router(const void *w, int w_bf16, int E, int H, float *out, hipStream_t s) {
+  const size_t n = (size_t)E * (H / 4);
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(pack_router_kernel, dim3(blocks < 4096 ? (unsigned)blocks : 4096u), dim3(256), 0, s, w, w_bf16,
+                     E, H, out);
+  return hipGetLastError();
 }

@@ -61,6 +61,15 @@ def pack_weights(dev: dict) -> dict:
     return dev
 
 
+def pack_router(dev: dict) -> dict:
+    """Add the router weight in the layout of moe_pack_router (exact fp32, [H/4, E, 4]) as
+    ``dev["w_router_packed"]``; decode-sized batches (moe_route_dispatch) then read it.  Done once,
+    like loading the weights; routing is bit-identical."""
+    if dev.get("w_router_packed") is None and dev["w_router"].shape[1] % 4 == 0:
+        dev["w_router_packed"] = moe.moe_pack_router(dev["w_router"])
+    return dev
+
+
 class LayerBuffers:
     """Device buffers of one layer shape, reused across calls."""
 
@@ -96,8 +105,10 @@ def run_layer(dev: dict, bufs: LayerBuffers, stream=None) -> torch.Tensor:
     p = bufs.perm
     packed = bool(dev.get("packed", False))
     if bufs.rd_ws is not None:  # one launch: route, dispatch and (fused combine) the zeroing of y
-        moe.moe_route_dispatch(dev["x"], dev["w_router"], dev["bias"], cfg.k, cfg.E, cfg.lo, cfg.hi, bufs.rd_ws,
-                               bufs.topk_ids, bufs.topk_w, p, y_zero=bufs.y if bufs.fused else None, stream=stream)
+        wp = dev.get("w_router_packed")
+        moe.moe_route_dispatch(dev["x"], dev["w_router"] if wp is None else wp, dev["bias"], cfg.k, cfg.E, cfg.lo,
+                               cfg.hi, bufs.rd_ws, bufs.topk_ids, bufs.topk_w, p,
+                               y_zero=bufs.y if bufs.fused else None, router_packed=wp is not None, stream=stream)
     else:
         moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=stream)
         moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=p, stream=stream)

@@ -16,7 +16,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP8 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP8, MOE_F32_ROUTER_PACKED = 0, 1, 2, 3, 4
 MOE_FFN_GATHER, MOE_FFN_ZERO_Y, MOE_FFN_ONLY_GATE_UP, MOE_FFN_ONLY_DOWN = 1, 2, 4, 8
 MOE_FFN_PACKED_WEIGHTS = 16
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE", -4: "MOE_ERR_WORKSPACE",
@@ -26,7 +26,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTY
 EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_permute_workspace_size",
            "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_quantize_mx", "moe_ffn_mx_workspace_size",
            "moe_grouped_ffn_mx", "moe_shared_workspace_size", "moe_shared_expert", "moe_route_dispatch_workspace_size",
-           "moe_route_dispatch", "moe_pack_weights")
+           "moe_route_dispatch", "moe_pack_weights", "moe_pack_router")
 
 
 class MoEError(RuntimeError):
@@ -78,6 +78,8 @@ def lib():
         L.moe_route_dispatch.argtypes = [P, I, P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
         L.moe_pack_weights.restype = I
         L.moe_pack_weights.argtypes = [P, I, I, I, I, P, P]
+        L.moe_pack_router.restype = I
+        L.moe_pack_router.argtypes = [P, I, I, I, P, P]
         _lib = L
     return _lib
 
@@ -291,14 +293,26 @@ def moe_route_dispatch_workspace(device="cuda") -> torch.Tensor:
     return torch.zeros(int(lib().moe_route_dispatch_workspace_size()), dtype=torch.uint8, device=device)
 
 
+def moe_pack_router(w_router: torch.Tensor, stream=None) -> torch.Tensor:
+    """The router weight [E, H] (bf16 or fp32) as exact fp32 in the layout of moe_pack_router,
+    [H/4, E, 4]; pass it to moe_route_dispatch with ``router_packed=True``."""
+    E, H = w_router.shape
+    out = torch.empty((H // 4, E, 4), dtype=torch.float32, device=w_router.device)
+    _check("moe_pack_router", lib().moe_pack_router(_ptr(w_router), _dtype(w_router), E, H, _ptr(out),
+                                                    _stream(stream)))
+    return out
+
+
 def moe_route_dispatch(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor], k: int, E: int,
                        e_begin: int, e_end: int, workspace: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
-                       out: dict, y_zero: Optional[torch.Tensor] = None, stream=None) -> dict:
+                       out: dict, y_zero: Optional[torch.Tensor] = None, router_packed: bool = False,
+                       stream=None) -> dict:
     """Route + local dispatch of a decode batch in one launch; ``out`` holds counts, offsets,
     row_token, row_w, token_row (as from moe_permute); zeroes ``y_zero`` when given."""
     T, H = x.shape
     _check("moe_route_dispatch", lib().moe_route_dispatch(
-        _ptr(x), _dtype(x), _ptr(w_router), _dtype(w_router), _ptr(bias), T, H, E, k, e_begin, e_end, _ptr(topk_ids),
+        _ptr(x), _dtype(x), _ptr(w_router), MOE_F32_ROUTER_PACKED if router_packed else _dtype(w_router), _ptr(bias),
+        T, H, E, k, e_begin, e_end, _ptr(topk_ids),
         _ptr(topk_w), _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["row_token"]), _ptr(out["row_w"]),
         _ptr(out["token_row"]), _ptr(y_zero), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))

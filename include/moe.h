@@ -67,6 +67,7 @@ extern "C" {
 #define MOE_BF16 1
 #define MOE_FP8_E4M3 2
 #define MOE_MXFP8 3
+#define MOE_F32_ROUTER_PACKED 4 /* router weight as written by moe_pack_router (moe_route_dispatch only) */
 
 /* status codes */
 #define MOE_OK 0
@@ -299,6 +300,23 @@ int moe_grouped_ffn_mx(const uint8_t *a_codes, const uint8_t *a_scales, const in
 int moe_combine(const float *y_perm, const int32_t *token_row, const float *topk_w, int T, int k, int H,
                 float *y, void *stream);
 
+/*
+ * moe_pack_router - the router weight in the layout the decode router reads fastest.
+ *
+ * For the callers of moe_route_dispatch that keep the router weight resident:
+ * out [H/4][E][4] fp32 with out[(j*E + e)*4 + i] = w_router[e, 4j + i], the
+ * exact fp32 value of each element (bf16 -> fp32 appends zero bits).  Passed
+ * as w_router with w_dtype MOE_F32_ROUTER_PACKED, the logits are the same
+ * fused-multiply-add chains on the same values, so routing and gates are
+ * bit-identical to the bf16 / fp32 weight; the 64 lanes of a wave (one expert
+ * each) then read 1 KB contiguously per load and unpack nothing.  Done once,
+ * like loading the weights (it costs E*H*4 bytes of HBM).  w_router [E,H]
+ * MOE_BF16 or MOE_F32 (element-aligned); out 16-byte aligned, caller-owned,
+ * not overlapping w_router; H a multiple of 4, 1 <= E <= 512.  Errors:
+ * MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_pack_router(const void *w_router, int w_dtype, int E, int H, float *out, void *stream);
+
 /* Bytes of workspace moe_route_dispatch needs (one ticket counter). */
 size_t moe_route_dispatch_workspace_size(void);
 
@@ -322,7 +340,8 @@ size_t moe_route_dispatch_workspace_size(void);
  * aligned (else MOE_ERR_SHAPE: use moe_route + moe_permute).  The workspace
  * (moe_route_dispatch_workspace_size() bytes, 256-byte aligned) holds a
  * ticket counter that must be zero before the first call (zero it once when
- * allocating); every call leaves it zero.  Calls that share a workspace must
+ * allocating); every call leaves it zero.  w_dtype: MOE_BF16, MOE_F32 or
+ * MOE_F32_ROUTER_PACKED (w_router written by moe_pack_router, same results).  Calls that share a workspace must
  * not overlap (run them on one stream).  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE,
  * MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP.
  */

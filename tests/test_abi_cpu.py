@@ -151,6 +151,18 @@ def test_pack_weights_validation(kw, code):
     assert moe.lib().moe_pack_weights(a["w"], a["dt"], a["E"], a["N"], a["K"], a["out"], None) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), -3), (dict(dt=4), -3), (dict(E=0), -2), (dict(E=513), -2), (dict(H=6), -2), (dict(H=0), -2),
+    (dict(w=None), -1), (dict(out=None), -1), (dict(w=P(0x1001)), -6), (dict(out=P(0x9008)), -6),
+    (dict(dt=0, w=P(0x1002)), -6),
+])
+def test_pack_router_validation(kw, code):
+    # every case is rejected on the host before anything is launched
+    a = dict(w=FAKE, dt=1, E=128, H=4096, out=P(0x9000))
+    a.update(kw)
+    assert moe.lib().moe_pack_router(a["w"], a["dt"], a["E"], a["H"], a["out"], None) == code
+
+
 def route_dispatch(x=FAKE, xd=1, w=FAKE, wd=1, T=64, H=256, E=16, k=4, lo=0, hi=16, ids=FAKE, g=FAKE, c=FAKE,
                    o=FAKE, rt=FAKE, rw=FAKE, tr=FAKE, y=None, ws=FAKE, wsb=256):
     return moe.lib().moe_route_dispatch(x, xd, w, wd, None, T, H, E, k, lo, hi, ids, g, c, o, rt, rw, tr, y, ws, wsb,
@@ -161,6 +173,7 @@ def route_dispatch(x=FAKE, xd=1, w=FAKE, wd=1, T=64, H=256, E=16, k=4, lo=0, hi=
     (dict(T=513), -2), (dict(T=300, k=32, E=64, hi=64), -2), (dict(E=257, hi=257), -2), (dict(H=100), -2),
     (dict(k=17, E=16), -2), (dict(lo=4, hi=4), -2), (dict(hi=17), -2), (dict(x=FAKE_ODD), -2), (dict(xd=2), -3),
     (dict(x=None), -1), (dict(c=None), -1), (dict(rt=None), -1), (dict(ws=None), -4), (dict(wsb=16), -4),
+    (dict(wd=5), -3), (dict(wd=2), -3), (dict(wd=4, ws=None), -4),
     (dict(y=FAKE_ODD), -6),
 ])
 def test_route_dispatch_validation(kw, code):

@@ -520,6 +520,56 @@ def test_route_dispatch_matches_route_then_permute(cfg):
         assert torch.all(ws == 0)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_pack_router_layout(dt):
+    """moe_pack_router: out[(j E + e) 4 + i] = w[e, 4j + i], exact fp32 values."""
+    rng = np.random.default_rng(601)
+    w = rng.standard_normal((21, 264), dtype=np.float32)
+    wt = torch.from_numpy(w).cuda()
+    if dt == "bf16":
+        wt = wt.to(torch.bfloat16)
+    out = moe.moe_pack_router(wt)
+    torch.cuda.synchronize()
+    ref = wt.float().cpu().numpy().reshape(21, 66, 4).transpose(1, 0, 2)
+    assert out.shape == (66, 21, 4) and np.array_equal(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("cfg", RD_CASES, ids=lambda c: c.name)
+def test_route_dispatch_packed_router_bit_identical(cfg):
+    """moe_route_dispatch on the moe_pack_router layout gives the same routing, gates, grouping and
+    zeroing as on the stored router weight (same chains on the same values)."""
+    inp = synth.make_inputs(cfg, with_weights=False)
+    dev = L.to_device(inp)
+    say(f"route+dispatch packed router {cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k}")
+    El = cfg.hi - cfg.lo
+    R_cap = cfg.T * min(cfg.k, El)
+    res = []
+    for packed in (False, True):
+        ws = moe.moe_route_dispatch_workspace()
+        out = dict(counts=torch.full((El,), -7, dtype=torch.int32, device="cuda"),
+                   offsets=torch.full((El + 1,), -7, dtype=torch.int32, device="cuda"),
+                   row_token=torch.full((max(R_cap, 1),), -7, dtype=torch.int32, device="cuda"),
+                   row_w=torch.full((max(R_cap, 1),), -7.0, dtype=torch.float32, device="cuda"),
+                   token_row=torch.full((cfg.T, cfg.k), -7, dtype=torch.int32, device="cuda"))
+        ids = torch.full((cfg.T, cfg.k), -7, dtype=torch.int32, device="cuda")
+        w = torch.full((cfg.T, cfg.k), -7.0, dtype=torch.float32, device="cuda")
+        y = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.float32, device="cuda")
+        wr = moe.moe_pack_router(dev["w_router"]) if packed else dev["w_router"]
+        moe.moe_route_dispatch(dev["x"], wr, dev["bias"], cfg.k, cfg.E, cfg.lo, cfg.hi, ws, ids, w, out, y_zero=y,
+                               router_packed=packed)
+        torch.cuda.synchronize()
+        assert torch.all(y == 0) and torch.all(ws == 0)
+        res.append((ids, w, out))
+    (i0, w0, o0), (i1, w1, o1) = res
+    assert torch.equal(i0, i1) and torch.equal(w0.view(torch.int32), w1.view(torch.int32))
+    R = int(o0["offsets"][-1])
+    for key in ("counts", "offsets", "token_row"):
+        assert torch.equal(o0[key], o1[key]), key
+    assert torch.equal(o0["row_token"][:R], o1["row_token"][:R])
+    ids_o, _, _ = O.route(inp["x"], inp["w_router"], inp["bias"], cfg.k)
+    assert np.array_equal(i1.cpu().numpy(), ids_o)
+
+
 def test_route_dispatch_empty_batch_zeroes_counts():
     ws = moe.moe_route_dispatch_workspace()
     x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
