@@ -385,12 +385,18 @@ def test_ffn_empty_batch_zeroes_y():
 # the decode layer under HIP graph capture: every replay against the oracle
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "combine"])
-def test_layer_graph_replay_matches_oracle(fused):
+@pytest.mark.parametrize("packed", [False, True], ids=["stored", "packed"])
+def test_layer_graph_replay_matches_oracle(fused, packed):
     # every step of the layer is a kernel of the library (zeroing included), so the whole call
-    # can be captured once and replayed; eager work runs between the replays
+    # can be captured once and replayed; eager work runs between the replays.  ``packed``: the
+    # expert weights and the router weight in their packed layouts (the benchmark's configuration)
     cfg = LayerConfig("graph", T=64, H=512, E=32, k=4, I=256, seed=601, w_std=0.05)
     inp = host_inputs(cfg)
     dev = L.to_device(inp)
+    if packed:
+        L.pack_weights(dev)
+        L.pack_router(dev)
+        assert dev.get("packed") and dev.get("w_router_packed") is not None
     bufs = L.LayerBuffers(cfg, fused=fused)
     r = O.layer(inp)
     s = torch.cuda.Stream()
@@ -408,7 +414,7 @@ def test_layer_graph_replay_matches_oracle(fused):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(bufs.topk_ids.cpu().numpy(), r["topk_ids"]), f"replay {rep}"
-        check_y(bufs.y.cpu().numpy(), r["y"], f"graph replay {rep} fused={fused}")
+        check_y(bufs.y.cpu().numpy(), r["y"], f"graph replay {rep} fused={fused} packed={packed}")
         junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between the replays
         torch.cuda.synchronize()
         del junk
