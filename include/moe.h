@@ -13,7 +13,8 @@
  * plus moe_route_dispatch (the first two calls of a decode batch in one
  * launch), moe_shared_expert (an always-active expert added to y), the W8A8
  * MXFP8 variant of the expert FFN (moe_quantize_mx, moe_grouped_ffn_mx) and
- * moe_pack_weights (a one-time reordering of resident weights for faster reads).
+ * moe_pack_weights / moe_pack_router (one-time reorderings of resident expert
+ * and router weights for faster reads).
  *
  * The method follows three pages: "AI-infra book, ch. 9 Distributed inference"
  * (section 9.3.4, Fig. 9-16: route, group rows by expert, expert GEMMs, weighted
