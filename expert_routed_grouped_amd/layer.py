@@ -65,9 +65,18 @@ def pack_router(dev: dict) -> dict:
     """Add the router weight in the layout of moe_pack_router (exact fp32, [H/4, E, 4]) as
     ``dev["w_router_packed"]``; decode-sized batches (moe_route_dispatch) then read it.  Done once,
     like loading the weights; routing is bit-identical."""
-    if dev.get("w_router_packed") is None and dev["w_router"].shape[1] % 4 == 0:
-        dev["w_router_packed"] = moe.moe_pack_router(dev["w_router"])
+    w = dev["w_router"]
+    if w.shape[1] % 4 == 0 and (dev.get("w_router_packed") is None or not _router_pack_current(dev)):
+        dev["w_router_packed"] = moe.moe_pack_router(w)
+        dev["w_router_packed_src"] = (w.data_ptr(), w._version)
     return dev
+
+
+def _router_pack_current(dev: dict) -> bool:
+    """True while ``w_router_packed`` was made from the present ``w_router`` tensor, unmodified since
+    (same storage, same in-place version counter)."""
+    w = dev["w_router"]
+    return dev.get("w_router_packed_src") == (w.data_ptr(), w._version)
 
 
 class LayerBuffers:
@@ -106,6 +115,8 @@ def run_layer(dev: dict, bufs: LayerBuffers, stream=None) -> torch.Tensor:
     packed = bool(dev.get("packed", False))
     if bufs.rd_ws is not None:  # one launch: route, dispatch and (fused combine) the zeroing of y
         wp = dev.get("w_router_packed")
+        if wp is not None and not _router_pack_current(dev):  # w_router replaced or edited: pack again
+            wp = pack_router(dev)["w_router_packed"]
         moe.moe_route_dispatch(dev["x"], dev["w_router"] if wp is None else wp, dev["bias"], cfg.k, cfg.E, cfg.lo,
                                cfg.hi, bufs.rd_ws, bufs.topk_ids, bufs.topk_w, p,
                                y_zero=bufs.y if bufs.fused else None, router_packed=wp is not None, stream=stream)

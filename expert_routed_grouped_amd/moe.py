@@ -308,8 +308,17 @@ def moe_route_dispatch(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[t
                        out: dict, y_zero: Optional[torch.Tensor] = None, router_packed: bool = False,
                        stream=None) -> dict:
     """Route + local dispatch of a decode batch in one launch; ``out`` holds counts, offsets,
-    row_token, row_w, token_row (as from moe_permute); zeroes ``y_zero`` when given."""
+    row_token, row_w, token_row (as from moe_permute); zeroes ``y_zero`` when given.
+    ``router_packed``: ``w_router`` is the fp32 [H/4, E, 4] tensor of moe_pack_router (the C ABI
+    cannot see buffer sizes, so the layout is checked here: a raw [E, H] weight passed as packed
+    would be read past its end)."""
     T, H = x.shape
+    if router_packed:
+        if w_router.dtype != torch.float32 or tuple(w_router.shape) != (H // 4, E, 4) or H % 4 != 0:
+            raise ValueError(f"router_packed needs the fp32 [H/4, E, 4] = {(H // 4, E, 4)} tensor of moe_pack_router, "
+                             f"got {w_router.dtype} {tuple(w_router.shape)}")
+    elif tuple(w_router.shape) != (E, H):
+        raise ValueError(f"w_router must be [E, H] = {(E, H)}, got {tuple(w_router.shape)}")
     _check("moe_route_dispatch", lib().moe_route_dispatch(
         _ptr(x), _dtype(x), _ptr(w_router), MOE_F32_ROUTER_PACKED if router_packed else _dtype(w_router), _ptr(bias),
         T, H, E, k, e_begin, e_end, _ptr(topk_ids),

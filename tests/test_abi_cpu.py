@@ -223,3 +223,36 @@ def test_binding_rejects_host_and_strided_tensors():
         moe.moe_route(x, wr, None, 2, torch.zeros((4, 2), dtype=torch.int32), torch.zeros((4, 2)))
     with pytest.raises(ValueError, match="contiguous"):
         moe.moe_quantize_mx(torch.zeros((64, 64)).t())
+
+
+def test_binding_checks_packed_router_layout():
+    # the C ABI cannot see buffer sizes: a raw [E, H] bf16 weight passed as packed fp32 would be read
+    # past its end, so the binding checks the moe_pack_router layout before calling the library
+    T, H, E, k = 4, 64, 8, 2
+    x = torch.zeros((T, H), dtype=torch.bfloat16)
+    out = {}
+    ids, gw = torch.zeros((T, k), dtype=torch.int32), torch.zeros((T, k))
+    for bad in (torch.zeros((E, H), dtype=torch.bfloat16), torch.zeros((H // 4, E, 4), dtype=torch.bfloat16),
+                torch.zeros((H // 4, E + 1, 4))):
+        with pytest.raises(ValueError, match="moe_pack_router"):
+            moe.moe_route_dispatch(x, bad, None, k, E, 0, E, None, ids, gw, out, router_packed=True)
+    with pytest.raises(ValueError, match=r"\[E, H\]"):
+        moe.moe_route_dispatch(x, torch.zeros((H // 4, E, 4)), None, k, E, 0, E, None, ids, gw, out)
+
+
+def test_layer_repacks_router_after_the_weight_changes(monkeypatch):
+    # layer.pack_router records which tensor (and which in-place version of it) the packed copy came
+    # from; a replaced or edited router weight is packed again instead of routing with stale values
+    from expert_routed_grouped_amd import layer as L
+    calls = []
+    monkeypatch.setattr(moe, "moe_pack_router", lambda w: calls.append(w) or ("packed", w.clone()))
+    dev = {"w_router": torch.zeros((8, 64))}
+    L.pack_router(dev)
+    L.pack_router(dev)
+    assert len(calls) == 1 and L._router_pack_current(dev)
+    dev["w_router"].add_(1.0)  # edited in place
+    assert not L._router_pack_current(dev)
+    L.pack_router(dev)
+    assert len(calls) == 2 and L._router_pack_current(dev)
+    dev["w_router"] = torch.ones((8, 64))  # replaced
+    assert not L._router_pack_current(dev)
