@@ -160,10 +160,36 @@ void oracle_mx_quantize(const void *x, int x_dt, int rows, int K, uint8_t *codes
     }
 }
 
-/* Exact value of MX element i of a row: code * 2^(scale of its block - 127). */
-static double mx_elem(const uint8_t *codes, const uint8_t *scales, size_t row, int K, int i)
+/* The 256 e4m3 values, filled once from oracle_e4m3_value (call it outside parallel regions). */
+static double e4m3_tab[256];
+static int e4m3_tab_ready = 0;
+
+static const double *e4m3_table(void)
 {
-    return ldexp(oracle_e4m3_value(codes[row * (size_t)K + i]), (int)scales[row * (size_t)(K / 32) + i / 32] - 127);
+    if (!e4m3_tab_ready) {
+        for (int c = 0; c < 256; c++)
+            e4m3_tab[c] = oracle_e4m3_value((uint8_t)c);
+        e4m3_tab_ready = 1;
+    }
+    return e4m3_tab;
+}
+
+/* Dot product of an exact fp64 vector a[0..K-1] with MX row ``row`` (codes [.., K], scales
+ * [.., K/32]): element i of the row is code * 2^(scale of its block - 127), formed exactly (the
+ * product of an e4m3 value and a power of two in [2^-127, 2^127] is exact in fp64), and the
+ * products are summed for i ascending. */
+static double mx_row_dot(const double *a, const uint8_t *codes, const uint8_t *scales, size_t row, int K,
+                         const double *tab)
+{
+    const uint8_t *q = codes + row * (size_t)K;
+    const uint8_t *sc = scales + row * (size_t)(K / 32);
+    double acc = 0.0;
+    for (int b = 0; b < K / 32; b++) {
+        const double f = ldexp(1.0, (int)sc[b] - 127);
+        for (int i = 32 * b; i < 32 * b + 32; i++)
+            acc += a[i] * (tab[q[i]] * f);
+    }
+    return acc;
 }
 
 static double elem(const void *p, int dt, size_t i)
@@ -362,6 +388,7 @@ void oracle_layer_tokens_mx(const int32_t *tokens, int n_tok, const void *x, int
                             int e_begin, int e_end, int I, const uint8_t *wgu_q, const uint8_t *wgu_s,
                             const uint8_t *wd_q, const uint8_t *wd_s, float *y_out)
 {
+    const double *tab = e4m3_table();
 #pragma omp parallel
     {
         double *yacc = (double *)malloc(sizeof(double) * (size_t)H);
@@ -389,12 +416,8 @@ void oracle_layer_tokens_mx(const int32_t *tokens, int n_tok, const void *x, int
                 size_t le = (size_t)(e - e_begin);
                 double g = (double)topk_w[(size_t)t * k + j];
                 for (int i = 0; i < I; i++) {
-                    double G = 0.0, U = 0.0;
-                    size_t rg = le * 2 * I + i, ru = le * 2 * I + I + i;
-                    for (int h = 0; h < H; h++) {
-                        G += xq[h] * mx_elem(wgu_q, wgu_s, rg, H, h);
-                        U += xq[h] * mx_elem(wgu_q, wgu_s, ru, H, h);
-                    }
+                    double G = mx_row_dot(xq, wgu_q, wgu_s, le * 2 * I + i, H, tab);
+                    double U = mx_row_dot(xq, wgu_q, wgu_s, le * 2 * I + I + i, H, tab);
                     hv[i] = (double)(float)(G / (1.0 + exp(-G)) * U);
                 }
                 for (int b = 0; b < I / 32; b++) {
@@ -402,13 +425,8 @@ void oracle_layer_tokens_mx(const int32_t *tokens, int n_tok, const void *x, int
                     for (int i = 0; i < 32; i++)
                         hq[32 * b + i] = ldexp(oracle_e4m3_value(codes[i]), (int)sb - 127);
                 }
-                for (int n = 0; n < H; n++) {
-                    double o = 0.0;
-                    size_t rd = le * H + n;
-                    for (int i = 0; i < I; i++)
-                        o += hq[i] * mx_elem(wd_q, wd_s, rd, I, i);
-                    yacc[n] += g * o;
-                }
+                for (int n = 0; n < H; n++)
+                    yacc[n] += g * mx_row_dot(hq, wd_q, wd_s, le * H + n, I, tab);
             }
             for (int n = 0; n < H; n++)
                 y_out[(size_t)q * H + n] = (float)yacc[n];
@@ -427,6 +445,7 @@ void oracle_layer_tokens_mx(const int32_t *tokens, int n_tok, const void *x, int
 void oracle_h_mx(const int32_t *row_token, const int32_t *row_expert, int R, const void *x, int x_dt, int H, int I,
                  const uint8_t *wgu_q, const uint8_t *wgu_s, uint8_t *h_codes, uint8_t *h_scales)
 {
+    const double *tab = e4m3_table();
 #pragma omp parallel
     {
         double *xq = (double *)malloc(sizeof(double) * (size_t)H);
@@ -445,12 +464,8 @@ void oracle_h_mx(const int32_t *row_token, const int32_t *row_expert, int R, con
                     xq[32 * b + i] = ldexp(oracle_e4m3_value(codes[i]), (int)sb - 127);
             }
             for (int i = 0; i < I; i++) {
-                double G = 0.0, U = 0.0;
-                size_t rg = le * 2 * I + i, ru = le * 2 * I + I + i;
-                for (int h = 0; h < H; h++) {
-                    G += xq[h] * mx_elem(wgu_q, wgu_s, rg, H, h);
-                    U += xq[h] * mx_elem(wgu_q, wgu_s, ru, H, h);
-                }
+                double G = mx_row_dot(xq, wgu_q, wgu_s, le * 2 * I + i, H, tab);
+                double U = mx_row_dot(xq, wgu_q, wgu_s, le * 2 * I + I + i, H, tab);
                 hv[i] = (double)(float)(G / (1.0 + exp(-G)) * U);
             }
             for (int b = 0; b < I / 32; b++)

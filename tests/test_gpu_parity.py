@@ -2,10 +2,9 @@
 
 Routing ids, counts, offsets, the permutation and x_perm must match bit for
 bit; gates within 1e-6; layer outputs within max|err| <= 1e-2 * RMS(oracle).
-Small shapes are compared element by element on every token; the full
-workload shapes (decode, prefill, skewed prefill, EP share) run in the launch
-configuration the benchmark times and are compared on sampled tokens, whose
-oracle rows are computed one token at a time.
+Small shapes and the full workload shapes (decode, prefill, skewed prefill, EP
+share, MXFP8, shared expert), the latter in the launch configuration the
+benchmark times, are compared element by element on every token.
 """
 import functools
 import sys
@@ -421,28 +420,34 @@ def test_layer_graph_replay_matches_oracle(fused, packed):
 
 
 # ----------------------------------------------------------------------------
-# full workload shapes, benchmark launch configuration, sampled tokens
+# full workload shapes, benchmark launch configuration, every output row
 # ----------------------------------------------------------------------------
-def sample_tokens(cfg, ids, n=24):
-    rng = np.random.default_rng(cfg.seed + 77)
-    pick = {0, cfg.T - 1}
-    counts = np.bincount(ids.ravel(), minlength=cfg.E)
-    local = [e for e in range(cfg.lo, cfg.hi) if counts[e] > 0]
-    hot = max(local, key=lambda e: counts[e])
-    cold = min(local, key=lambda e: counts[e])
-    for e in (hot, cold):
-        toks = np.nonzero(np.any(ids == e, axis=1))[0]
-        pick.update(int(t) for t in (toks[0], toks[-1]))
-    pick.update(int(t) for t in rng.choice(cfg.T, size=n, replace=False))
-    return np.array(sorted(pick), dtype=np.int32)
+@functools.lru_cache(maxsize=None)
+def oracle_full_y(name):
+    """The oracle's y for every token of a full workload (token-major, all host cores), computed
+    once per workload and shared by the row-major and packed-weight runs."""
+    cfg = CONFIGS[name]
+    inp = host_inputs(cfg)
+    ids, w = oracle_routing(cfg)
+    toks = np.arange(cfg.T, dtype=np.int32)
+    say(f"full layer {name}: oracle on all {cfg.T} tokens ({O.num_threads()} threads)")
+    y = O.layer_tokens(toks, inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"], inp["s_gate_up"],
+                       inp["s_down"])
+    if cfg.I_s > 0:
+        y = (y.astype(np.float64) + O.shared_tokens(toks, inp["x"], inp["ws_gate_up"], inp["ws_down"],
+                                                     inp["ss_gate_up"], inp["ss_down"])).astype(np.float32)
+    return y
 
 
 FULL_CASES = [(n, False) for n in ["decode", "prefill", "skew", "ep_share", "decode_shared", "prefill_shared"]]
-FULL_CASES += [(n, True) for n in ["decode", "prefill", "ep_share", "decode_shared"]]
+FULL_CASES += [(n, True) for n in ["decode", "prefill", "skew", "ep_share", "decode_shared", "prefill_shared"]]
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name,packed", FULL_CASES, ids=[f"{n}{'_packed' if p else ''}" for n, p in FULL_CASES])
 def test_full_workload_layer(name, packed):
+    """The layer as the benchmark launches it (same kernels, grid and tile walk), compared with the
+    oracle on every one of the T x H outputs."""
     cfg = CONFIGS[name]
     inp = host_inputs(cfg)
     say(f"full layer {name}: generating / uploading")
@@ -450,6 +455,8 @@ def test_full_workload_layer(name, packed):
     if packed:
         L.pack_weights(dev)
     bufs = L.LayerBuffers(cfg)
+    if bufs.rd_ws is not None and packed:
+        L.pack_router(dev)
     say(f"full layer {name}: run_layer fused={bufs.fused} R_cap={bufs.R_cap} packed={packed}")
     y = L.run_layer(dev, bufs)
     torch.cuda.synchronize()
@@ -458,18 +465,13 @@ def test_full_workload_layer(name, packed):
     assert np.max(np.abs(bufs.topk_w.cpu().numpy() - w)) <= GATE_TOL
     p_or = O.permute(ids, w, cfg.lo, cfg.hi)
     check_permutation(bufs.perm, p_or, cfg.T, cfg.k, same_gates=False)
-    toks = sample_tokens(cfg, ids)
-    say(f"full layer {name}: oracle on {len(toks)} sampled tokens")
-    y_o = O.layer_tokens(toks, inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"], inp["s_gate_up"],
-                         inp["s_down"])
-    if cfg.I_s > 0:
-        y_o = y_o.astype(np.float64) + O.shared_tokens(toks, inp["x"], inp["ws_gate_up"], inp["ws_down"],
-                                                       inp["ss_gate_up"], inp["ss_down"])
+    y_o = oracle_full_y(name)
     yg = y.cpu().numpy()
-    check_y(yg[toks], y_o, name)
+    say(f"full layer {name}: comparing all {cfg.T} rows x {cfg.H} columns")
+    check_y(yg, y_o, name)
     # a second call reuses the buffers and gives the same routing and (up to atomic order) the same y
     y2 = L.run_layer(dev, bufs).cpu().numpy()
-    check_y(y2[toks], y_o, name + " (repeat)")
+    check_y(y2, y_o, name + " (repeat)")
     del dev, bufs
     torch.cuda.empty_cache()
 
@@ -721,6 +723,23 @@ def h_exact_and_slack(inp, t, e, cols, I, H):
     return h, slack
 
 
+@functools.lru_cache(maxsize=None)
+def oracle_full_mx(name):
+    """Oracle MX intermediate of every assignment row and y of every token of a full MXFP8
+    workload, computed once and shared by its row-major and packed-weight runs."""
+    cfg = CONFIGS[name]
+    inp = host_inputs(cfg)
+    ids, w = oracle_routing(cfg)
+    perm = O.permute(ids, w, cfg.lo, cfg.hi)
+    row_exp = np.repeat(np.arange(cfg.E_loc, dtype=np.int32), perm["counts"])
+    say(f"  {name}: oracle MX intermediate of all {perm['R']} rows and y of all {cfg.T} tokens "
+        f"({O.num_threads()} threads)")
+    hq, hs = O.h_mx(perm["row_token"], row_exp, inp["x"], inp["w_gate_up"], inp["s_gate_up"])
+    y = O.layer_tokens_mx(np.arange(cfg.T), inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["s_gate_up"],
+                          inp["w_down"], inp["s_down"])
+    return hq, hs, y
+
+
 def check_mx_layer(cfg, inp, ids, w, y, h_gpu, tokens=None):
     """MX parity.  h is the quantisation of an fp32 value whose last bits depend on the order
     of the fp32 accumulation, so a GPU code may differ from the oracle's where the exact h lies
@@ -737,7 +756,11 @@ def check_mx_layer(cfg, inp, ids, w, y, h_gpu, tokens=None):
     row_tok = perm["row_token"]
     row_exp = np.repeat(np.arange(cfg.E_loc, dtype=np.int32), counts)
     sel = np.arange(R) if tokens is None else np.nonzero(np.isin(row_tok, tokens))[0]
-    hq_o, hs_o = O.h_mx(row_tok[sel], row_exp[sel], inp["x"], inp["w_gate_up"], inp["s_gate_up"])
+    if tokens is None and CONFIGS.get(cfg.name) == cfg:
+        hq_o, hs_o, y_full = oracle_full_mx(cfg.name)
+    else:
+        hq_o, hs_o = O.h_mx(row_tok[sel], row_exp[sel], inp["x"], inp["w_gate_up"], inp["s_gate_up"])
+        y_full = None
     hq_g, hs_g = h_gpu[0][sel], h_gpu[1][sel]
     sc_o = np.repeat(hs_o.astype(np.int64), 32, axis=1) - 127
     sc_g = np.repeat(hs_g.astype(np.int64), 32, axis=1) - 127
@@ -774,8 +797,9 @@ def check_mx_layer(cfg, inp, ids, w, y, h_gpu, tokens=None):
     assert worst <= 1.0, "an h value differs where fp32 rounding cannot explain it"
     # y: oracle rows, tolerance widened only by the differing h values of each token
     toks = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
-    y_o = O.layer_tokens_mx(toks, inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["s_gate_up"],
-                            inp["w_down"], inp["s_down"])
+    y_o = y_full if y_full is not None else O.layer_tokens_mx(toks, inp["x"], ids, w, cfg.lo, cfg.hi,
+                                                              inp["w_gate_up"], inp["s_gate_up"], inp["w_down"],
+                                                              inp["s_down"])
     rms = np.sqrt(np.mean(y_o.astype(np.float64) ** 2))
     bound = np.full(len(toks), Y_TOL * rms)
     pos = {int(t): n for n, t in enumerate(toks)}
@@ -861,19 +885,23 @@ def test_mx_packed_weights_bit_identical(cfg):
     check_mx_layer(cfg, inp, ids, w, y, h)
 
 
-@pytest.mark.parametrize("name,fused", [("prefill_mx", False), ("decode_mx", True), ("decode_mx", False)])
-def test_full_workload_layer_mx(name, fused):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,fused,packed", [("prefill_mx", False, False), ("prefill_mx", False, True),
+                                               ("decode_mx", True, False), ("decode_mx", False, False),
+                                               ("decode_mx", True, True)])
+def test_full_workload_layer_mx(name, fused, packed):
+    """Full MXFP8 workloads in the benchmark's launch configuration: every assignment row's MX
+    intermediate and every token's output row against the oracle."""
     cfg = CONFIGS[name]
     ids, w = oracle_routing(cfg)
-    toks = sample_tokens(cfg, ids)
-    used = sorted(set(int(e) for e in ids[toks].ravel()))
-    inp = synth.make_inputs(cfg)
-    dev = mx_dev(inp)
-    say(f"full MX layer {cfg.name}: T={cfg.T}, sampled tokens {toks.tolist()}")
+    inp = host_inputs(cfg)
+    dev = mx_dev(inp)  # mx_layer packs the weight codes itself when ``packed``
+    say(f"full MX layer {cfg.name}: T={cfg.T}, fused={fused}, packed={packed}, all rows")
     ids_d, w_d = to_dev_routing(ids, w)
-    y, p, h = mx_layer(dev, cfg, ids_d, w_d, fused=fused)
-    assert len(used) > 0
-    check_mx_layer(cfg, inp, ids, w, y, h, tokens=toks)
+    y, p, h = mx_layer(dev, cfg, ids_d, w_d, fused=fused, packed=packed)
+    del dev
+    torch.cuda.empty_cache()
+    check_mx_layer(cfg, inp, ids, w, y, h)
 
 
 # ----------------------------------------------------------------------------

@@ -48,8 +48,14 @@ MUTANTS = {
                            "xq[32 * b + i] = xv[32 * b + i];"),
     "mx_h_not_quantised": ("hq[32 * b + i] = ldexp(oracle_e4m3_value(codes[i]), (int)sb - 127);",
                            "hq[32 * b + i] = hv[32 * b + i];"),
-    "mx_weight_scale_wrong_block": ("return ldexp(oracle_e4m3_value(codes[row * (size_t)K + i]), (int)scales[row * (size_t)(K / 32) + i / 32] - 127);",
-                                    "return ldexp(oracle_e4m3_value(codes[row * (size_t)K + i]), (int)scales[row * (size_t)(K / 32) + (i / 32 + 1) % (K / 32)] - 127);"),
+    "mx_weight_scale_wrong_block": ("const double f = ldexp(1.0, (int)sc[b] - 127);",
+                                    "const double f = ldexp(1.0, (int)sc[(b + 1) % (K / 32)] - 127);"),
+    "mx_weight_scale_bias_126": ("const double f = ldexp(1.0, (int)sc[b] - 127);",
+                                 "const double f = ldexp(1.0, (int)sc[b] - 126);"),
+    "mx_table_drops_subnormals": ("e4m3_tab[c] = oracle_e4m3_value((uint8_t)c);",
+                                  "e4m3_tab[c] = (c & 0x78) ? oracle_e4m3_value((uint8_t)c) : 0.0;"),
+    "mx_weight_row_misread": ("const uint8_t *q = codes + row * (size_t)K;",
+                              "const uint8_t *q = codes + (row ^ 1) * (size_t)K;"),
     "shared_up_rows_misplaced": ("size_t rg = (size_t)i * H, ru = (size_t)(I_s + i) * H;",
                                  "size_t rg = (size_t)i * H, ru = (size_t)(I_s / 2 + i) * H;"),
     "shared_silu_dropped": ("float hf = (float)(G / (1.0 + exp(-G)) * U);", "float hf = (float)(G * U);"),
