@@ -1,24 +1,38 @@
 #!/usr/bin/env python3
 """Benchmark of one MoE FFN layer step on one MI355X.
 
-A step is the whole hot path on one batch already resident in HBM:
-moe_route -> moe_permute -> moe_grouped_ffn (gate/up half, down half with the
-combine) [-> moe_combine for large batches].  Default workload: the decode
-layer (T=64 tokens, top-8 of 128 experts, H=4096, I=1536, bf16), which is
-weight-load bound; ``--config prefill`` times the 6000-token prefill layer
-(matrix-core bound).
+A step is the whole hot path on one batch already resident in HBM: routing
+(router GEMM, top-k, renormalised gates), the grouping of assignments by
+expert, the SwiGLU grouped GEMMs (gate/up, then down with the combine) and,
+for large batches, the standalone combine.
 
-Prints ONE JSON line.  ``roofline`` covers the dominant kernel (the gate/up
-grouped GEMM): its algorithmic bytes (decode) or FLOPs (prefill) per launch
-over its average duration, measured with HIP events on the stream the library
-launches on.  ``cpu_baseline`` is the CPU oracle timed on this host on a
-bounded sample of the same workload.
+The default run measures both halves of the headline metric in one process:
+
+* ``decode`` (the headline ``value``): T=64 tokens x top-8 of 128 experts,
+  H=4096, I=1536, bf16 -- weight-load bound, reported against HBM bandwidth.
+  Each of the K timed steps follows a 1 GiB write that evicts the L2 and the
+  Infinity Cache (the weights of a real model come from HBM, other layers ran
+  in between); the warm back-to-back rate is reported beside it.
+* ``prefill`` (the ``prefill`` object): T=6000 tokens, same layer -- matrix-core
+  bound, reported against the bf16 MFMA peak, for the gate/up kernel and for
+  the whole layer.
+
+``--config NAME`` measures one workload alone (the other workloads are parity
+and reporting cases: skew, ep_share, prefill_mx, decode_mx, decode_shared,
+prefill_shared).
+
+Prints ONE JSON line.  ``roofline`` covers the dominant kernel of the headline
+workload: its algorithmic bytes (decode) or FLOPs (prefill) per launch over its
+average duration, measured with HIP events on the stream the library launches
+on.  ``cpu_baseline`` is the CPU oracle timed on this host on a bounded sample
+of the headline workload.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -31,6 +45,7 @@ METRIC = "MoE-layer tokens/sec + % bf16 MFMA peak (prefill) / % HBM BW (decode)"
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix cores
+FLUSH_BYTES = 1 << 30       # written before each flushed step: more than the L2s and the Infinity Cache hold
 WORKLOADS = {
     "decode": "decode MoE layer: T=64 tokens x top-8 of E=128 experts (512 assignments), H=4096, SwiGLU I=1536, bf16",
     "prefill": "prefill MoE layer: T=6000 tokens x top-8 of E=128 experts, H=4096, SwiGLU I=1536, bf16",
@@ -49,20 +64,36 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="default", choices=["default"] + sorted(WORKLOADS),
+                    help="default: decode (headline) and prefill in one run; otherwise one workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time budget of the oracle sample")
-    ap.add_argument("--flush-steps", type=int, default=20,
-                    help="extra steps, each after writing a 1 GiB scratch buffer (cold L2 and Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="time warm back-to-back steps only (no cache-flushing write before each step)")
     ap.add_argument("--router", default="packed", choices=["packed", "as-stored"],
                     help="decode-sized batches: read the router weight in the layout of moe_pack_router (exact "
                          "fp32, packed once before timing; routing is bit-identical)")
     ap.add_argument("--weights", default="packed", choices=["packed", "row-major"],
                     help="layout of the resident bf16/fp8 expert weights (packed once with moe_pack_weights "
-                         "before timing; MXFP8 and fp32 weights are always row-major)")
+                         "before timing)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def say(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
 def measured_traffic(kernel, workload, weights):
@@ -138,11 +169,231 @@ def cpu_baseline(inp, cfg, seconds):
         dt = td - t0
         if dt >= seconds:
             break
-    return {"value": done / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{done} tokens in {chunk}-token chunks of the same {cfg.T}-token batch (wrapping around), "
-                      f"whole layer per chunk (route, permute, token-major SwiGLU FFN + combine"
+    return {"value": round(done / dt, 2), "unit": "tokens/s", "cores": O.num_threads(), "cpu_model": cpu_model(),
+            "kind": "oracle",
+            "sample": f"{done} tokens of the {cfg.name} workload in {chunk}-token chunks of its {cfg.T}-token batch "
+                      f"(wrapping around), whole layer per chunk (route, permute, token-major SwiGLU FFN + combine"
                       f"{' + shared expert' if cfg.I_s > 0 else ''}), {dt:.1f} s",
             "stage_tokens_per_s": {k: round(done / v, 1) if v > 0 else None for k, v in stage.items()}}
+
+
+def stats(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p50": round(float(np.median(a)), 4), "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+class Workload:
+    """One workload's resident inputs, buffers and the step as a list of phases (each a few library
+    calls on one stream), so that HIP events between phases time each kernel group."""
+
+    def __init__(self, name, args):
+        import torch
+        from expert_routed_grouped_amd import layer as L
+        from expert_routed_grouped_amd import moe, synth
+        self.name = name
+        cfg = self.cfg = synth.CONFIGS[name]
+        say(f"generating {name} inputs")
+        self.inp = synth.make_inputs(cfg)
+        dev = self.dev = L.to_device(self.inp)
+        if args.weights == "packed":
+            L.pack_weights(dev)  # one-time layout change of the resident weights, like loading them
+        self.packed = bool(dev.get("packed", False))
+        bufs = self.bufs = L.LayerBuffers(cfg)
+        if bufs.rd_ws is not None and args.router == "packed":
+            L.pack_router(dev)  # one-time layout change of the resident router weight
+        self.wrp = dev.get("w_router_packed") if bufs.rd_ws is not None else None
+        self.stream = torch.cuda.current_stream()
+        self.mx = cfg.wdt == "mxfp8"
+        if self.mx:  # activations quantised on the fly into these, h lives in the MX workspace
+            self.xq = torch.empty((cfg.T, cfg.H), dtype=torch.uint8, device="cuda")
+            self.xs = torch.empty((cfg.T, cfg.H // 32), dtype=torch.uint8, device="cuda")
+            bufs.workspace = torch.empty(moe.moe_ffn_mx_workspace_size(bufs.R_cap, cfg.I), dtype=torch.uint8,
+                                         device="cuda")
+        self.moe = moe
+        self.phases = [("route", self.route), ("gate_up", lambda: self.ffn_half("gate_up")),
+                       ("down", self.down)]
+
+    def route(self):
+        moe, cfg, bufs, dev, p, s = self.moe, self.cfg, self.bufs, self.dev, self.bufs.perm, self.stream
+        if bufs.rd_ws is not None:  # decode: route + dispatch (+ zeroing of y) in one launch
+            moe.moe_route_dispatch(dev["x"], dev["w_router"] if self.wrp is None else self.wrp, dev["bias"], cfg.k,
+                                   cfg.E, cfg.lo, cfg.hi, bufs.rd_ws, bufs.topk_ids, bufs.topk_w, p,
+                                   y_zero=bufs.y if bufs.fused else None, router_packed=self.wrp is not None,
+                                   stream=s)
+        else:
+            moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=s)
+            moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=p, stream=s)
+        if self.mx:
+            moe.moe_quantize_mx(dev["x"], self.xq, self.xs, stream=s)
+
+    def ffn_half(self, phase):
+        moe, cfg, bufs, dev, p = self.moe, self.cfg, self.bufs, self.dev, self.bufs.perm
+        common = dict(workspace=bufs.workspace, gather=True, stream=self.stream, phase=phase, packed=self.packed)
+        outs = (dict(y=bufs.y, zero_y=bufs.rd_ws is None) if bufs.fused else dict(y_perm=bufs.y_perm, zero_y=False))
+        if self.mx:
+            moe.moe_grouped_ffn_mx(self.xq, self.xs, p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
+                                   dev["w_gate_up"], dev["s_gate_up"], dev["w_down"], dev["s_down"], **outs, **common)
+        else:
+            moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
+                                dev["w_gate_up"], dev["w_down"], dev["s_gate_up"], dev["s_down"], **outs, **common)
+
+    def down(self):
+        self.ffn_half("down")
+        if not self.bufs.fused:
+            self.moe.moe_combine(self.bufs.y_perm, self.bufs.perm["token_row"], self.bufs.topk_w, y=self.bufs.y,
+                                 stream=self.stream)
+        if self.bufs.shared_ws is not None:
+            self.shared()
+
+    def shared(self):
+        dev = self.dev
+        self.moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], self.bufs.y, dev.get("ss_gate_up"),
+                                   dev.get("ss_down"), workspace=self.bufs.shared_ws, packed=self.packed,
+                                   stream=self.stream)
+
+    def step(self, ev=None):
+        if ev is not None:
+            ev[0].record(self.stream)
+        for i, (_, fn) in enumerate(self.phases):
+            fn()
+            if ev is not None:
+                ev[i + 1].record(self.stream)
+
+
+def measure(wl: Workload, args):
+    """W warm-up steps; K timed steps each after a cache-flushing write (HIP events around the step);
+    K warm back-to-back steps (HIP events, and the wall clock between two synchronisations)."""
+    import torch
+    from expert_routed_grouped_amd import accounting as A
+    cfg, bufs = wl.cfg, wl.bufs
+    T, H, I = cfg.T, cfg.H, cfg.I
+    nph = len(wl.phases)
+    say(f"{wl.name}: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)]
+
+    def phase_ms(evs):
+        return {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                for i, (name, _) in enumerate(wl.phases)}
+
+    flushed = None
+    if not args.no_flush:
+        say(f"{wl.name}: timing {args.steps} steps, each after a {FLUSH_BYTES >> 20} MiB cache-flushing write")
+        scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        fevs = [events() for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for i in range(args.steps):
+            scratch.fill_(0x5A)
+            wl.step(fevs[i])
+            torch.cuda.synchronize()
+        w1 = time.perf_counter()
+        del scratch
+        fl = [e[0].elapsed_time(e[nph]) for e in fevs]
+        flushed = {"ms": stats(fl), "phase_ms": {k: round(v, 4) for k, v in phase_ms(fevs).items()},
+                   "wall_ms_per_step_incl_flush_and_sync": round((w1 - w0) * 1e3 / args.steps, 4)}
+
+    say(f"{wl.name}: timing {args.steps} warm back-to-back steps")
+    wevs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wl.step(wevs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    warm_wall = (t1 - t0) * 1e3 / args.steps
+    warm = {"ms_per_step_wall": round(warm_wall, 4), "ms": stats([e[0].elapsed_time(e[nph]) for e in wevs]),
+            "phase_ms": {k: round(v, 4) for k, v in phase_ms(wevs).items()}}
+
+    shared_ms = None
+    if bufs.shared_ws is not None:  # the shared expert alone, on the same stream
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a, b in sev:
+            a.record(wl.stream)
+            wl.shared()
+            b.record(wl.stream)
+        torch.cuda.synchronize()
+        shared_ms = round(float(np.mean([a.elapsed_time(b) for a, b in sev])), 4)
+
+    counts = bufs.perm["counts"].cpu().numpy().astype(np.int64)
+    R = int(counts.sum())
+    U = int((counts > 0).sum())
+    mx = wl.mx
+    # MXFP8 tensors carry one E8M0 scale byte per 32 codes
+    wbytes = {"bf16": 2, "fp8": 1, "f32": 4, "mxfp8": 1 + 1 / 32}[cfg.wdt]
+    abytes = 4 if cfg.act == "f32" else 2
+    gu_abytes = 1 + 1 / 32 if mx else abytes   # x codes read, h codes written
+    scale_gu = 4 * 2 * I if cfg.wdt == "fp8" else 0
+    # gate/up half, algorithmic: each active expert's gate/up weights once, x read once, h written once
+    gu_bytes = int(U * (2 * I * H * wbytes + scale_gu) + T * H * gu_abytes + R * I * gu_abytes)
+    gu_flops = 4 * R * H * I
+    layer_flops = A.useful_flops(R, H, I) + A.router_flops(T, H, cfg.E)
+    # the router weight as the timed step reads it: the moe_pack_router copy is exact fp32
+    router_bytes = cfg.E * H * (4 if wl.wrp is not None else abytes)
+    layer_bytes = A.layer_hbm_bytes(counts, T, H, I, cfg.E, abytes, A.expert_bytes(H, I, wbytes, cfg.wdt == "fp8"),
+                                    router_bytes)
+    if cfg.I_s > 0:  # the shared expert: every token once, its weights once
+        layer_flops += A.useful_flops(T, H, cfg.I_s)
+        layer_bytes += A.expert_bytes(H, cfg.I_s, wbytes, cfg.wdt == "fp8")
+    # headline timing: the flushed steps (weights from HBM), else the warm ones
+    step_ms = flushed["ms"]["mean"] if flushed else warm["ms"]["mean"]
+    gu_ms = (flushed or warm)["phase_ms"]["gate_up"]
+    gu_s = gu_ms * 1e-3
+    hbm_bound = wl.name.startswith("decode")  # a few rows per expert: the weight stream bounds the kernel
+    peak_mfma = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+    if hbm_bound:
+        achieved = gu_bytes / gu_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        achieved = gu_flops / gu_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_mfma, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_mfma, 4), "traffic": None}
+    streaming = bufs.R_cap <= 48 * cfg.E_loc
+    kernel = (("ffn_mx_stream_kernel" if streaming else "ffn_mx_kernel") if mx else
+              ("ffn_stream_kernel" if streaming else
+               ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel")))
+    roof["traffic"] = measured_traffic(kernel, wl.name, "packed" if wl.packed else "row-major")
+    # rows the grouped GEMM actually multiplies, by the tiling of the kernel in use
+    padded = (A.padded_rows(counts, 64) if kernel == "ffn_stream_kernel" else
+              A.padded_rows(counts, 32 if bufs.R_cap <= 16 * cfg.E_loc else 64) if kernel == "ffn_mx_stream_kernel" else
+              (A.split_padded_rows(counts, 256, 64) if kernel == "ffn_dma_kernel" else
+               (A.split_padded_rows(counts, 192, 64) if kernel == "ffn_mx_kernel" else A.padded_rows(counts, 256))))
+    roof.update({"kernel": f"{kernel}<0> (gate/up + SwiGLU half, one launch)", "avg_ms": round(gu_ms, 4),
+                 "algorithmic_per_launch": gu_bytes if hbm_bound else gu_flops,
+                 "timing": "cache-flushed steps" if flushed else "warm steps"})
+    layer_s = step_ms * 1e-3
+    warm_s = warm["ms"]["mean"] * 1e-3
+    return {
+        "workload": WORKLOADS[wl.name], "name": wl.name, "T": T, "H": H, "E": cfg.E, "k": cfg.k, "I": I,
+        "local_experts": [cfg.lo, cfg.hi],
+        "tokens_per_s": round(T / layer_s, 1), "ms_per_step": round(step_ms, 4),
+        "timing": ("mean of K steps, each after a 1 GiB cache-flushing write, HIP events around the step"
+                   if flushed else "mean of K warm back-to-back steps, HIP events"),
+        "flushed": flushed, "warm": dict(warm, tokens_per_s=round(T / warm_s, 1)),
+        "roofline": roof,
+        "layer": {"hbm_bytes": int(layer_bytes), "hbm_frac": round(layer_bytes / layer_s / 1e9 / PEAK_HBM_GBS, 4),
+                  "hbm_frac_warm": round(layer_bytes / warm_s / 1e9 / PEAK_HBM_GBS, 4),
+                  "router_weight_bytes": int(router_bytes), "flops": int(layer_flops),
+                  "mfma_frac": round(layer_flops / layer_s / 1e12 / peak_mfma, 4),
+                  "mfma_frac_warm": round(layer_flops / warm_s / 1e12 / peak_mfma, 4),
+                  "shared_expert_ms": shared_ms},
+        "config": {"combine": "fused atomic epilogue" if bufs.fused else "per-row outputs + moe_combine",
+                   "dispatch": "route + dispatch in one launch" if bufs.rd_ws is not None else "moe_route + moe_permute",
+                   "weights": "packed 32x64 blocks (moe_pack_weights, once before timing)" if wl.packed else "row-major",
+                   "router_weight": ("fp32 [H/4, E, 4] (moe_pack_router, once before timing)" if wl.wrp is not None
+                                     else "as stored")},
+        "routing": {"assignments": R, "active_experts": U, "max_rows": int(counts.max()),
+                    "padded_rows": padded, "padded_over_R": round(padded / R, 4) if R else None,
+                    "skew": round(float(counts.max() / (R / max(len(counts), 1))), 3) if R else None},
+        "dtype": {"bf16": "bf16", "fp8": "fp8-weights/bf16", "mxfp8": "mxfp8 (e4m3 + e8m0 block scales)"}.get(
+            cfg.wdt, "f32"),
+    }
 
 
 def main():
@@ -155,199 +406,57 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
-    from expert_routed_grouped_amd import accounting as A
-    from expert_routed_grouped_amd import layer as L
-    from expert_routed_grouped_amd import moe, synth
 
-    cfg = synth.CONFIGS[args.config]
-    print(f"[bench] generating {args.config} inputs", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(cfg)
-    dev = L.to_device(inp)
-    if args.weights == "packed":
-        L.pack_weights(dev)  # one-time layout change of the resident weights, like loading them
-    packed = bool(dev.get("packed", False))
-    bufs = L.LayerBuffers(cfg)
-    if bufs.rd_ws is not None and args.router == "packed":
-        L.pack_router(dev)  # one-time layout change of the resident router weight
-    wrp = dev.get("w_router_packed") if bufs.rd_ws is not None else None
-    stream = torch.cuda.current_stream()
-    p = bufs.perm
-    mx = cfg.wdt == "mxfp8"
-    if mx:  # activations quantised on the fly into these, h lives in the MX workspace
-        xq = torch.empty((cfg.T, cfg.H), dtype=torch.uint8, device="cuda")
-        xs = torch.empty((cfg.T, cfg.H // 32), dtype=torch.uint8, device="cuda")
-        bufs.workspace = torch.empty(moe.moe_ffn_mx_workspace_size(bufs.R_cap, cfg.I), dtype=torch.uint8,
-                                     device="cuda")
-
-    def ffn_half(phase, outs, common):
-        if mx:
-            moe.moe_grouped_ffn_mx(xq, xs, p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
-                                   dev["w_gate_up"], dev["s_gate_up"], dev["w_down"], dev["s_down"], phase=phase,
-                                   packed=packed, **outs, **common)
-        else:
-            moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
-                                dev["w_gate_up"], dev["w_down"], dev["s_gate_up"], dev["s_down"], phase=phase,
-                                packed=packed, **outs, **common)
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        if bufs.rd_ws is not None:  # decode: route + dispatch (+ zeroing of y) in one launch
-            moe.moe_route_dispatch(dev["x"], dev["w_router"] if wrp is None else wrp, dev["bias"], cfg.k, cfg.E,
-                                   cfg.lo, cfg.hi, bufs.rd_ws, bufs.topk_ids, bufs.topk_w, p,
-                                   y_zero=bufs.y if bufs.fused else None, router_packed=wrp is not None,
-                                   stream=stream)
-        else:
-            moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=stream)
-            moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=p, stream=stream)
-        if mx:
-            moe.moe_quantize_mx(dev["x"], xq, xs, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        common = dict(workspace=bufs.workspace, gather=True, stream=stream)
-        outs = (dict(y=bufs.y, zero_y=bufs.rd_ws is None) if bufs.fused else dict(y_perm=bufs.y_perm, zero_y=False))
-        ffn_half("gate_up", outs, common)
-        if ev is not None:
-            ev[2].record(stream)
-        ffn_half("down", outs, common)
-        if not bufs.fused:
-            moe.moe_combine(bufs.y_perm, p["token_row"], bufs.topk_w, y=bufs.y, stream=stream)
-        if bufs.shared_ws is not None:
-            shared()
-        if ev is not None:
-            ev[3].record(stream)
-
-    def shared():
-        moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], bufs.y, dev.get("ss_gate_up"),
-                              dev.get("ss_down"), workspace=bufs.shared_ws, packed=packed, stream=stream)
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    layer_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
-    route_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    gu_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    down_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-
-    shared_ms = None
-    if bufs.shared_ws is not None:  # the shared expert alone, on the same stream
-        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-        for a, b in sev:
-            a.record(stream)
-            shared()
-            b.record(stream)
-        torch.cuda.synchronize()
-        shared_ms = float(np.mean([a.elapsed_time(b) for a, b in sev]))
-
-    flushed = None
-    if args.flush_steps > 0:
-        # each step after a 1 GiB write: the weights come from HBM, as when other layers ran in between
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        fl_ms = []
-        for _ in range(args.flush_steps):
-            scratch.fill_(0x5A)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            step(e)
-            torch.cuda.synchronize()
-            fl_ms.append(e[0].elapsed_time(e[3]))
-        del scratch
-        fl = np.array(fl_ms)
-        flushed = {"steps": args.flush_steps, "ms_p50": round(float(np.median(fl)), 4),
-                   "ms_p10": round(float(np.percentile(fl, 10)), 4), "ms_p90": round(float(np.percentile(fl, 90)), 4),
-                   "tokens_per_s_p50": round(cfg.T / (float(np.median(fl)) * 1e-3), 1)}
-
-    counts = p["counts"].cpu().numpy().astype(np.int64)
-    R = int(counts.sum())
-    U = int((counts > 0).sum())
-    H, I, T = cfg.H, cfg.I, cfg.T
-    # MXFP8 tensors carry one E8M0 scale byte per 32 codes
-    wbytes = {"bf16": 2, "fp8": 1, "f32": 4, "mxfp8": 1 + 1 / 32}[cfg.wdt]
-    abytes = 4 if cfg.act == "f32" else 2
-    gu_abytes = 1 + 1 / 32 if mx else abytes   # x codes read, h codes written
-    scale_gu = 4 * 2 * I if cfg.wdt == "fp8" else 0
-    # gate/up half, algorithmic: each active expert's gate/up weights once, x read once, h written once
-    gu_bytes = int(U * (2 * I * H * wbytes + scale_gu) + T * H * gu_abytes + R * I * gu_abytes)
-    gu_flops = 4 * R * H * I
-    layer_flops = A.useful_flops(R, H, I) + A.router_flops(T, H, cfg.E)
-    layer_bytes = A.layer_hbm_bytes(counts, T, H, I, cfg.E, abytes,
-                                    A.expert_bytes(H, I, wbytes, cfg.wdt == "fp8"), cfg.E * H * abytes)
-    if cfg.I_s > 0:  # the shared expert: every token once, its weights once
-        layer_flops += A.useful_flops(T, H, cfg.I_s)
-        layer_bytes += A.expert_bytes(H, cfg.I_s, wbytes, cfg.wdt == "fp8")
-    gu_s = float(np.mean(gu_ms)) * 1e-3
-    hbm_bound = args.config.startswith("decode")  # a few rows per expert: the weight stream bounds the kernel
-    if hbm_bound:
-        achieved = gu_bytes / gu_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    else:
-        achieved = gu_flops / gu_s / 1e12
-        peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None}
-    streaming = bufs.R_cap <= 48 * cfg.E_loc
-    kernel = (("ffn_mx_stream_kernel" if streaming else "ffn_mx_kernel") if mx else
-              ("ffn_stream_kernel" if streaming else
-               ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel")))
-    roof["traffic"] = measured_traffic(kernel, args.config, "packed" if packed else "row-major")
-    # rows the grouped GEMM actually multiplies, by the tiling of the kernel in use
-    padded = (A.padded_rows(counts, 64) if kernel == "ffn_stream_kernel" else
-              A.padded_rows(counts, 32 if bufs.R_cap <= 16 * cfg.E_loc else 64) if kernel == "ffn_mx_stream_kernel" else
-              (A.split_padded_rows(counts, 256, 64) if kernel == "ffn_dma_kernel" else
-               (A.split_padded_rows(counts, 192, 64) if kernel == "ffn_mx_kernel" else A.padded_rows(counts, 256))))
-    roof.update({"kernel": f"{kernel} (gate/up + SwiGLU half, one launch)", "avg_ms": round(float(np.mean(gu_ms)), 4),
-                 "algorithmic_per_launch": gu_bytes if hbm_bound else gu_flops})
-    layer_s = ms_per_step * 1e-3
+    head_name = "decode" if args.config == "default" else args.config
+    head = Workload(head_name, args)
+    h = measure(head, args)
+    cpu = None
+    if not args.no_cpu_baseline:
+        say("cpu baseline (oracle)")
+        cpu = cpu_baseline(head.inp, head.cfg, args.cpu_seconds)
+    pre = None
+    if args.config == "default":
+        del head
+        torch.cuda.empty_cache()
+        pre_wl = Workload("prefill", args)
+        p = measure(pre_wl, args)
+        del pre_wl
+        pre = {k: p[k] for k in ("workload", "tokens_per_s", "ms_per_step", "timing", "roofline", "layer", "warm",
+                                 "flushed", "routing", "config")}
+        pre["roofline_layer"] = {"bound": "mfma", "achieved": round(p["layer"]["flops"] / p["ms_per_step"] / 1e9, 1),
+                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": p["layer"]["mfma_frac"],
+                                 "flops_per_step": p["layer"]["flops"]}
     res = {
         "metric": METRIC,
-        "value": round(T / layer_s, 1),
+        "value": h["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8-weights/bf16", "mxfp8": "mxfp8 (e4m3 + e8m0 block scales)"}.get(cfg.wdt,
-                                                                                                            "f32"),
+        "dtype": h["dtype"],
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config], "T": T, "H": H, "E": cfg.E, "k": cfg.k, "I": I,
-                   "local_experts": [cfg.lo, cfg.hi], "parallelism": "none (one GPU)",
-                   "combine": "fused atomic epilogue" if bufs.fused else "per-row outputs + moe_combine",
-                   "dispatch": "route + dispatch in one launch" if bufs.rd_ws is not None else "moe_route + moe_permute",
-                   "weights": "packed 32x64 blocks (moe_pack_weights, once before timing)" if packed else "row-major",
-                   "router_weight": ("fp32 [H/4, E, 4] (moe_pack_router, once before timing)" if wrp is not None
-                                     else "as stored")},
-        "roofline": roof,
-        "layer": {"ms_p50": round(float(np.median(layer_ms)), 4), "ms_p10": round(float(np.percentile(layer_ms, 10)), 4),
-                  "ms_p90": round(float(np.percentile(layer_ms, 90)), 4),
-                  "route_permute_ms": round(float(np.mean(route_ms)), 4), "gate_up_ms": round(float(np.mean(gu_ms)), 4),
-                  "down_combine_ms": round(float(np.mean(down_ms)), 4),
-                  "shared_expert_ms": None if shared_ms is None else round(shared_ms, 4),
-                  "hbm_bytes": int(layer_bytes), "hbm_frac": round(layer_bytes / layer_s / 1e9 / PEAK_HBM_GBS, 4),
-                  "flops": int(layer_flops),
-                  "mfma_frac": round(layer_flops / layer_s / 1e12 / (PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS), 4)},
-        "flushed_caches": flushed,
-        "routing": {"assignments": R, "active_experts": U, "max_rows": int(counts.max()),
-                    "padded_rows": padded, "padded_over_R": round(padded / R, 4) if R else None,
-                    "skew": round(float(counts.max() / (R / max(len(counts), 1))), 3) if R else None},
+        "config": dict({"workload": h["workload"], "T": h["T"], "H": h["H"], "E": h["E"], "k": h["k"], "I": h["I"],
+                        "local_experts": h["local_experts"], "parallelism": "none (one GPU)"}, **h["config"]),
+        "timing": h["timing"],
+        "layer_fractions": {f"{h['name']}_layer_hbm_frac": h["layer"]["hbm_frac"],
+                            f"{h['name']}_layer_mfma_frac": h["layer"]["mfma_frac"]},
+        "roofline": h["roofline"],
+        "layer": h["layer"],
+        "warm": h["warm"],
+        "flushed": h["flushed"],
+        "routing": h["routing"],
     }
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
-    else:
-        res["cpu_baseline"] = None
+    if pre is not None:
+        res["layer_fractions"] = {"decode_layer_hbm_frac": h["layer"]["hbm_frac"],
+                                  "decode_layer_hbm_frac_warm": h["layer"]["hbm_frac_warm"],
+                                  "prefill_layer_mfma_frac": pre["layer"]["mfma_frac"],
+                                  "prefill_gate_up_kernel_mfma_frac": pre["roofline"]["frac"]}
+        res["prefill"] = pre
+    res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
