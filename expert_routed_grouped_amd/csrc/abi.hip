@@ -4,16 +4,43 @@
 #include "../../include/moe.h"
 #include "common.h"
 
+#include <mutex>
+
 #ifndef SHARED_SPLIT_WG
 #define SHARED_SPLIT_WG 192  // measured on the 64-token decode batch (I_s = 1536): 1024 -> 72 us, 384 -> 72, 192 -> 55, 96 -> 57, 48 -> 74
 #endif
 
 #define MOE_VERSION_NUMBER 100  // 0.1.0
 
+// Intermediate h of moe_grouped_ffn_noalloc, for callers that cannot allocate device memory.  Each
+// GPU the library runs on holds its own copy until the process ends; host code never passes the
+// array's name to a kernel (on the host it is only a stand-in), always the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of ``scratch`` per device, looked up once
+
+// Device address of the current device's copy of ``scratch``; the first call on a device looks it up
+// with that device current and keeps it.
+int scratch_for_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -124,10 +151,17 @@ size_t moe_ffn_workspace_size(int R_cap, int E_loc, int H, int I, int a_dtype) {
   return align_up((size_t)R_cap * (size_t)I * esz, 256);
 }
 
-int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const int32_t *row_token, const float *row_w,
-                    int E_loc, int T, int R_cap, int H, int I, const void *w_gate_up, const void *w_down, int w_dtype,
-                    const float *s_gate_up, const float *s_down, float *y, float *y_perm, void *workspace,
-                    size_t workspace_bytes, unsigned flags, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launches of moe_grouped_ffn, whose intermediate h lives in ``workspace`` or, with
+// ``static_scratch``, in the current device's copy of ``scratch`` (looked up after every check passed).
+int grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const int32_t *row_token, const float *row_w,
+                int E_loc, int T, int R_cap, int H, int I, const void *w_gate_up, const void *w_down, int w_dtype,
+                const float *s_gate_up, const float *s_down, float *y, float *y_perm, void *workspace,
+                size_t workspace_bytes, unsigned flags, void *stream, bool static_scratch = false) {
+  if (static_scratch) workspace_bytes = MOE_NOALLOC_SCRATCH_BYTES;
   if (T < 0 || R_cap < 0 || E_loc < 1 || E_loc > 512 || H < 64 || I < 64 || H % 64 != 0 || I % 64 != 0)
     return MOE_ERR_SHAPE;
   if ((long long)R_cap > (long long)T * E_loc) return MOE_ERR_SHAPE;
@@ -143,7 +177,7 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
   if ((gather || y) && !row_token) return MOE_ERR_NULL;
   if (y && !row_w) return MOE_ERR_NULL;
   if (w_dtype == MOE_FP8_E4M3 && (!s_gate_up || !s_down)) return MOE_ERR_NULL;
-  if (!workspace) return MOE_ERR_WORKSPACE;
+  if (!workspace && !static_scratch) return MOE_ERR_WORKSPACE;
   if (workspace_bytes < moe_ffn_workspace_size(R_cap, E_loc, H, I, a_dtype)) return MOE_ERR_WORKSPACE;
   if (!aligned16(a) || !aligned16(w_gate_up) || !aligned16(w_down) || (y && !aligned16(y)) ||
       (y_perm && !aligned16(y_perm)) || ((uintptr_t)workspace & 255u) != 0)
@@ -155,6 +189,10 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
     return MOE_ERR_SHAPE;
   const bool packed = (flags & MOE_FFN_PACKED_WEIGHTS) != 0;
   if (packed && w_dtype == MOE_F32) return MOE_ERR_DTYPE;
+  if (static_scratch) {
+    const int st = scratch_for_current_device(&workspace);
+    if (st != MOE_OK) return st;
+  }
   hipStream_t s = (hipStream_t)stream;
   if (y && (flags & MOE_FFN_ZERO_Y) && only != MOE_FFN_ONLY_GATE_UP) {
     hipError_t err = launch_zero_f32(y, (size_t)T * H, s);
@@ -183,6 +221,28 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
   fa.phase = only == MOE_FFN_ONLY_GATE_UP ? 1 : (only == MOE_FFN_ONLY_DOWN ? 2 : 3);
   fa.wpacked = packed;
   return hip_status(launch_ffn(fa, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const int32_t *row_token, const float *row_w,
+                    int E_loc, int T, int R_cap, int H, int I, const void *w_gate_up, const void *w_down, int w_dtype,
+                    const float *s_gate_up, const float *s_down, float *y, float *y_perm, void *workspace,
+                    size_t workspace_bytes, unsigned flags, void *stream) {
+  return grouped_ffn(a, a_dtype, offsets, row_token, row_w, E_loc, T, R_cap, H, I, w_gate_up, w_down, w_dtype,
+                     s_gate_up, s_down, y, y_perm, workspace, workspace_bytes, flags, stream);
+}
+
+int moe_grouped_ffn_noalloc(const void *a, int a_dtype, const int32_t *offsets, const int32_t *row_token,
+                            const float *row_w, int E_loc, int T, int R_cap, int H, int I, const void *w_gate_up,
+                            const void *w_down, int w_dtype, const float *s_gate_up, const float *s_down, float *y,
+                            float *y_perm, unsigned flags, void *stream) {
+  // the intermediate h goes to this GPU's copy of the static scratch array; sizes whose h does not
+  // fit it are refused (MOE_ERR_WORKSPACE) with the other argument errors, before anything is enqueued
+  return grouped_ffn(a, a_dtype, offsets, row_token, row_w, E_loc, T, R_cap, H, I, w_gate_up, w_down, w_dtype,
+                     s_gate_up, s_down, y, y_perm, nullptr, 0, flags, stream, true);
 }
 
 int moe_pack_weights(const void *w, int w_dtype, int E, int N, int K, void *packed, void *stream) {

@@ -26,7 +26,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTY
 EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_permute_workspace_size",
            "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_quantize_mx", "moe_ffn_mx_workspace_size",
            "moe_grouped_ffn_mx", "moe_shared_workspace_size", "moe_shared_expert", "moe_route_dispatch_workspace_size",
-           "moe_route_dispatch", "moe_pack_weights", "moe_pack_router")
+           "moe_route_dispatch", "moe_pack_weights", "moe_pack_router", "moe_grouped_ffn_noalloc")
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class MoEError(RuntimeError):
@@ -60,6 +61,8 @@ def lib():
         L.moe_ffn_workspace_size.argtypes = [I, I, I, I, I]
         L.moe_grouped_ffn.restype = I
         L.moe_grouped_ffn.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, P, Z, ctypes.c_uint, P]
+        L.moe_grouped_ffn_noalloc.restype = I
+        L.moe_grouped_ffn_noalloc.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, ctypes.c_uint, P]
         L.moe_combine.restype = I
         L.moe_combine.argtypes = [P, P, P, I, I, I, P, P]
         L.moe_quantize_mx.restype = I
@@ -199,6 +202,26 @@ def moe_grouped_ffn(a: torch.Tensor, offsets: torch.Tensor, row_token: torch.Ten
         _ptr(a), adt, _ptr(offsets), _ptr(row_token), _ptr(row_w), El, T, R_cap, H, I, _ptr(w_gate_up),
         _ptr(w_down), _dtype(w_gate_up), _ptr(s_gate_up), _ptr(s_down), _ptr(y), _ptr(y_perm), _ptr(workspace),
         workspace.numel() * workspace.element_size(), flags, _stream(stream)))
+    return y if y is not None else y_perm
+
+
+def moe_grouped_ffn_noalloc(a: torch.Tensor, offsets: torch.Tensor, row_token: torch.Tensor, row_w: torch.Tensor,
+                            T: int, R_cap: int, w_gate_up: torch.Tensor, w_down: torch.Tensor,
+                            s_gate_up: Optional[torch.Tensor] = None, s_down: Optional[torch.Tensor] = None,
+                            y: Optional[torch.Tensor] = None, y_perm: Optional[torch.Tensor] = None,
+                            gather: bool = True, zero_y: bool = True, phase: str = "both", packed: bool = False,
+                            stream=None):
+    """moe_grouped_ffn with its intermediate in the library's static per-GPU scratch array (no
+    workspace argument, nothing allocated by the call).  Calls on one GPU must not overlap."""
+    El, twoI, H = w_gate_up.shape
+    I = twoI // 2
+    flags = (MOE_FFN_GATHER if gather else 0) | (MOE_FFN_ZERO_Y if zero_y else 0)
+    flags |= {"both": 0, "gate_up": MOE_FFN_ONLY_GATE_UP, "down": MOE_FFN_ONLY_DOWN}[phase]
+    flags |= MOE_FFN_PACKED_WEIGHTS if packed else 0
+    _check("moe_grouped_ffn_noalloc", lib().moe_grouped_ffn_noalloc(
+        _ptr(a), _dtype(a), _ptr(offsets), _ptr(row_token), _ptr(row_w), El, T, R_cap, H, I, _ptr(w_gate_up),
+        _ptr(w_down), _dtype(w_gate_up), _ptr(s_gate_up), _ptr(s_down), _ptr(y), _ptr(y_perm), flags,
+        _stream(stream)))
     return y if y is not None else y_perm
 
 

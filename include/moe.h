@@ -14,7 +14,8 @@
  * launch), moe_shared_expert (an always-active expert added to y), the W8A8
  * MXFP8 variant of the expert FFN (moe_quantize_mx, moe_grouped_ffn_mx) and
  * moe_pack_weights / moe_pack_router (one-time reorderings of resident expert
- * and router weights for faster reads).
+ * and router weights for faster reads), and moe_grouped_ffn_noalloc (the expert
+ * FFN for callers that cannot allocate a workspace).
  *
  * The method follows three pages: "AI-infra book, ch. 9 Distributed inference"
  * (section 9.3.4, Fig. 9-16: route, group rows by expert, expert GEMMs, weighted
@@ -31,8 +32,9 @@
  * --------------------------------
  *  - Every array argument is a DEVICE pointer to row-major memory owned by the
  *    caller.  The library allocates nothing, frees nothing and keeps no mutable
- *    global state; calls on different streams may run concurrently as long as
- *    they do not share output buffers.
+ *    global state (one exception: moe_grouped_ffn_noalloc keeps its intermediate
+ *    in a static per-GPU scratch array); calls on different streams may run
+ *    concurrently as long as they do not share output buffers.
  *  - ``stream`` is a hipStream_t passed as ``void*`` (NULL = the null stream).
  *    All work is enqueued on it; the calls return without waiting for the GPU.
  *    There is no device-to-host copy anywhere inside the calls.
@@ -206,6 +208,36 @@ int moe_grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const in
                     const void *w_gate_up, const void *w_down, int w_dtype,
                     const float *s_gate_up, const float *s_down, float *y, float *y_perm,
                     void *workspace, size_t workspace_bytes, unsigned flags, void *stream);
+
+/* Size of the device scratch array that moe_grouped_ffn_noalloc keeps its intermediate h in. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * moe_grouped_ffn_noalloc - moe_grouped_ffn without a caller-provided workspace.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments (less
+ * the workspace), same kernels, same results and errors as moe_grouped_ffn; the
+ * intermediate h [R_cap, I] lives in a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (32 MiB) instead.  Each GPU the library runs on holds
+ * its own copy of that array from the first call on it until the process ends;
+ * the call uses the copy of the current device (``stream`` must belong to it).
+ * The call itself allocates nothing (no hipMalloc / hipFree, no allocating
+ * library routine).  Limit: moe_ffn_workspace_size(R_cap, E_loc, H, I, a_dtype)
+ * must not exceed MOE_NOALLOC_SCRATCH_BYTES (e.g. R_cap * I <= 16 M bf16 values:
+ * every decode-sized batch of the 3 x 4096 x 1536 expert with T * k up to 10922),
+ * else MOE_ERR_WORKSPACE before anything is enqueued.  Nothing in the array has
+ * to start at zero: the gate/up half writes every row of h the down half reads.
+ * Every call on one GPU shares its array, which keeps the last call's contents,
+ * so calls that overlap on one GPU (several streams, several host threads) race
+ * and give wrong results: run them one after another, e.g. on one stream.  With
+ * MOE_FFN_ONLY_GATE_UP / MOE_FFN_ONLY_DOWN no other call of this entry point on
+ * the same GPU may come between the two halves.
+ */
+int moe_grouped_ffn_noalloc(const void *a, int a_dtype, const int32_t *offsets, const int32_t *row_token,
+                            const float *row_w, int E_loc, int T, int R_cap, int H, int I, const void *w_gate_up,
+                            const void *w_down, int w_dtype, const float *s_gate_up, const float *s_down, float *y,
+                            float *y_perm, unsigned flags, void *stream);
 
 /*
  * moe_pack_weights - copy expert weights into the packed block layout.

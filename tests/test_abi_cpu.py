@@ -256,3 +256,29 @@ def test_layer_repacks_router_after_the_weight_changes(monkeypatch):
     assert len(calls) == 2 and L._router_pack_current(dev)
     dev["w_router"] = torch.ones((8, 64))  # replaced
     assert not L._router_pack_current(dev)
+
+
+@pytest.mark.parametrize("kw,code", [
+    # h [R_cap, I] bf16 past the 32 MiB static scratch: 10923 rows x 1536 x 2 bytes
+    (dict(T=10923, R=10923, H=4096, I=1536, El=128), -4),
+    (dict(T=64, R=1 << 20, H=64, I=64, El=1 << 15), -2),
+    (dict(ad=2), -3), (dict(y=None), -1), (dict(y=FAKE, yp=FAKE), -1), (dict(a=FAKE_ODD), -6),
+    (dict(flags=1 << 7), -2), (dict(flags=4 | 8), -2),
+])
+def test_ffn_noalloc_validation(kw, code):
+    # every argument error is found on the host before the static scratch is looked up (no GPU needed)
+    a = dict(a=FAKE, ad=1, off=FAKE, rt=FAKE, rw=FAKE, El=8, T=16, R=32, H=128, I=64, wgu=FAKE, wd=FAKE, wdt=1,
+             sgu=None, sd=None, y=FAKE, yp=None, flags=3)
+    a.update(kw)
+    assert moe.lib().moe_grouped_ffn_noalloc(a["a"], a["ad"], a["off"], a["rt"], a["rw"], a["El"], a["T"], a["R"],
+                                             a["H"], a["I"], a["wgu"], a["wd"], a["wdt"], a["sgu"], a["sd"], a["y"],
+                                             a["yp"], a["flags"], None) == code
+
+
+def test_noalloc_limit_matches_header():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)" in src
+    assert moe.MOE_NOALLOC_SCRATCH_BYTES == 32 << 20
+    # the largest decode-sized h that fits: 10922 rows of I = 1536 bf16 values
+    assert moe.moe_ffn_workspace_size(10922, 128, 4096, 1536, moe.MOE_BF16) <= moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert moe.moe_ffn_workspace_size(10923, 128, 4096, 1536, moe.MOE_BF16) > moe.MOE_NOALLOC_SCRATCH_BYTES
