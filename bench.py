@@ -10,9 +10,10 @@ The default run measures both halves of the headline metric in one process:
 
 * ``decode`` (the headline ``value``): T=64 tokens x top-8 of 128 experts,
   H=4096, I=1536, bf16 -- weight-load bound, reported against HBM bandwidth.
-  Each of the K timed steps follows a 1 GiB write that evicts the L2 and the
-  Infinity Cache (the weights of a real model come from HBM, other layers ran
-  in between); the warm back-to-back rate is reported beside it.
+  Each of the K timed steps follows a 1 GiB write and a 1 GiB read of other
+  buffers, which evict the L2s and the Infinity Cache (the weights of a real
+  model come from HBM, other layers ran in between); the warm back-to-back rate
+  and the rate after the write alone are reported beside it.
 * ``prefill`` (the ``prefill`` object): T=6000 tokens, same layer -- matrix-core
   bound, reported against the bf16 MFMA peak, for the gate/up kernel and for
   the whole layer.
@@ -76,6 +77,9 @@ def parse():
     ap.add_argument("--weights", default="packed", choices=["packed", "row-major"],
                     help="layout of the resident bf16/fp8 expert weights (packed once with moe_pack_weights "
                          "before timing)")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="decode batches: the whole layer as one launch (moe_decode_layer) instead of route + "
+                         "dispatch, gate/up, down (three launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -199,10 +203,12 @@ class Workload:
         if args.weights == "packed":
             L.pack_weights(dev)  # one-time layout change of the resident weights, like loading them
         self.packed = bool(dev.get("packed", False))
-        bufs = self.bufs = L.LayerBuffers(cfg)
-        if bufs.rd_ws is not None and args.router == "packed":
+        bufs = self.bufs = L.LayerBuffers(cfg, use_decode_layer=args.one_launch)
+        self.one_launch = bufs.dec_ws is not None
+        decode_router = bufs.rd_ws is not None or self.one_launch
+        if decode_router and args.router == "packed":
             L.pack_router(dev)  # one-time layout change of the resident router weight
-        self.wrp = dev.get("w_router_packed") if bufs.rd_ws is not None else None
+        self.wrp = dev.get("w_router_packed") if decode_router else None
         self.stream = torch.cuda.current_stream()
         self.mx = cfg.wdt == "mxfp8"
         if self.mx:  # activations quantised on the fly into these, h lives in the MX workspace
@@ -211,8 +217,20 @@ class Workload:
             bufs.workspace = torch.empty(moe.moe_ffn_mx_workspace_size(bufs.R_cap, cfg.I), dtype=torch.uint8,
                                          device="cuda")
         self.moe = moe
-        self.phases = [("route", self.route), ("gate_up", lambda: self.ffn_half("gate_up")),
-                       ("down", self.down)]
+        if self.one_launch:  # the whole layer in one kernel (then the shared expert, if any)
+            self.phases = [("layer_kernel", self.decode_layer)]
+            if bufs.shared_ws is not None:
+                self.phases.append(("shared_expert", self.shared))
+        else:
+            self.phases = [("route", self.route), ("gate_up", lambda: self.ffn_half("gate_up")),
+                           ("down", self.down)]
+
+    def decode_layer(self):
+        moe, cfg, bufs, dev = self.moe, self.cfg, self.bufs, self.dev
+        moe.moe_decode_layer(dev["x"], dev["w_router"] if self.wrp is None else self.wrp, dev["bias"], cfg.k, cfg.E,
+                             cfg.lo, cfg.hi, dev["w_gate_up"], dev["w_down"], dev["s_gate_up"], dev["s_down"],
+                             bufs.dec_ws, bufs.topk_ids, bufs.topk_w, bufs.perm, bufs.y,
+                             router_packed=self.wrp is not None, packed=self.packed, stream=self.stream)
 
     def route(self):
         moe, cfg, bufs, dev, p, s = self.moe, self.cfg, self.bufs, self.dev, self.bufs.perm, self.stream
@@ -281,22 +299,39 @@ def measure(wl: Workload, args):
         return {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
                 for i, (name, _) in enumerate(wl.phases)}
 
-    flushed = None
+    flushed = flushed_w = None
     if not args.no_flush:
-        say(f"{wl.name}: timing {args.steps} steps, each after a {FLUSH_BYTES >> 20} MiB cache-flushing write")
+        # Before each flushed step 1 GiB is written and another 1 GiB read: the L2s and the Infinity
+        # Cache then hold none of the layer's data, and no dirty lines either.  After the write alone
+        # they hold ~290 MB of dirty lines whose write-back the next kernel pays for (measured on the
+        # decode layer: +59 us in its first kernel, nothing elsewhere); that cost belongs to the flush,
+        # not to the layer, so it is reported beside the headline rather than in it.
         scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-        fevs = [events() for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        for i in range(args.steps):
-            scratch.fill_(0x5A)
-            wl.step(fevs[i])
+        other = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        total = torch.zeros((), dtype=torch.float32, device="cuda")
+
+        def flushed_steps(n, read):
+            evs = [events() for _ in range(n)]
             torch.cuda.synchronize()
-        w1 = time.perf_counter()
-        del scratch
-        fl = [e[0].elapsed_time(e[nph]) for e in fevs]
-        flushed = {"ms": stats(fl), "phase_ms": {k: round(v, 4) for k, v in phase_ms(fevs).items()},
-                   "wall_ms_per_step_incl_flush_and_sync": round((w1 - w0) * 1e3 / args.steps, 4)}
+            w0 = time.perf_counter()
+            for i in range(n):
+                scratch.fill_(0x5A)
+                if read:
+                    torch.sum(other, dim=0, out=total)
+                wl.step(evs[i])
+                torch.cuda.synchronize()
+            w1 = time.perf_counter()
+            return {"ms": stats([e[0].elapsed_time(e[nph]) for e in evs]),
+                    "phase_ms": {k: round(v, 4) for k, v in phase_ms(evs).items()},
+                    "wall_ms_per_step_incl_flush_and_sync": round((w1 - w0) * 1e3 / n, 4)}
+
+        say(f"{wl.name}: timing {args.steps} steps, each after a {FLUSH_BYTES >> 20} MiB write and a "
+            f"{FLUSH_BYTES >> 20} MiB read of other buffers")
+        flushed = dict(flushed_steps(args.steps, True), flush="1 GiB written, then another 1 GiB read")
+        nw = min(args.steps, 20)
+        say(f"{wl.name}: timing {nw} steps, each after the 1 GiB write alone")
+        flushed_w = dict(flushed_steps(nw, False), flush="1 GiB written (dirty lines left to write back)")
+        del scratch, other, total
 
     say(f"{wl.name}: timing {args.steps} warm back-to-back steps")
     wevs = [events() for _ in range(args.steps)]
@@ -341,50 +376,71 @@ def measure(wl: Workload, args):
         layer_flops += A.useful_flops(T, H, cfg.I_s)
         layer_bytes += A.expert_bytes(H, cfg.I_s, wbytes, cfg.wdt == "fp8")
     # headline timing: the flushed steps (weights from HBM), else the warm ones
+    fw_s = flushed_w["ms"]["mean"] * 1e-3 if flushed_w else None
     step_ms = flushed["ms"]["mean"] if flushed else warm["ms"]["mean"]
-    gu_ms = (flushed or warm)["phase_ms"]["gate_up"]
-    gu_s = gu_ms * 1e-3
     hbm_bound = wl.name.startswith("decode")  # a few rows per expert: the weight stream bounds the kernel
     peak_mfma = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
-    if hbm_bound:
-        achieved = gu_bytes / gu_s / 1e9
+    timing = "cache-flushed steps" if flushed else "warm steps"
+    weights = "packed" if wl.packed else "row-major"
+    if wl.one_launch:
+        # the dominant kernel is the whole routed layer: its algorithmic bytes are the layer's minus
+        # the shared expert's (a separate launch)
+        k_ms = (flushed or warm)["phase_ms"]["layer_kernel"]
+        k_bytes = int(layer_bytes - (A.expert_bytes(H, cfg.I_s, wbytes, cfg.wdt == "fp8") if cfg.I_s > 0 else 0))
+        achieved = k_bytes / (k_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic("decode_layer_kernel", wl.name, weights),
+                "kernel": "decode_layer_kernel (routing, grouping, gate/up, down + combine: one launch)",
+                "avg_ms": round(k_ms, 4), "algorithmic_per_launch": k_bytes, "timing": timing}
+        padded = A.padded_rows(counts, 64)
     else:
-        achieved = gu_flops / gu_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_mfma, "unit": "TFLOP/s",
-                "frac": round(achieved / peak_mfma, 4), "traffic": None}
-    streaming = bufs.R_cap <= 48 * cfg.E_loc
-    kernel = (("ffn_mx_stream_kernel" if streaming else "ffn_mx_kernel") if mx else
-              ("ffn_stream_kernel" if streaming else
-               ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel")))
-    roof["traffic"] = measured_traffic(kernel, wl.name, "packed" if wl.packed else "row-major")
-    # rows the grouped GEMM actually multiplies, by the tiling of the kernel in use
-    padded = (A.padded_rows(counts, 64) if kernel == "ffn_stream_kernel" else
-              A.padded_rows(counts, 32 if bufs.R_cap <= 16 * cfg.E_loc else 64) if kernel == "ffn_mx_stream_kernel" else
-              (A.split_padded_rows(counts, 256, 64) if kernel == "ffn_dma_kernel" else
-               (A.split_padded_rows(counts, 192, 64) if kernel == "ffn_mx_kernel" else A.padded_rows(counts, 256))))
-    roof.update({"kernel": f"{kernel}<0> (gate/up + SwiGLU half, one launch)", "avg_ms": round(gu_ms, 4),
-                 "algorithmic_per_launch": gu_bytes if hbm_bound else gu_flops,
-                 "timing": "cache-flushed steps" if flushed else "warm steps"})
+        gu_ms = (flushed or warm)["phase_ms"]["gate_up"]
+        gu_s = gu_ms * 1e-3
+        if hbm_bound:
+            achieved = gu_bytes / gu_s / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        else:
+            achieved = gu_flops / gu_s / 1e12
+            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_mfma, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak_mfma, 4)}
+        streaming = bufs.R_cap <= 48 * cfg.E_loc
+        kernel = (("ffn_mx_stream_kernel" if streaming else "ffn_mx_kernel") if mx else
+                  ("ffn_stream_kernel" if streaming else
+                   ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel")))
+        roof["traffic"] = measured_traffic(kernel, wl.name, weights)
+        # rows the grouped GEMM actually multiplies, by the tiling of the kernel in use
+        padded = (A.padded_rows(counts, 64) if kernel == "ffn_stream_kernel" else
+                  A.padded_rows(counts, 32 if bufs.R_cap <= 16 * cfg.E_loc else 64)
+                  if kernel == "ffn_mx_stream_kernel" else
+                  (A.split_padded_rows(counts, 256, 64) if kernel == "ffn_dma_kernel" else
+                   (A.split_padded_rows(counts, 192, 64) if kernel == "ffn_mx_kernel" else A.padded_rows(counts, 256))))
+        roof.update({"kernel": f"{kernel}<0> (gate/up + SwiGLU half, one launch)", "avg_ms": round(gu_ms, 4),
+                     "algorithmic_per_launch": gu_bytes if hbm_bound else gu_flops, "timing": timing})
     layer_s = step_ms * 1e-3
     warm_s = warm["ms"]["mean"] * 1e-3
     return {
         "workload": WORKLOADS[wl.name], "name": wl.name, "T": T, "H": H, "E": cfg.E, "k": cfg.k, "I": I,
         "local_experts": [cfg.lo, cfg.hi],
         "tokens_per_s": round(T / layer_s, 1), "ms_per_step": round(step_ms, 4),
-        "timing": ("mean of K steps, each after a 1 GiB cache-flushing write, HIP events around the step"
-                   if flushed else "mean of K warm back-to-back steps, HIP events"),
-        "flushed": flushed, "warm": dict(warm, tokens_per_s=round(T / warm_s, 1)),
+        "timing": ("mean of K steps, each after writing 1 GiB and reading another 1 GiB (caches hold none of the "
+                   "layer's data), HIP events around the step" if flushed else
+                   "mean of K warm back-to-back steps, HIP events"),
+        "flushed": flushed, "flushed_write_only": flushed_w, "warm": dict(warm, tokens_per_s=round(T / warm_s, 1)),
         "roofline": roof,
         "layer": {"hbm_bytes": int(layer_bytes), "hbm_frac": round(layer_bytes / layer_s / 1e9 / PEAK_HBM_GBS, 4),
                   "hbm_frac_warm": round(layer_bytes / warm_s / 1e9 / PEAK_HBM_GBS, 4),
+                  "hbm_frac_flushed_write_only": (round(layer_bytes / fw_s / 1e9 / PEAK_HBM_GBS, 4) if fw_s
+                                                  else None),
                   "router_weight_bytes": int(router_bytes), "flops": int(layer_flops),
                   "mfma_frac": round(layer_flops / layer_s / 1e12 / peak_mfma, 4),
                   "mfma_frac_warm": round(layer_flops / warm_s / 1e12 / peak_mfma, 4),
                   "shared_expert_ms": shared_ms},
         "config": {"combine": "fused atomic epilogue" if bufs.fused else "per-row outputs + moe_combine",
-                   "dispatch": "route + dispatch in one launch" if bufs.rd_ws is not None else "moe_route + moe_permute",
+                   "dispatch": ("the whole layer in one launch (moe_decode_layer)" if wl.one_launch else
+                                "route + dispatch in one launch" if bufs.rd_ws is not None else
+                                "moe_route + moe_permute"),
                    "weights": "packed 32x64 blocks (moe_pack_weights, once before timing)" if wl.packed else "row-major",
                    "router_weight": ("fp32 [H/4, E, 4] (moe_pack_router, once before timing)" if wl.wrp is not None
                                      else "as stored")},
@@ -414,15 +470,24 @@ def main():
     if not args.no_cpu_baseline:
         say("cpu baseline (oracle)")
         cpu = cpu_baseline(head.inp, head.cfg, args.cpu_seconds)
-    pre = None
+    pre = one = None
     if args.config == "default":
         del head
         torch.cuda.empty_cache()
+        # the same decode layer as one launch (moe_decode_layer), reported beside the headline
+        one_args = argparse.Namespace(**dict(vars(args), one_launch=True))
+        one_wl = Workload("decode", one_args)
+        o = measure(one_wl, one_args)
+        del one_wl
+        torch.cuda.empty_cache()
+        one = {k: o[k] for k in ("tokens_per_s", "ms_per_step", "timing", "roofline", "warm", "flushed",
+                                 "flushed_write_only", "config")}
+        one["layer_hbm_frac"] = o["layer"]["hbm_frac"]
         pre_wl = Workload("prefill", args)
         p = measure(pre_wl, args)
         del pre_wl
         pre = {k: p[k] for k in ("workload", "tokens_per_s", "ms_per_step", "timing", "roofline", "layer", "warm",
-                                 "flushed", "routing", "config")}
+                                 "flushed", "flushed_write_only", "routing", "config")}
         pre["roofline_layer"] = {"bound": "mfma", "achieved": round(p["layer"]["flops"] / p["ms_per_step"] / 1e9, 1),
                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": p["layer"]["mfma_frac"],
                                  "flops_per_step": p["layer"]["flops"]}
@@ -448,14 +513,17 @@ def main():
         "layer": h["layer"],
         "warm": h["warm"],
         "flushed": h["flushed"],
+        "flushed_write_only": h["flushed_write_only"],
         "routing": h["routing"],
     }
     if pre is not None:
         res["layer_fractions"] = {"decode_layer_hbm_frac": h["layer"]["hbm_frac"],
                                   "decode_layer_hbm_frac_warm": h["layer"]["hbm_frac_warm"],
+                                  "decode_layer_hbm_frac_flushed_write_only": h["layer"]["hbm_frac_flushed_write_only"],
                                   "prefill_layer_mfma_frac": pre["layer"]["mfma_frac"],
                                   "prefill_gate_up_kernel_mfma_frac": pre["roofline"]["frac"]}
         res["prefill"] = pre
+        res["decode_one_launch"] = one
     res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 

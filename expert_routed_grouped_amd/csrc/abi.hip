@@ -109,6 +109,67 @@ int moe_route_dispatch(const void *x, int x_dtype, const void *w_router, int w_d
                                           row_w, token_row, y_zero, (uint32_t *)workspace, (hipStream_t)stream));
 }
 
+size_t moe_decode_layer_workspace_size(int T, int k, int E_loc, int I) {
+  if (T < 0 || k < 1 || E_loc < 1 || I < 1) return 0;
+  return decode_layer_ws_bytes(T, k, E_loc, I);
+}
+
+int moe_decode_layer(const void *x, int x_dtype, const void *w_router, int wr_dtype, const float *bias, int T, int H,
+                     int E, int k, int e_begin, int e_end, int I, const void *w_gate_up, const void *w_down,
+                     int w_dtype, const float *s_gate_up, const float *s_down, int32_t *topk_ids, float *topk_w,
+                     int32_t *counts, int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
+                     float *y, void *workspace, size_t workspace_bytes, unsigned flags, void *stream) {
+  if (T < 0 || H < 64 || I < 64 || H % 64 != 0 || I % 64 != 0 || E < 1 || E > 256 || k < 1 || k > E || k > 32)
+    return MOE_ERR_SHAPE;
+  if (e_begin < 0 || e_end <= e_begin || e_end > E) return MOE_ERR_SHAPE;
+  if (T > kDecodeLayerMaxT || H > 16384 || (long long)H * I >= (1LL << 30)) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (wr_dtype != MOE_F32 && wr_dtype != MOE_BF16 && wr_dtype != MOE_F32_ROUTER_PACKED) return MOE_ERR_DTYPE;
+  if (w_dtype != MOE_BF16 && w_dtype != MOE_FP8_E4M3) return MOE_ERR_DTYPE;
+  if ((flags & ~MOE_FFN_PACKED_WEIGHTS) != 0) return MOE_ERR_SHAPE;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (T > 0 && (!x || !w_router || !w_gate_up || !w_down || !topk_ids || !topk_w || !row_token || !row_w ||
+                !token_row || !y))
+    return MOE_ERR_NULL;
+  if (T > 0 && w_dtype == MOE_FP8_E4M3 && (!s_gate_up || !s_down)) return MOE_ERR_NULL;
+  const int El = e_end - e_begin;
+  if (!workspace || workspace_bytes < decode_layer_ws_bytes(T, k, El, I)) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return MOE_ERR_ALIGN;
+  if (T == 0)  // nothing to route: zero counts and offsets as moe_permute does
+    return hip_status(launch_permute(nullptr, nullptr, 0, k, e_begin, El, counts, offsets, row_token, row_w,
+                                     token_row, nullptr, (hipStream_t)stream));
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y))
+    return MOE_ERR_ALIGN;
+  DecodeArgs a{};
+  a.x = x;
+  a.wr = w_router;
+  a.wmode = wr_dtype == MOE_BF16 ? 1 : (wr_dtype == MOE_F32_ROUTER_PACKED ? 2 : 0);
+  a.bias = bias;
+  a.T = T;
+  a.H = H;
+  a.E = E;
+  a.k = k;
+  a.lo = e_begin;
+  a.El = El;
+  a.I = I;
+  a.ids = topk_ids;
+  a.gates = topk_w;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.row_token = row_token;
+  a.row_w = row_w;
+  a.token_row = token_row;
+  a.y = y;
+  a.wgu = w_gate_up;
+  a.wd = w_down;
+  a.sgu = s_gate_up;
+  a.sd = s_down;
+  a.fp8 = w_dtype == MOE_FP8_E4M3;
+  a.wpacked = (flags & MOE_FFN_PACKED_WEIGHTS) != 0;
+  a.ws = workspace;
+  return hip_status(launch_decode_layer(a, (hipStream_t)stream));
+}
+
 int moe_permute(const int32_t *topk_ids, const float *topk_w, int T, int k, int E, int e_begin, int e_end,
                 int32_t *counts, int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
                 const void *x, int x_dtype, int H, void *x_perm, void *workspace, size_t workspace_bytes,

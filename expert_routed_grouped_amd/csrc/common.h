@@ -76,6 +76,33 @@ hipError_t launch_route_dispatch(const void *x, int x_bf16, const void *w, int w
                                  int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
                                  float *y_zero, uint32_t *ticket, hipStream_t s);
 
+// Fused decode layer (decode_fused.hip): routing, grouping, gate/up and down + combine in one
+// persistent launch.  Its workspace starts with uint32 control words (the work queue, the routing
+// ticket, the ``routed`` flag, the exit count, an error word and one completion count per local
+// expert), zero before the call and zero again after it (the error word excepted), then h
+// [El, T, I] bf16 (every token of every local expert).
+enum : int { kDecQueue = 0, kDecTicket = 1, kDecRouted = 2, kDecExit = 3, kDecError = 4, kDecDone = 64 };
+constexpr int kDecodeLayerMaxT = 64;  // every token of the batch fits one 64-row tile
+struct DecodeArgs {
+  const void *x;            // [T, H] bf16
+  const void *wr;           // router weight
+  int wmode;                // 0 fp32 [E, H], 1 bf16 [E, H], 2 fp32 packed [H/4, E, 4]
+  const float *bias;        // [E] or NULL
+  int T, H, E, k, lo, El, I;
+  int32_t *ids;
+  float *gates;
+  int32_t *counts, *offsets, *row_token;
+  float *row_w;
+  int32_t *token_row;
+  float *y;                 // [T, H] fp32, overwritten
+  const void *wgu, *wd;     // expert weights (bf16 or e4m3)
+  const float *sgu, *sd;    // e4m3 per-channel scales
+  int fp8, wpacked;
+  void *ws;                 // decode_layer_ws_bytes(T, k, El, I) bytes, 256-byte aligned (T <= kDecodeLayerMaxT)
+};
+size_t decode_layer_ws_bytes(int T, int k, int El, int I);
+hipError_t launch_decode_layer(const DecodeArgs &a, hipStream_t s);
+
 // Row maps of one group holding every token once, in order: offsets = {0, T},
 // row_token[i] = i, row_w[i] = 1 (the shared expert as a one-expert grouped FFN).
 hipError_t launch_identity_rows(int T, int32_t *offsets, int32_t *row_token, float *row_w, hipStream_t s);

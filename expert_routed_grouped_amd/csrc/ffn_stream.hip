@@ -11,20 +11,17 @@
 //    columns of one expert (32 gate + 32 up rows for the gate/up half) for up to
 //    64 rows of that expert (two 32-row MFMA blocks);
 //  - the wave streams its weight rows straight from HBM into registers in the
-//    operand layout of v_mfma_f32_32x32x16_bf16.  The contraction index may be
-//    permuted freely as long as both operands use the same permutation, so in
-//    every 64-wide k chunk lane (n, g) reads 64 contiguous bytes of row n at
-//    k-offset 32g and feeds them to four MFMAs; the two lanes of a row cover
-//    one whole 128-byte line.  The activations are read with the same layout
-//    (they are small and stay in L2);
-//  - two chunks are in flight per wave (register double buffering), and many
-//    waves per CU cover the HBM latency.
+//    operand layout of v_mfma_f32_32x32x16_bf16 (stream_core.h: every lane reads
+//    64 contiguous bytes of one row per 64-wide k chunk, two chunks in flight);
+//    the activations are read with the same layout (they are small and stay in
+//    L2), and many waves per CU cover the HBM latency.
 //
 // Tiles are located the same way as in the tile kernels (64-row M tiles, found
 // from the expert offsets on the device); an expert with more than 64 rows gets
 // more M tiles and its weights are streamed once per M tile, which is still
 // correct.
 #include "ffn_common.h"
+#include "stream_core.h"
 
 namespace {
 
@@ -38,24 +35,8 @@ constexpr int SBM = 32 * SMB;   // rows per M tile
 constexpr int SWAVES = 4;   // waves per block, 32 output columns each
 constexpr int SCOLS = 32 * SWAVES;  // gate/up columns per block (down: twice as many)
 
-// 8 bf16 from 16 bytes of bf16, or from 8 bytes of e4m3.
-template <bool FP8>
-__device__ __forceinline__ bf16x8_t as_operand(const u32x4_t *q, int s) {
-  if constexpr (FP8) {
-    // q[0] holds k 0..15, q[1] k 16..31 of this lane's 32-element slice
-    const u32x4_t v = q[s >> 1];
-    const uint32_t w0 = (s & 1) ? v.z : v.x, w1 = (s & 1) ? v.w : v.y;
-    uint2 a = e4m3x4_to_bf16x4(w0), b = e4m3x4_to_bf16x4(w1);
-    u32x4_t r = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(bf16x8_t, r);
-  } else {
-    return __builtin_bit_cast(bf16x8_t, q[s]);
-  }
-}
-
 template <int MODE, bool FP8, bool GATHER, bool ATOMIC>
 __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
-  constexpr int WQ = FP8 ? 2 : 4;  // 16-byte weight loads per lane per 64-wide k chunk
   const int K = MODE == 0 ? p.H : p.I;
   const int Ncols = MODE == 0 ? p.I : p.H;
   const int Nw = MODE == 0 ? 2 * p.I : p.H;
@@ -92,48 +73,7 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
   }
 
   f32x16_t acc[SMB][NB];
-#pragma unroll
-  for (int mb = 0; mb < SMB; mb++)
-#pragma unroll
-    for (int b = 0; b < NB; b++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[mb][b][r] = 0.0f;
-
-  u32x4_t wq[2][NB][WQ], aq[2][SMB][4];
-  auto load = [&](int buf, int k0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int b = 0; b < NB; b++)
-#pragma unroll
-      for (int q = 0; q < WQ; q++) wq[buf][b][q] = *(const u32x4_t *)(wrow[b] + (size_t)(k0 >> 6) * cstep + 16 * q);
-#pragma unroll
-    for (int q = 0; q < 4; q++) aq[buf][0][q] = *(const u32x4_t *)(arow[0] + k0 + 8 * q);
-    if constexpr (SMB > 1) {
-      if (two_m) {
-#pragma unroll
-        for (int q = 0; q < 4; q++) aq[buf][SMB - 1][q] = *(const u32x4_t *)(arow[SMB - 1] + k0 + 8 * q);
-      }
-    }
-  };
-  auto compute = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-      bf16x8_t bo[NB];
-#pragma unroll
-      for (int b = 0; b < NB; b++) bo[b] = as_operand<FP8>(wq[buf][b], s);
-      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, aq[buf][0][s]);
-#pragma unroll
-      for (int b = 0; b < NB; b++) acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bo[b], acc[0][b], 0, 0, 0);
-      if constexpr (SMB > 1) {
-        if (two_m) {
-          const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, aq[buf][SMB - 1][s]);
-#pragma unroll
-          for (int b = 0; b < NB; b++)
-            acc[SMB - 1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bo[b], acc[SMB - 1][b], 0, 0, 0);
-        }
-      }
-    }
-  };
-
+  sc::zero_acc(acc);
   // this workgroup's 64-wide k chunks: [kb, kb + KC) of the K / 64 (K is a multiple of 64)
   const int kb = ks * (K / 64) / KS;
   const int KC = (ks + 1) * (K / 64) / KS - kb;
@@ -141,15 +81,7 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
   for (int b = 0; b < NB; b++) wrow[b] += (size_t)kb * cstep;
 #pragma unroll
   for (int mb = 0; mb < SMB; mb++) arow[mb] += (size_t)kb * 64;
-  if (KC > 0) load(0, 0);
-  int kc = 0;
-  for (; kc + 2 <= KC; kc += 2) {
-    load(1, (kc + 1) * 64);
-    compute(0);
-    if (kc + 2 < KC) load(0, (kc + 2) * 64);
-    compute(1);
-  }
-  if (kc < KC) compute(0);
+  sc::stream_mfma<FP8, SMB, NB>(wrow, cstep, arow, two_m, KC, acc);
 
   // ---- epilogue: acc[mb][b][r] at lane l is row mb*32 + 8*(r/4) + 4*(l/32) + r%4, column c0 + l%32
   const int col = c0 + n;

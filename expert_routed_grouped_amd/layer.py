@@ -82,7 +82,8 @@ def _router_pack_current(dev: dict) -> bool:
 class LayerBuffers:
     """Device buffers of one layer shape, reused across calls."""
 
-    def __init__(self, cfg, device="cuda", fused: Optional[bool] = None, use_route_dispatch: bool = True):
+    def __init__(self, cfg, device="cuda", fused: Optional[bool] = None, use_route_dispatch: bool = True,
+                 use_decode_layer: bool = False):
         T, k, El, H, I = cfg.T, cfg.k, cfg.E_loc, cfg.H, cfg.I
         self.cfg = cfg
         self.R_cap = T * min(k, El)
@@ -103,20 +104,38 @@ class LayerBuffers:
         self.y_perm = None if self.fused else torch.empty((max(self.R_cap, 1), H), dtype=torch.float32, **d)
         self.shared_ws = (torch.empty(moe.moe_shared_workspace_size(T, cfg.I_s, adt), dtype=torch.uint8, **d)
                           if cfg.I_s > 0 else None)
-        # decode-sized batches route and dispatch in one launch (its ticket workspace starts zeroed)
+        # use_decode_layer: decode batches (T <= 64) run the whole layer in one launch
+        # (moe_decode_layer; its workspace starts zeroed).  Off by default: on MI355X the one-launch
+        # kernel measured 1.03 ms for the 64-token layer against 0.86 ms for route + dispatch, gate/up
+        # and down as three launches
+        dec = (use_decode_layer and self.fused and 1 <= T <= 64 and cfg.act == "bf16" and cfg.wdt in ("bf16", "fp8")
+               and cfg.E <= 256 and H % 64 == 0 and I % 64 == 0 and H <= 16384)
+        self.dec_ws = moe.moe_decode_layer_workspace(T, k, El, I, device) if dec else None
+        # otherwise decode-sized batches route and dispatch in one launch (its ticket workspace starts zeroed)
         fits = 1 <= T <= 512 and T * k <= 8192 and cfg.E <= 256 and H % 8 == 0 and H <= 16384
-        self.rd_ws = moe.moe_route_dispatch_workspace(device) if (fits and use_route_dispatch) else None
+        self.rd_ws = (moe.moe_route_dispatch_workspace(device) if (fits and use_route_dispatch and not dec)
+                      else None)
 
 
 def run_layer(dev: dict, bufs: LayerBuffers, stream=None) -> torch.Tensor:
-    """route -> permute -> grouped FFN (-> combine) (-> shared expert).  Returns y [T,H] fp32."""
+    """route -> permute -> grouped FFN (-> combine) (-> shared expert), or for decode-sized batches
+    moe_decode_layer (-> shared expert).  Returns y [T,H] fp32."""
     cfg = bufs.cfg
     p = bufs.perm
     packed = bool(dev.get("packed", False))
+    wp = dev.get("w_router_packed")
+    if wp is not None and not _router_pack_current(dev):  # w_router replaced or edited: pack again
+        wp = pack_router(dev)["w_router_packed"]
+    if bufs.dec_ws is not None:  # the whole layer in one launch
+        moe.moe_decode_layer(dev["x"], dev["w_router"] if wp is None else wp, dev["bias"], cfg.k, cfg.E, cfg.lo, cfg.hi,
+                             dev["w_gate_up"], dev["w_down"], dev.get("s_gate_up"), dev.get("s_down"), bufs.dec_ws,
+                             bufs.topk_ids, bufs.topk_w, p, bufs.y, router_packed=wp is not None, packed=packed,
+                             stream=stream)
+        if bufs.shared_ws is not None:
+            moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], bufs.y, dev.get("ss_gate_up"),
+                                  dev.get("ss_down"), workspace=bufs.shared_ws, packed=packed, stream=stream)
+        return bufs.y
     if bufs.rd_ws is not None:  # one launch: route, dispatch and (fused combine) the zeroing of y
-        wp = dev.get("w_router_packed")
-        if wp is not None and not _router_pack_current(dev):  # w_router replaced or edited: pack again
-            wp = pack_router(dev)["w_router_packed"]
         moe.moe_route_dispatch(dev["x"], dev["w_router"] if wp is None else wp, dev["bias"], cfg.k, cfg.E, cfg.lo,
                                cfg.hi, bufs.rd_ws, bufs.topk_ids, bufs.topk_w, p,
                                y_zero=bufs.y if bufs.fused else None, router_packed=wp is not None, stream=stream)

@@ -26,7 +26,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTY
 EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_permute_workspace_size",
            "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_quantize_mx", "moe_ffn_mx_workspace_size",
            "moe_grouped_ffn_mx", "moe_shared_workspace_size", "moe_shared_expert", "moe_route_dispatch_workspace_size",
-           "moe_route_dispatch", "moe_pack_weights", "moe_pack_router", "moe_grouped_ffn_noalloc")
+           "moe_route_dispatch", "moe_pack_weights", "moe_pack_router", "moe_grouped_ffn_noalloc",
+           "moe_decode_layer_workspace_size", "moe_decode_layer")
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -63,6 +64,11 @@ def lib():
         L.moe_grouped_ffn.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, P, Z, ctypes.c_uint, P]
         L.moe_grouped_ffn_noalloc.restype = I
         L.moe_grouped_ffn_noalloc.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, ctypes.c_uint, P]
+        L.moe_decode_layer_workspace_size.restype = Z
+        L.moe_decode_layer_workspace_size.argtypes = [I, I, I, I]
+        L.moe_decode_layer.restype = I
+        L.moe_decode_layer.argtypes = [P, I, P, I, P, I, I, I, I, I, I, I, P, P, I, P, P, P, P, P, P, P, P, P, P, P,
+                                       Z, ctypes.c_uint, P]
         L.moe_combine.restype = I
         L.moe_combine.argtypes = [P, P, P, I, I, I, P, P]
         L.moe_quantize_mx.restype = I
@@ -349,3 +355,41 @@ def moe_route_dispatch(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[t
         _ptr(out["token_row"]), _ptr(y_zero), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return out
+
+
+def moe_decode_layer_workspace(T: int, k: int, E_loc: int, I: int, device="cuda") -> torch.Tensor:
+    """A zeroed workspace for moe_decode_layer (its control words must start at zero)."""
+    return torch.zeros(int(lib().moe_decode_layer_workspace_size(T, k, E_loc, I)), dtype=torch.uint8, device=device)
+
+
+def moe_decode_layer(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor], k: int, E: int,
+                     e_begin: int, e_end: int, w_gate_up: torch.Tensor, w_down: torch.Tensor,
+                     s_gate_up: Optional[torch.Tensor], s_down: Optional[torch.Tensor], workspace: torch.Tensor,
+                     topk_ids: torch.Tensor, topk_w: torch.Tensor, out: dict, y: torch.Tensor,
+                     router_packed: bool = False, packed: bool = False, stream=None) -> torch.Tensor:
+    """The whole decode layer in one launch: routing into ``topk_ids``/``topk_w``, the grouping into
+    ``out`` (counts, offsets, row_token, row_w, token_row as from moe_permute) and y [T, H]
+    (overwritten).  ``router_packed``: ``w_router`` is the moe_pack_router tensor; ``packed``: the
+    expert weights come from moe_pack_weights."""
+    T, H = x.shape
+    El, twoI, _ = w_gate_up.shape
+    if router_packed:
+        if w_router.dtype != torch.float32 or tuple(w_router.shape) != (H // 4, E, 4):
+            raise ValueError(f"router_packed needs the fp32 [H/4, E, 4] = {(H // 4, E, 4)} tensor of moe_pack_router, "
+                             f"got {w_router.dtype} {tuple(w_router.shape)}")
+    elif tuple(w_router.shape) != (E, H):
+        raise ValueError(f"w_router must be [E, H] = {(E, H)}, got {tuple(w_router.shape)}")
+    if El != e_end - e_begin or tuple(w_down.shape) != (El, H, twoI // 2):
+        raise ValueError("expert weights must be [E_loc, 2I, H] and [E_loc, H, I]")
+    _check("moe_decode_layer", lib().moe_decode_layer(
+        _ptr(x), _dtype(x), _ptr(w_router), MOE_F32_ROUTER_PACKED if router_packed else _dtype(w_router), _ptr(bias),
+        T, H, E, k, e_begin, e_end, twoI // 2, _ptr(w_gate_up), _ptr(w_down), _dtype(w_gate_up), _ptr(s_gate_up),
+        _ptr(s_down), _ptr(topk_ids), _ptr(topk_w), _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["row_token"]),
+        _ptr(out["row_w"]), _ptr(out["token_row"]), _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        MOE_FFN_PACKED_WEIGHTS if packed else 0, _stream(stream)))
+    return y
+
+
+def decode_layer_error_word(workspace: torch.Tensor) -> int:
+    """The diagnostic word of a moe_decode_layer workspace (nonzero: a wait in the kernel gave up)."""
+    return int(workspace[16:20].view(torch.int32).item())

@@ -11,7 +11,7 @@
  *   moe_combine      gate-weighted gather-sum of per-row outputs to token order
  *
  * plus moe_route_dispatch (the first two calls of a decode batch in one
- * launch), moe_shared_expert (an always-active expert added to y), the W8A8
+ * launch), moe_decode_layer (all four of a decode batch in one launch), moe_shared_expert (an always-active expert added to y), the W8A8
  * MXFP8 variant of the expert FFN (moe_quantize_mx, moe_grouped_ffn_mx) and
  * moe_pack_weights / moe_pack_router (one-time reorderings of resident expert
  * and router weights for faster reads), and moe_grouped_ffn_noalloc (the expert
@@ -382,6 +382,49 @@ int moe_route_dispatch(const void *x, int x_dtype, const void *w_router, int w_d
                        int E, int k, int e_begin, int e_end, int32_t *topk_ids, float *topk_w, int32_t *counts,
                        int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row, float *y_zero,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace moe_decode_layer needs: 256-byte aligned control words (one per local expert
+ * plus a few), then h [E_loc, T, I] bf16.
+ */
+size_t moe_decode_layer_workspace_size(int T, int k, int E_loc, int I);
+
+/*
+ * moe_decode_layer - the whole MoE layer of a decode batch in one launch.
+ *
+ * Defined by: "Hosting Qwen on Blackwell", section "Expert parallelism" (for decoding the whole
+ * MoE kernel is merged into one), with the steps of moe_route, moe_permute and moe_grouped_ffn
+ * (fused combine) as defined above.
+ *
+ * Results: topk_ids, topk_w exactly as moe_route; counts, offsets, row_token, row_w, token_row
+ * exactly as moe_permute (no x_perm); y [T,H] fp32 OVERWRITTEN with the layer output
+ *   y[t,:] = sum over the local assignments (t, j) of topk_w[t,j] * FFN_{topk_ids[t,j]}(x[t,:])
+ * with the FFN of moe_grouped_ffn (h rounded to bf16; fp32 atomic accumulation, so the order of a
+ * token's additions is not fixed).  One persistent launch: routing items, then gate/up items, then
+ * down items, taken from a work queue by at most as many workgroups as the device holds at once.
+ * The gate/up items compute h for every token of the batch (the one 64-row tile the weight stream
+ * pads to anyway) and do not wait for the routing, so the expert weights stream while the router
+ * runs; h [E_loc, T, I] is left in the workspace after the control words, and its rows of the
+ * routed (token, expert) pairs are bit-identical to moe_grouped_ffn's h with few rows per expert.
+ *
+ * x [T,H] MOE_BF16; w_router [E,H] MOE_BF16 or MOE_F32, or MOE_F32_ROUTER_PACKED (moe_pack_router);
+ * bias [E] or NULL; expert weights and scales as moe_grouped_ffn (MOE_BF16 or MOE_FP8_E4M3; flag
+ * MOE_FFN_PACKED_WEIGHTS for weights from moe_pack_weights; no other flag).  Supported sizes:
+ * 0 <= T <= 64 (decode batches; larger ones use moe_route_dispatch or moe_route + moe_permute, then
+ * moe_grouped_ffn), 1 <= k <= min(E, 32), E <= 256, H and I multiples of 64, H <= 16384; T == 0
+ * only zeroes counts and offsets.  Pointers 16-byte aligned.
+ * The workspace (moe_decode_layer_workspace_size bytes, 256-byte aligned) must be all zero before
+ * the first call (zero it once when allocating); every call leaves its control words zero again.
+ * Calls that share a workspace must not overlap (run them on one stream).  Its uint32 word 4
+ * (byte 16) is a diagnostic: nonzero if a wait inside the kernel gave up (never expected; the
+ * results of that call are then invalid); the library does not clear it.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP.
+ */
+int moe_decode_layer(const void *x, int x_dtype, const void *w_router, int wr_dtype, const float *bias, int T, int H,
+                     int E, int k, int e_begin, int e_end, int I, const void *w_gate_up, const void *w_down,
+                     int w_dtype, const float *s_gate_up, const float *s_down, int32_t *topk_ids, float *topk_w,
+                     int32_t *counts, int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
+                     float *y, void *workspace, size_t workspace_bytes, unsigned flags, void *stream);
 
 /* Bytes of workspace moe_shared_expert needs (h [T, I_s] of x_dtype, then its row maps). */
 size_t moe_shared_workspace_size(int T, int I_s, int x_dtype);

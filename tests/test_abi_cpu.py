@@ -282,3 +282,29 @@ def test_noalloc_limit_matches_header():
     # the largest decode-sized h that fits: 10922 rows of I = 1536 bf16 values
     assert moe.moe_ffn_workspace_size(10922, 128, 4096, 1536, moe.MOE_BF16) <= moe.MOE_NOALLOC_SCRATCH_BYTES
     assert moe.moe_ffn_workspace_size(10923, 128, 4096, 1536, moe.MOE_BF16) > moe.MOE_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=65), -2), (dict(H=96), -2), (dict(I=100), -2), (dict(E=257, hi=257), -2), (dict(k=0), -2),
+    (dict(lo=4, hi=4), -2), (dict(xd=0), -3), (dict(wrd=2), -3), (dict(wd=0), -3), (dict(flags=1), -2),
+    (dict(y=None), -1), (dict(wgu=None), -1), (dict(wd=2, sgu=None), -1), (dict(ws=None), -4), (dict(wsb=64), -4),
+    (dict(ws=P(0x1010)), -6), (dict(x=FAKE_ODD), -6),
+])
+def test_decode_layer_validation(kw, code):
+    # every case is refused on the host before anything is launched (no GPU needed)
+    a = dict(x=FAKE, xd=1, wr=FAKE, wrd=1, b=None, T=64, H=256, E=16, k=4, lo=0, hi=16, I=128, wgu=FAKE, wd=1,
+             wdown=FAKE, sgu=FAKE, sd=FAKE, ids=FAKE, gw=FAKE, c=FAKE, o=FAKE, rt=FAKE, rw=FAKE, tr=FAKE, y=FAKE,
+             ws=FAKE, wsb=1 << 30, flags=0)
+    a.update(kw)
+    wdt = a["wd"]
+    assert moe.lib().moe_decode_layer(a["x"], a["xd"], a["wr"], a["wrd"], a["b"], a["T"], a["H"], a["E"], a["k"],
+                                      a["lo"], a["hi"], a["I"], a["wgu"], a["wdown"], 2 if wdt == 2 else wdt,
+                                      a["sgu"], a["sd"], a["ids"], a["gw"], a["c"], a["o"], a["rt"], a["rw"], a["tr"],
+                                      a["y"], a["ws"], a["wsb"], a["flags"], None) == code
+
+
+def test_decode_layer_workspace_size():
+    L = moe.lib()
+    # control words (64 + E_loc, 256-byte aligned), then the dense h [E_loc, T, I] bf16
+    assert L.moe_decode_layer_workspace_size(64, 8, 128, 1536) == 768 + 128 * 64 * 1536 * 2
+    assert L.moe_decode_layer_workspace_size(1, 4, 16, 128) == 512 + 16 * 128 * 2

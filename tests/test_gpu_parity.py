@@ -439,13 +439,16 @@ def oracle_full_y(name):
     return y
 
 
-FULL_CASES = [(n, False) for n in ["decode", "prefill", "skew", "ep_share", "decode_shared", "prefill_shared"]]
-FULL_CASES += [(n, True) for n in ["decode", "prefill", "skew", "ep_share", "decode_shared", "prefill_shared"]]
+FULL_CASES = [(n, False, True) for n in ["decode", "prefill", "skew", "ep_share", "decode_shared", "prefill_shared"]]
+FULL_CASES += [(n, True, True) for n in ["decode", "prefill", "skew", "ep_share", "decode_shared", "prefill_shared"]]
+# the decode workloads also through the four-call path (route + dispatch launch, grouped FFN)
+FULL_CASES += [(n, p, False) for n in ["decode", "decode_shared"] for p in (False, True)]
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,packed", FULL_CASES, ids=[f"{n}{'_packed' if p else ''}" for n, p in FULL_CASES])
-def test_full_workload_layer(name, packed):
+@pytest.mark.parametrize("name,packed,one_launch", FULL_CASES,
+                         ids=[f"{n}{'_packed' if p else ''}{'' if o else '_4calls'}" for n, p, o in FULL_CASES])
+def test_full_workload_layer(name, packed, one_launch):
     """The layer as the benchmark launches it (same kernels, grid and tile walk), compared with the
     oracle on every one of the T x H outputs."""
     cfg = CONFIGS[name]
@@ -454,10 +457,11 @@ def test_full_workload_layer(name, packed):
     dev = L.to_device(inp)
     if packed:
         L.pack_weights(dev)
-    bufs = L.LayerBuffers(cfg)
-    if bufs.rd_ws is not None and packed:
+    bufs = L.LayerBuffers(cfg, use_decode_layer=one_launch)
+    if (bufs.rd_ws is not None or bufs.dec_ws is not None) and packed:
         L.pack_router(dev)
-    say(f"full layer {name}: run_layer fused={bufs.fused} R_cap={bufs.R_cap} packed={packed}")
+    say(f"full layer {name}: run_layer fused={bufs.fused} R_cap={bufs.R_cap} packed={packed} "
+        f"one_launch={bufs.dec_ws is not None}")
     y = L.run_layer(dev, bufs)
     torch.cuda.synchronize()
     ids, w = oracle_routing(cfg)
