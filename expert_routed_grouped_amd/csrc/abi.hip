@@ -12,6 +12,8 @@
 
 #define MOE_VERSION_NUMBER 100  // 0.1.0
 
+constexpr int kMaxExperts = 1024;  // experts of a layer (routing) and local experts of a call
+
 // Intermediate h of moe_grouped_ffn_noalloc, for callers that cannot allocate device memory.  Each
 // GPU the library runs on holds its own copy until the process ends; host code never passes the
 // array's name to a kernel (on the host it is only a stand-in), always the device address that
@@ -64,9 +66,25 @@ const char *moe_status_str(int status) {
   }
 }
 
+size_t moe_workspace_size(int op, int T, int k, int E_loc, int H, int I) {
+  if (T < 0 || k < 1 || E_loc < 1 || H < 1 || I < 1) return 0;
+  const int R_cap = (int)((long long)T * (k < E_loc ? k : E_loc));
+  switch (op) {
+    case MOE_OP_PERMUTE: return moe_permute_workspace_size(T, k, E_loc);
+    case MOE_OP_GROUPED_FFN: return moe_ffn_workspace_size(R_cap, E_loc, H, I, MOE_BF16);
+    case MOE_OP_GROUPED_FFN_F32: return moe_ffn_workspace_size(R_cap, E_loc, H, I, MOE_F32);
+    case MOE_OP_GROUPED_FFN_MX: return moe_ffn_mx_workspace_size(R_cap, I);
+    case MOE_OP_ROUTE_DISPATCH: return moe_route_dispatch_workspace_size();
+    case MOE_OP_DECODE_LAYER: return moe_decode_layer_workspace_size(T, k, E_loc, I);
+    case MOE_OP_SHARED_EXPERT: return moe_shared_workspace_size(T, I, MOE_BF16);
+    case MOE_OP_SHARED_EXPERT_F32: return moe_shared_workspace_size(T, I, MOE_F32);
+    default: return 0;
+  }
+}
+
 int moe_route(const void *x, int x_dtype, const void *w_router, int w_dtype, const float *bias, int T, int H, int E,
               int k, int32_t *topk_ids, float *topk_w, void *stream) {
-  if (T < 0 || H < 1 || E < 1 || E > 512 || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
+  if (T < 0 || H < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
   if ((long long)T * k >= (1LL << 31) || (long long)T * H >= (1LL << 40)) return MOE_ERR_SHAPE;
   if ((x_dtype != MOE_F32 && x_dtype != MOE_BF16) || (w_dtype != MOE_F32 && w_dtype != MOE_BF16)) return MOE_ERR_DTYPE;
   if (T == 0) return MOE_OK;
@@ -78,7 +96,7 @@ int moe_route(const void *x, int x_dtype, const void *w_router, int w_dtype, con
 size_t moe_route_dispatch_workspace_size(void) { return 256; }
 
 int moe_pack_router(const void *w_router, int w_dtype, int E, int H, float *out, void *stream) {
-  if (E < 1 || E > 512 || H < 4 || H % 4 != 0) return MOE_ERR_SHAPE;
+  if (E < 1 || E > kMaxExperts || H < 4 || H % 4 != 0) return MOE_ERR_SHAPE;
   if (w_dtype != MOE_F32 && w_dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (!w_router || !out) return MOE_ERR_NULL;
   if (((uintptr_t)w_router & (w_dtype == MOE_BF16 ? 1u : 3u)) != 0 || !aligned16(out)) return MOE_ERR_ALIGN;
@@ -89,7 +107,7 @@ int moe_route_dispatch(const void *x, int x_dtype, const void *w_router, int w_d
                        int E, int k, int e_begin, int e_end, int32_t *topk_ids, float *topk_w, int32_t *counts,
                        int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row, float *y_zero,
                        void *workspace, size_t workspace_bytes, void *stream) {
-  if (T < 0 || H < 1 || E < 1 || E > 512 || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
+  if (T < 0 || H < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
   if (e_begin < 0 || e_end <= e_begin || e_end > E) return MOE_ERR_SHAPE;
   if ((x_dtype != MOE_F32 && x_dtype != MOE_BF16) ||
       (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_F32_ROUTER_PACKED))
@@ -174,7 +192,7 @@ int moe_permute(const int32_t *topk_ids, const float *topk_w, int T, int k, int 
                 int32_t *counts, int32_t *offsets, int32_t *row_token, float *row_w, int32_t *token_row,
                 const void *x, int x_dtype, int H, void *x_perm, void *workspace, size_t workspace_bytes,
                 void *stream) {
-  if (T < 0 || E < 1 || E > 512 || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
+  if (T < 0 || E < 1 || E > kMaxExperts || k < 1 || k > E || k > 32) return MOE_ERR_SHAPE;
   if (e_begin < 0 || e_end <= e_begin || e_end > E) return MOE_ERR_SHAPE;
   if ((long long)T * k >= (1LL << 31)) return MOE_ERR_SHAPE;
   if (!counts || !offsets) return MOE_ERR_NULL;
@@ -223,7 +241,7 @@ int grouped_ffn(const void *a, int a_dtype, const int32_t *offsets, const int32_
                 const float *s_gate_up, const float *s_down, float *y, float *y_perm, void *workspace,
                 size_t workspace_bytes, unsigned flags, void *stream, bool static_scratch = false) {
   if (static_scratch) workspace_bytes = MOE_NOALLOC_SCRATCH_BYTES;
-  if (T < 0 || R_cap < 0 || E_loc < 1 || E_loc > 512 || H < 64 || I < 64 || H % 64 != 0 || I % 64 != 0)
+  if (T < 0 || R_cap < 0 || E_loc < 1 || E_loc > kMaxExperts || H < 64 || I < 64 || H % 64 != 0 || I % 64 != 0)
     return MOE_ERR_SHAPE;
   if ((long long)R_cap > (long long)T * E_loc) return MOE_ERR_SHAPE;
   // the tile kernels address a row-major operand with 32-bit byte offsets (rows x dim x 4 < 2^32)
@@ -425,7 +443,7 @@ int moe_grouped_ffn_mx(const uint8_t *a_codes, const uint8_t *a_scales, const in
                        const uint8_t *wgu_codes, const uint8_t *wgu_scales, const uint8_t *wd_codes,
                        const uint8_t *wd_scales, float *y, float *y_perm, void *workspace, size_t workspace_bytes,
                        unsigned flags, void *stream) {
-  if (T < 0 || R_cap < 0 || E_loc < 1 || E_loc > 512 || H < 128 || I < 128 || H % 128 != 0 || I % 128 != 0)
+  if (T < 0 || R_cap < 0 || E_loc < 1 || E_loc > kMaxExperts || H < 128 || I < 128 || H % 128 != 0 || I % 128 != 0)
     return MOE_ERR_SHAPE;
   if ((long long)R_cap > (long long)T * E_loc) return MOE_ERR_SHAPE;
   if ((long long)(T > R_cap ? T : R_cap) * (H > I ? H : I) >= (1LL << 30) || (long long)H * I >= (1LL << 30))

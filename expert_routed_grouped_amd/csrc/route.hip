@@ -17,11 +17,15 @@ namespace {
 
 using namespace rt;
 
+// Up to 1024 experts: 16 waves per block (four per SIMD) leave 128 registers per lane, so the weight
+// ring is half as deep there.
 template <int TT, int EC, bool XB, bool WB, bool VEC>
 __global__ __launch_bounds__(64 * EC) void route_kernel(const void *__restrict__ x, const void *__restrict__ w,
                                                         const float *__restrict__ bias, int T, int H, int E, int k,
                                                         int32_t *__restrict__ ids, float *__restrict__ gates) {
-  route_tokens<TT, EC, XB, WB, VEC>(x, w, bias, T, H, E, k, ids, gates, blockIdx.x * TT, blockIdx.x, gridDim.x);
+  constexpr int ring = EC >= 16 ? ROUTE_NS / 2 : ROUTE_NS;
+  route_tokens<TT, EC, XB, WB, VEC, false, ring>(x, w, bias, T, H, E, k, ids, gates, blockIdx.x * TT, blockIdx.x,
+                                                 gridDim.x);
 }
 
 // Decode route + local dispatch in one launch: block t routes token t (as route_kernel with one
@@ -288,7 +292,11 @@ hipError_t launch_route(const void *x, int x_bf16, const void *w, int w_bf16, co
     case 2: return launch_ec<2>(x, x_bf16, w, w_bf16, bias, T, H, E, k, ids, gates, s);
     case 3:
     case 4: return launch_ec<4>(x, x_bf16, w, w_bf16, bias, T, H, E, k, ids, gates, s);
-    default: return launch_ec<8>(x, x_bf16, w, w_bf16, bias, T, H, E, k, ids, gates, s);
+    case 5:
+    case 6:
+    case 7:
+    case 8: return launch_ec<8>(x, x_bf16, w, w_bf16, bias, T, H, E, k, ids, gates, s);
+    default: return launch_ec<16>(x, x_bf16, w, w_bf16, bias, T, H, E, k, ids, gates, s);
   }
 }
 

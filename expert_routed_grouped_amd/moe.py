@@ -27,7 +27,9 @@ EXPORTS = ("moe_version", "moe_status_str", "moe_route", "moe_permute", "moe_per
            "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine", "moe_quantize_mx", "moe_ffn_mx_workspace_size",
            "moe_grouped_ffn_mx", "moe_shared_workspace_size", "moe_shared_expert", "moe_route_dispatch_workspace_size",
            "moe_route_dispatch", "moe_pack_weights", "moe_pack_router", "moe_grouped_ffn_noalloc",
-           "moe_decode_layer_workspace_size", "moe_decode_layer")
+           "moe_decode_layer_workspace_size", "moe_decode_layer", "moe_workspace_size")
+MOE_OP_PERMUTE, MOE_OP_GROUPED_FFN, MOE_OP_GROUPED_FFN_F32, MOE_OP_GROUPED_FFN_MX = 0, 1, 2, 3
+MOE_OP_ROUTE_DISPATCH, MOE_OP_DECODE_LAYER, MOE_OP_SHARED_EXPERT, MOE_OP_SHARED_EXPERT_F32 = 4, 5, 6, 7
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -64,6 +66,8 @@ def lib():
         L.moe_grouped_ffn.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, P, Z, ctypes.c_uint, P]
         L.moe_grouped_ffn_noalloc.restype = I
         L.moe_grouped_ffn_noalloc.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P, I, P, P, P, P, ctypes.c_uint, P]
+        L.moe_workspace_size.restype = Z
+        L.moe_workspace_size.argtypes = [I, I, I, I, I, I]
         L.moe_decode_layer_workspace_size.restype = Z
         L.moe_decode_layer_workspace_size.argtypes = [I, I, I, I]
         L.moe_decode_layer.restype = I
@@ -175,6 +179,11 @@ def moe_permute(topk_ids: torch.Tensor, topk_w: torch.Tensor, E: int, e_begin: i
                                             o["workspace"].numel() * o["workspace"].element_size(), _stream(stream)))
     o["R_cap"] = R_cap
     return o
+
+
+def moe_workspace_size(op: int, T: int, k: int, E_loc: int, H: int, I: int) -> int:
+    """Bytes of workspace one call of ``op`` (MOE_OP_*) needs."""
+    return int(lib().moe_workspace_size(op, T, k, E_loc, H, I))
 
 
 def moe_permute_workspace_size(T: int, k: int, E_loc: int) -> int:

@@ -50,7 +50,7 @@
  *    the contraction axis, in a separate uint8 array [rows, K/32]; used by
  *    moe_quantize_mx and moe_grouped_ffn_mx).
  *  - Sizes: T >= 0 tokens, hidden H, E experts with 1 <= k <= min(E, 32),
- *    E <= 512, intermediate I.  Local experts are [e_begin, e_end) with
+ *    E <= 1024, intermediate I.  Local experts are [e_begin, e_end) with
  *    E_loc = e_end - e_begin >= 1; R_cap = T * min(k, E_loc) bounds the number
  *    of local assignments, so every row buffer is sized without knowing the
  *    routing on the host.
@@ -90,11 +90,30 @@ extern "C" {
 #define MOE_FFN_PACKED_WEIGHTS 16u /* w_gate_up and w_down are in the packed block layout that
                                       moe_pack_weights writes (bf16 and fp8 weights only) */
 
+/* moe_workspace_size operations */
+#define MOE_OP_PERMUTE 0          /* moe_permute */
+#define MOE_OP_GROUPED_FFN 1      /* moe_grouped_ffn / moe_shared_expert with bf16 activations */
+#define MOE_OP_GROUPED_FFN_F32 2  /* moe_grouped_ffn / moe_shared_expert with fp32 activations */
+#define MOE_OP_GROUPED_FFN_MX 3   /* moe_grouped_ffn_mx */
+#define MOE_OP_ROUTE_DISPATCH 4   /* moe_route_dispatch */
+#define MOE_OP_DECODE_LAYER 5     /* moe_decode_layer */
+#define MOE_OP_SHARED_EXPERT 6    /* moe_shared_expert with bf16 activations (I = I_s, E_loc and k unused) */
+#define MOE_OP_SHARED_EXPERT_F32 7 /* moe_shared_expert with fp32 activations */
+
 /* Library version (major*10000 + minor*100 + patch). */
 int moe_version(void);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char *moe_status_str(int status);
+
+/*
+ * Bytes of workspace one call of operation ``op`` (MOE_OP_*) needs for T tokens, top-k, E_loc local
+ * experts, hidden H and intermediate I (row buffers sized by R_cap = T * min(k, E_loc)); the same
+ * numbers as the per-call functions below (moe_permute_workspace_size, moe_ffn_workspace_size,
+ * moe_ffn_mx_workspace_size, moe_route_dispatch_workspace_size, moe_decode_layer_workspace_size,
+ * moe_shared_workspace_size).  0 for an unknown op or sizes out of range.
+ */
+size_t moe_workspace_size(int op, int T, int k, int E_loc, int H, int I);
 
 /*
  * moe_route - router GEMM, top-k selection and renormalised gates.
@@ -115,7 +134,7 @@ const char *moe_status_str(int status);
  * x [T,H] and w_router [E,H]: MOE_F32 or MOE_BF16 each; bias [E] fp32 or NULL.
  * Outputs topk_ids [T,k] int32 and topk_w [T,k] fp32 are overwritten.
  * Errors: MOE_ERR_NULL (x, w_router, topk_ids or topk_w NULL with T > 0),
- * MOE_ERR_SHAPE (T < 0, H < 1, E < 1 or E > 512, k < 1, k > min(E, 32)),
+ * MOE_ERR_SHAPE (T < 0, H < 1, E < 1 or E > 1024, k < 1, k > min(E, 32)),
  * MOE_ERR_DTYPE, MOE_ERR_HIP.  T == 0 enqueues nothing.
  */
 int moe_route(const void *x, int x_dtype, const void *w_router, int w_dtype, const float *bias,
@@ -145,7 +164,7 @@ int moe_route(const void *x, int x_dtype, const void *w_router, int w_dtype, con
  * MOE_BF16), 16-byte aligned, H a multiple of 8.  topk_ids must hold distinct
  * experts per token in [0, E) (as moe_route writes them).  workspace: at least
  * moe_permute_workspace_size(T, k, E_loc) bytes, 256-byte aligned.
- * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (0 <= e_begin < e_end <= E, E <= 512,
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (0 <= e_begin < e_end <= E, E <= 1024,
  * 1 <= k <= min(E,32), T*k < 2^31), MOE_ERR_DTYPE, MOE_ERR_ALIGN,
  * MOE_ERR_WORKSPACE, MOE_ERR_HIP.
  */
@@ -345,7 +364,7 @@ int moe_combine(const float *y_perm, const int32_t *token_row, const float *topk
  * each) then read 1 KB contiguously per load and unpack nothing.  Done once,
  * like loading the weights (it costs E*H*4 bytes of HBM).  w_router [E,H]
  * MOE_BF16 or MOE_F32 (element-aligned); out 16-byte aligned, caller-owned,
- * not overlapping w_router; H a multiple of 4, 1 <= E <= 512.  Errors:
+ * not overlapping w_router; H a multiple of 4, 1 <= E <= 1024.  Errors:
  * MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_HIP.
  */
 int moe_pack_router(const void *w_router, int w_dtype, int E, int H, float *out, void *stream);

@@ -48,7 +48,7 @@ def route(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(k=0), -2), (dict(k=9), -2), (dict(E=513, k=2), -2), (dict(E=64, k=33), -2), (dict(T=-1), -2),
+    (dict(k=0), -2), (dict(k=9), -2), (dict(E=1025, k=2), -2), (dict(E=64, k=33), -2), (dict(T=-1), -2),
     (dict(H=0), -2), (dict(xd=2), -3), (dict(wd=7), -3), (dict(x=None), -1), (dict(ids=None), -1),
     (dict(gw=None), -1), (dict(T=0), 0),
 ])
@@ -65,7 +65,7 @@ def permute(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(lo=3, hi=3), -2), (dict(lo=-1), -2), (dict(hi=9), -2), (dict(k=9), -2), (dict(E=600, hi=600), -2),
+    (dict(lo=3, hi=3), -2), (dict(lo=-1), -2), (dict(hi=9), -2), (dict(k=9), -2), (dict(E=1100, hi=1100), -2),
     (dict(c=None), -1), (dict(rt=None), -1), (dict(x=FAKE), -1), (dict(xp=FAKE), -1),
     (dict(x=FAKE, xp=FAKE, H=12), -2), (dict(x=FAKE, xp=FAKE, H=64, xd=2), -3),
     (dict(x=FAKE_ODD, xp=FAKE, H=64), -6), (dict(ws=None), -4), (dict(wsb=0), -4), (dict(ws=P(0x1010)), -6),
@@ -152,7 +152,7 @@ def test_pack_weights_validation(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dt=2), -3), (dict(dt=4), -3), (dict(E=0), -2), (dict(E=513), -2), (dict(H=6), -2), (dict(H=0), -2),
+    (dict(dt=2), -3), (dict(dt=4), -3), (dict(E=0), -2), (dict(E=1025), -2), (dict(H=6), -2), (dict(H=0), -2),
     (dict(w=None), -1), (dict(out=None), -1), (dict(w=P(0x1001)), -6), (dict(out=P(0x9008)), -6),
     (dict(dt=0, w=P(0x1002)), -6),
 ])
@@ -308,3 +308,24 @@ def test_decode_layer_workspace_size():
     # control words (64 + E_loc, 256-byte aligned), then the dense h [E_loc, T, I] bf16
     assert L.moe_decode_layer_workspace_size(64, 8, 128, 1536) == 768 + 128 * 64 * 1536 * 2
     assert L.moe_decode_layer_workspace_size(1, 4, 16, 128) == 512 + 16 * 128 * 2
+
+
+@pytest.mark.parametrize("T,k,El,H,I", [(6000, 8, 128, 4096, 1536), (64, 8, 128, 4096, 1536), (1, 1, 1, 64, 64),
+                                        (8192, 8, 32, 4096, 1536), (0, 4, 16, 256, 128), (70, 32, 1024, 256, 64)])
+def test_workspace_size_by_operation(T, k, El, H, I):
+    # moe_workspace_size(op, ...) gives the per-call functions' numbers
+    L = moe.lib()
+    R = T * min(k, El)
+    assert moe.moe_workspace_size(moe.MOE_OP_PERMUTE, T, k, El, H, I) == L.moe_permute_workspace_size(T, k, El)
+    assert moe.moe_workspace_size(moe.MOE_OP_GROUPED_FFN, T, k, El, H, I) == moe.moe_ffn_workspace_size(R, El, H, I, 1)
+    assert (moe.moe_workspace_size(moe.MOE_OP_GROUPED_FFN_F32, T, k, El, H, I)
+            == moe.moe_ffn_workspace_size(R, El, H, I, 0))
+    assert moe.moe_workspace_size(moe.MOE_OP_GROUPED_FFN_MX, T, k, El, H, I) == moe.moe_ffn_mx_workspace_size(R, I)
+    assert moe.moe_workspace_size(moe.MOE_OP_ROUTE_DISPATCH, T, k, El, H, I) == 256
+    assert (moe.moe_workspace_size(moe.MOE_OP_DECODE_LAYER, T, k, El, H, I)
+            == L.moe_decode_layer_workspace_size(T, k, El, I))
+    assert moe.moe_workspace_size(moe.MOE_OP_SHARED_EXPERT, T, k, El, H, I) == moe.moe_shared_workspace_size(T, I, 1)
+    assert (moe.moe_workspace_size(moe.MOE_OP_SHARED_EXPERT_F32, T, k, El, H, I)
+            == moe.moe_shared_workspace_size(T, I, 0))
+    assert moe.moe_workspace_size(99, T, k, El, H, I) == 0
+    assert moe.moe_workspace_size(moe.MOE_OP_PERMUTE, -1, k, El, H, I) == 0

@@ -92,6 +92,9 @@ ROUTE_CASES = [
     LayerConfig("r_k1", T=513, H=64, E=64, k=1, I=64, seed=105),
     # 16 tokens per workgroup (at least 512 workgroups), the last one partly empty
     LayerConfig("r_tr4_ragged", T=8195, H=256, E=128, k=8, I=64, seed=106, w_std=0.05),
+    # up to 1024 experts: 16 router waves, one and four tokens per workgroup
+    LayerConfig("r_E1024", T=70, H=256, E=1024, k=8, I=64, seed=107, w_std=0.05),
+    LayerConfig("r_E1000_t600", T=600, H=192, E=1000, k=32, I=64, seed=108, w_std=0.05),
 ]
 
 
@@ -283,6 +286,8 @@ FFN_CASES = [
                 w_std=0.05),
     # one hot expert with more than 64 rows: several 64-row tiles and both 32-row blocks
     LayerConfig("stream_hot", T=120, H=256, E=16, k=2, I=128, bias="zipf", seed=209, w_std=0.05),
+    # many experts: 1000 routed, 600 of them local (mostly empty experts, a few rows each)
+    LayerConfig("many_experts", T=300, H=128, E=1000, k=8, I=64, e_begin=200, e_end=800, seed=210, w_std=0.05),
 ]
 
 
