@@ -17,6 +17,7 @@ struct TileParams {
   int ksplit;             // weight-streaming kernel: K slices per tile (0 or 1: none)
   float *gu32;            // with ksplit > 1: fp32 G and U partial sums [R_cap, 2I], zeroed beforehand
   int wpacked;            // weights in 32-row x 64-k blocks (moe_pack_weights) instead of row-major
+  int T;                  // tokens (rows of x when the gate/up half gathers)
 };
 
 // Byte offset of weight row ``row`` (counted over all experts of the tensor) at k = 0, and the

@@ -1,153 +1,215 @@
 // Grouped FFN tiles for large batches with bf16 weights: operands move from
-// HBM/L2 straight into LDS (global_load_lds, no register staging).
+// HBM/L2 straight into LDS (buffer_load ... lds, no register staging).
 //
 // Tile: up to 256 rows of one expert x 256 weight rows, K step 64 (one full
 // 128-byte line per row and step).  An expert with c rows is cut into
 // m = ceil(c / 256) M tiles of equal size rounded up to 64 rows, so an expert
 // of 375 rows runs as two tiles of 192 rows rather than 256 + 119.  Eight
-// waves as 2 (M) x 4 (N); each wave owns half the tile rows x 64 weight rows
-// as up to 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (fp32 accumulation).
-// Gate/up tiles hold the gate rows and the up rows of the same 128
-// intermediate columns, so the SwiGLU epilogue finds G and U of one output in
-// the same lane and register.
+// waves, two per SIMD, as 2 (M) x 4 (N); each wave owns half the tile rows x
+// 64 weight rows as up to 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (fp32
+// accumulation).  Gate/up tiles hold the gate rows and the up rows of the same
+// 128 intermediate columns, so the SwiGLU epilogue finds G and U of one output
+// in the same lane and register.
 //
 // Pipeline: the weight operand, whose first touch comes from HBM, is fetched
 // two K steps ahead through a three-slot ring; the activation rows, mostly L2
 // hits, one step ahead through a two-slot ring (2 x 32 KB + 3 x 32 KB = 160 KB
 // of LDS, one workgroup per CU).  The loads of the next steps are issued
-// between the MFMAs of the current step, two per 16-wide K slice, so no wave
-// stalls on a long burst of memory instructions.  Per K step: wait until this
-// wave's loads of the step have landed (vmcnt; loads retire in issue order),
-// one barrier (everyone's loads have landed and nobody still reads the slots
-// about to be refilled), then MFMAs.  The barrier carries no memory fence: a
-// fence would drain every load still in flight.
+// between the MFMAs of the current step, and the fragments of the next 16-wide
+// K slice are read while the MFMAs of the current one run.  Per K step: wait
+// until this wave's loads of the step have landed (vmcnt; loads retire in
+// issue order), one barrier (everyone's loads have landed and nobody still
+// reads the slots about to be refilled), then MFMAs.  The barrier carries no
+// memory fence: a fence would drain every load still in flight.
+//
+// Instruction economy of the K loop (it runs at the chip's power limit, so
+// every issued instruction costs MFMA clock): the loads are buffer loads whose
+// per-lane byte offset is fixed for the whole tile and whose K advance is one
+// scalar offset, and the LDS destination (M0) is scalar arithmetic; the loop is
+// unrolled over the lcm of the two ring lengths (6 steps), so every fragment
+// read is a precomputed per-lane base plus an immediate offset.  The loop body
+// then holds MFMAs, LDS reads, loads and a few scalar instructions only.
 //
 // LDS rows are 64 bf16 = eight 16-byte chunks; chunk c of row r sits in slot
 // c ^ ((r >> 1) & 7), which keeps the 16 lanes of one LDS cycle on 16 distinct
-// 16-byte bank groups when they read one chunk of 16 consecutive rows.  A
-// global_load_lds writes the 16 bytes of lane i to slot i of a 1 KB segment
-// (8 rows), so every lane fetches the global chunk that belongs to its slot.
+// 16-byte bank groups when they read one chunk of 16 consecutive rows.  A load
+// to LDS writes the 16 bytes of lane i to slot i of a 1 KB segment (8 rows), so
+// every lane fetches the global chunk that belongs to its slot.
 //
 // Rows past the expert's count are never multiplied: the K loop is
-// instantiated for 0..4 active 32-row blocks per wave.
+// instantiated for 0..4 active 32-row blocks per wave.  The fp32 sums of every
+// output run over K in the same order as in a plain 16-wide-slice MFMA chain.
 #include "ffn_common.h"
+
+#include <type_traits>
 
 namespace {
 
 using ffn::TileParams;
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 512;
+constexpr int BM = 256, BN = 256, BK = 64, NWAVE = 8, NTHR = 64 * NWAVE;
+constexpr int WN = NWAVE / 2;                         // waves along N (two along M)
 constexpr int A_BYTES = BM * BK * 2;                  // 32 KB: one activation slot
 constexpr int B_BYTES = BN * BK * 2;                  // 32 KB: one weight slot
 constexpr int LDS_BYTES = 2 * A_BYTES + 3 * B_BYTES;  // 160 KB
-
-__device__ __forceinline__ int lds_off64(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+constexpr int NB = 8 / WN;                            // 32-row weight blocks per wave
+constexpr int B_SEG = BN / 8 / NWAVE;                 // weight segments (1 KB) per wave and K step
+constexpr int A_SEG = BM / 8 / NWAVE;                 // most activation segments per wave and K step
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 struct DmaSrc {
-  uint32_t aoff[4], boff[4];  // byte offsets of this lane's A and B segments at K step 0
-  uint32_t bstep;             // bytes from one K step of the weights to the next (row-major or packed)
+  __amdgpu_buffer_rsrc_t ra, rb;  // buffer resources: activations (whole tensor), this expert's weights
+  uint32_t aoff[A_SEG], boff[B_SEG];  // byte offsets of this lane's A and B segments at K step 0
+  uint32_t bstep;                 // bytes from one K step of the weights to the next (row-major or packed)
 };
 
-template <int NMB>
-__device__ __forceinline__ void dma_kloop(const char *abase, const char *bbase, const DmaSrc &src, int nA, int K,
-                                          int wave, int lane, int arow0, int wn, char *lds,
-                                          f32x16_t (&acc)[NMB > 0 ? NMB : 1][2]) {
-  const int KT = K / BK;
-  // A of step kt lives in A slot kt % 2, B of step kt in B slot kt % 3.  Within a step every A load
-  // is issued before any B load, so once only the four B loads of step kt+1 are in flight, all of
-  // step kt has landed.
-  auto loadA = [&](int kt, int u) __attribute__((always_inline)) {
-    if (u < nA)
-      __builtin_amdgcn_global_load_lds((const void *)(abase + (size_t)kt * BK * 2 + src.aoff[u]),
-                                       (lds_void *)(lds + (kt & 1) * A_BYTES + (wave + 8 * u) * 1024), 16, 0, 0);
+constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+// One K step with compile-time ring slots: P = kt % 6 (A slot P % 2, B slot P % 3).
+template <int NMB, int P>
+__device__ __forceinline__ void dma_step(int kt, bool nextA, bool nextB, const DmaSrc &src, int nA, int wave,
+                                         const uint32_t (&abase)[4], const uint32_t (&bbase)[3][4], char *lds,
+                                         f32x16_t (&acc)[NMB > 0 ? NMB : 1][NB]) {
+  constexpr int NA = NMB > 0 ? NMB : 1;
+  constexpr int SA = P % 2, SB = P % 3, SA1 = (P + 1) % 2, SB2 = (P + 2) % 3;
+  auto frags = [&](int kk, bf16x8_t (&af)[NA], bf16x8_t (&bf)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NB; j++) bf[j] = *(const bf16x8_t *)(lds + bbase[SB][kk] + j * 4096);
+#pragma unroll
+    for (int i = 0; i < NA; i++) af[i] = *(const bf16x8_t *)(lds + abase[kk] + SA * A_BYTES + i * 4096);
   };
-  auto loadB = [&](int kt, int u) __attribute__((always_inline)) {
-    __builtin_amdgcn_global_load_lds((const void *)(bbase + (size_t)kt * src.bstep + src.boff[u]),
-                                     (lds_void *)(lds + 2 * A_BYTES + (kt % 3) * B_BYTES + (wave + 8 * u) * 1024), 16, 0,
-                                     0);
-  };
-  auto step = [&](int kt, bool nextA, bool nextB) __attribute__((always_inline)) {
-    const char *A = lds + (kt & 1) * A_BYTES, *B = lds + 2 * A_BYTES + (kt % 3) * B_BYTES;
+  bf16x8_t af[2][NA], bf[2][NB];
+  if constexpr (NMB > 0) frags(0, af[0], bf[0]);
+  const uint32_t soA = (uint32_t)(kt + 1) * (BK * 2), soB = (uint32_t)(kt + 2) * src.bstep;
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) {
-      const int ch = kk * 2 + (lane >> 5);
-      bf16x8_t bf[2], af[NMB > 0 ? NMB : 1];
-      if constexpr (NMB > 0) {
+  for (int kk = 0; kk < 4; kk++) {
+    if constexpr (NMB > 0) {
+      if (kk < 3) frags(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+    }
+    if (kk < 2) {
+      if (nextA) {
 #pragma unroll
-        for (int j = 0; j < 2; j++) bf[j] = *(const bf16x8_t *)(B + lds_off64(wn * 64 + j * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int i = 0; i < NMB; i++) af[i] = *(const bf16x8_t *)(A + lds_off64(arow0 + i * 32 + (lane & 31), ch));
-      }
-      if (kk < 2) {
-        if (nextA) {
-          loadA(kt + 1, 2 * kk);
-          loadA(kt + 1, 2 * kk + 1);
+        for (int v = 0; v < (A_SEG + 1) / 2; v++) {
+          const int u = (A_SEG + 1) / 2 * kk + v;
+          if (u < nA)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                src.ra, (lds_void *)(lds + SA1 * A_BYTES + (wave + NWAVE * u) * 1024), 16, src.aoff[u], soA, 0, 0);
         }
-      } else if (nextB) {
-        loadB(kt + 2, 2 * (kk - 2));
-        loadB(kt + 2, 2 * (kk - 2) + 1);
       }
-      if constexpr (NMB > 0) {
+    } else if (nextB) {
 #pragma unroll
-        for (int i = 0; i < NMB; i++)
-#pragma unroll
-          for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      for (int v = 0; v < B_SEG / 2; v++) {
+        const int u = B_SEG / 2 * (kk - 2) + v;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            src.rb, (lds_void *)(lds + 2 * A_BYTES + SB2 * B_BYTES + (wave + NWAVE * u) * 1024), 16, src.boff[u], soB,
+            0, 0);
       }
     }
-  };
+    if constexpr (NMB > 0) {
 #pragma unroll
-  for (int u = 0; u < 4; u++) loadB(0, u);
+      for (int i = 0; i < NMB; i++)
 #pragma unroll
-  for (int u = 0; u < 4; u++) loadA(0, u);
+        for (int j = 0; j < NB; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bf[kk & 1][j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+template <int NMB>
+__device__ __forceinline__ void dma_kloop(const DmaSrc &src, int nA, int K, int wave, int lane, int arow0, int wn,
+                                          char *lds, f32x16_t (&acc)[NMB > 0 ? NMB : 1][NB]) {
+  const int KT = K / BK;
+  // LDS byte offsets of this lane's fragments: row r, 16-byte chunk ch = 2 kk + lane / 32 at slot
+  // ch ^ ((r >> 1) & 7); rows of one lane differ by multiples of 32, which leave that XOR alone.
+  uint32_t abase[4], bbase[3][4];
+  {
+    const int r = lane & 31, sw = (r >> 1) & 7, g = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      const uint32_t o = (uint32_t)(((2 * kk + g) ^ sw) << 4);
+      abase[kk] = (uint32_t)(arow0 + r) * 128u + o;
+#pragma unroll
+      for (int s = 0; s < 3; s++)
+        bbase[s][kk] = 2u * A_BYTES + (uint32_t)s * B_BYTES + (uint32_t)(wn * NB * 32 + r) * 128u + o;
+    }
+  }
+  // A of step kt lives in A slot kt % 2, B of step kt in B slot kt % 3.  Within a step every A load
+  // is issued before any B load, so once only the B loads of step kt+1 are in flight, all of step
+  // kt has landed.
+#pragma unroll
+  for (int u = 0; u < B_SEG; u++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rb, (lds_void *)(lds + 2 * A_BYTES + (wave + NWAVE * u) * 1024), 16,
+                                             src.boff[u], 0, 0, 0);
+#pragma unroll
+  for (int u = 0; u < A_SEG; u++)
+    if (u < nA)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.ra, (lds_void *)(lds + (wave + NWAVE * u) * 1024), 16,
+                                               src.aoff[u], 0, 0, 0);
   if (KT > 1) {
 #pragma unroll
-    for (int u = 0; u < 4; u++) loadB(1, u);
+    for (int u = 0; u < B_SEG; u++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          src.rb, (lds_void *)(lds + 2 * A_BYTES + B_BYTES + (wave + NWAVE * u) * 1024), 16, src.boff[u], src.bstep,
+          0, 0);
   }
-  for (int kt = 0; kt < KT; kt++) {
-    if (kt + 1 < KT) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    barrier_no_fence();
-    step(kt, kt + 1 < KT, kt + 2 < KT);
+  auto one = [&](auto PC, int kt) __attribute__((always_inline)) {
+    constexpr int P = decltype(PC)::value;
+    if (kt < KT) {
+      if (kt + 1 < KT) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(B_SEG) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      barrier_no_fence();
+      dma_step<NMB, P>(kt, kt + 1 < KT, kt + 2 < KT, src, nA, wave, abase, bbase, lds, acc);
+    }
+  };
+  for (int kt = 0; kt < KT; kt += 6) {
+    one(std::integral_constant<int, 0>{}, kt);
+    one(std::integral_constant<int, 1>{}, kt + 1);
+    one(std::integral_constant<int, 2>{}, kt + 2);
+    one(std::integral_constant<int, 3>{}, kt + 3);
+    one(std::integral_constant<int, 4>{}, kt + 4);
+    one(std::integral_constant<int, 5>{}, kt + 5);
   }
 }
 
 template <int MODE, bool ATOMIC, int NMB>
-__device__ __forceinline__ void dma_body(const TileParams &p, const char *abase, const char *bbase, const DmaSrc &src,
+__device__ __forceinline__ void dma_body(const TileParams &p, const DmaSrc &src,
                                          int nA, int K, int nt, int rbase, int mvalid, int wave, int lane, int arow0,
                                          int wn, char *lds) {
   constexpr int NA = NMB > 0 ? NMB : 1;
-  f32x16_t acc[NA][2];
+  f32x16_t acc[NA][NB];
 #pragma unroll
   for (int i = 0; i < NA; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < NB; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
-  dma_kloop<NMB>(abase, bbase, src, nA, K, wave, lane, arow0, wn, lds, acc);
+  dma_kloop<NMB>(src, nA, K, wave, lane, arow0, wn, lds, acc);
   if constexpr (NMB > 0) {
     // acc[i][j][r] at lane l is tile row arow0 + i*32 + 8*(r/4) + 4*(l/32) + r%4,
-    // weight row wn*64 + j*32 + l%32 of the tile
+    // weight row wn*128 + j*32 + l%32 of the tile
     if constexpr (MODE == 0) {
-      if (nt * 128 + wn * 32 >= p.I) return;
-      const int col = nt * 128 + wn * 32 + (lane & 31);  // intermediate index
       uint16_t *hout = (uint16_t *)p.out;
 #pragma unroll
-      for (int i = 0; i < NA; i++)
+      for (int q = 0; q < NB / 2; q++) {  // blocks 2q (gate) and 2q+1 (up) of the same 32 columns
+        const int col = nt * 128 + wn * NB * 16 + q * 32 + (lane & 31);  // intermediate index
+        if (col - (lane & 31) >= p.I) continue;
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (m < mvalid)
-            hout[(size_t)(rbase + m) * p.I + col] = f32_to_bf16(silu_fast(acc[i][0][r]) * acc[i][1][r]);
-        }
+        for (int i = 0; i < NA; i++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m < mvalid)
+              hout[(size_t)(rbase + m) * p.I + col] = f32_to_bf16(silu_fast(acc[i][2 * q][r]) * acc[i][2 * q + 1][r]);
+          }
+      }
     } else {
       float *out = (float *)p.out;
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
-        const int n = nt * BN + wn * 64 + j * 32 + (lane & 31);
+      for (int j = 0; j < NB; j++) {
+        const int n = nt * BN + wn * NB * 32 + j * 32 + (lane & 31);
         if (n >= p.H) continue;
 #pragma unroll
         for (int i = 0; i < NA; i++)
@@ -168,13 +230,18 @@ __device__ __forceinline__ void dma_body(const TileParams &p, const char *abase,
 // MODE 0: gate/up + SwiGLU -> h (bf16).  MODE 1: down + combine epilogue.
 // GATHER (mode 0): A row r is a[row_token[r]].  ATOMIC (mode 1): fused combine.
 template <int MODE, bool GATHER, bool ATOMIC>
-__global__ __launch_bounds__(NTHR, 1) void ffn_dma_kernel(TileParams p) {
+__global__ __launch_bounds__(NTHR, 1) __attribute__((amdgpu_waves_per_eu(NWAVE / 4, NWAVE / 4))) void ffn_dma_kernel(
+    TileParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   const int K = MODE == 0 ? p.H : p.I;
   const int Nw = MODE == 0 ? 2 * p.I : p.H;
   const int NT = MODE == 0 ? (p.I + 127) / 128 : (p.H + BN - 1) / BN;
   int e, nt, mt, mtiles;
   if (!ffn::locate_tile<BM>(p, NT, e, nt, mt, mtiles)) return;
+  e = __builtin_amdgcn_readfirstlane(e);  // the same in every lane: keep it scalar
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  mt = __builtin_amdgcn_readfirstlane(mt);
+  mtiles = __builtin_amdgcn_readfirstlane(mtiles);
   // equal split of the expert's rows over its M tiles, rounded up to 64 rows
   const int beg = p.offsets[e], cnt = p.offsets[e + 1] - beg;
   const int trows = __builtin_amdgcn_readfirstlane(min(BM, (((cnt + mtiles - 1) / mtiles) + 63) & ~63));
@@ -182,21 +249,25 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_dma_kernel(TileParams p) {
   const int rows = min(trows, min(beg + cnt, p.R_cap) - r0);
   if (rows <= 0) return;
   const int half = trows >> 1;  // rows per M wave, a multiple of 32
-  const int nA = trows >> 6;    // A segments (8 rows each) per wave and K step
+  const int nA = trows / (8 * NWAVE);  // A segments (8 rows each) per wave and K step
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
   const int mvalid = rows - wm * half;
   const int nmb = __builtin_amdgcn_readfirstlane(mvalid <= 0 ? 0 : min(half >> 5, (mvalid + 31) >> 5));
 
   // Sources of this lane's slots: segment s (1 KB) holds tile rows 8s .. 8s+7; wave w fills
-  // segments w + 8u.  Slot i of a segment is row 8s + i/8, chunk (i%8) ^ ((row >> 1) & 7).
+  // segments w + 4u.  Slot i of a segment is row 8s + i/8, chunk (i%8) ^ ((row >> 1) & 7).
   DmaSrc src;
-  const char *abase = (const char *)p.a;
-  const char *bbase = (const char *)p.w + (size_t)e * Nw * K * 2;
+  {
+    const int arows = (MODE == 0 && GATHER) ? p.T : p.R_cap;  // rows of the activation tensor
+    src.ra = __builtin_amdgcn_make_buffer_rsrc((void *)p.a, (short)0, (int)((size_t)arows * K * 2), kRsrcWord3);
+    src.rb = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)p.w + (size_t)e * Nw * K * 2), (short)0,
+                                               (int)((size_t)Nw * K * 2), kRsrcWord3);
+  }
 #pragma unroll
-  for (int u = 0; u < 4; u++) {
-    const int row = (wave + 8 * u) * 8 + (lane >> 3);
+  for (int u = 0; u < B_SEG; u++) {
+    const int row = (wave + NWAVE * u) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     const int r = r0 + min(row, rows - 1);  // rows past the end repeat the last valid row
     const uint32_t arow = (MODE == 0 && GATHER) ? (uint32_t)p.row_token[r] : (uint32_t)r;
@@ -211,7 +282,7 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_dma_kernel(TileParams p) {
   src.bstep = (uint32_t)ffn::w_chunk_step(p.wpacked, 2);
   const int arow0 = wm * half;
   const int rbase = r0 + arow0;
-#define DMA_BODY(n) dma_body<MODE, ATOMIC, n>(p, abase, bbase, src, nA, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
+#define DMA_BODY(n) dma_body<MODE, ATOMIC, n>(p, src, nA, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
   switch (nmb) {
     case 0: DMA_BODY(0); break;
     case 1: DMA_BODY(1); break;
@@ -240,6 +311,7 @@ hipError_t launch_ffn_dma(const TileParams &base, const FfnArgs &a, hipStream_t 
   const long long mt2 = (long long)a.El * ceil_div_i(a.T, BM);
   const long long max_mt = mt1 < mt2 ? mt1 : mt2;
   TileParams tp = base;
+  tp.T = a.T;
   if (a.phase & 1) {
     tp.a = a.a;
     tp.w = a.w_gu;
