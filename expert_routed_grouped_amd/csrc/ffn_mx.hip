@@ -3,8 +3,8 @@
 // Tiling as in the bf16 direct-to-LDS kernel (ffn_dma.hip), with at most 192 rows
 // of one expert per tile (equal M tiles per expert, rounded to 64 rows; the fp8
 // operand fragments are twice as wide, so 4 x 2 accumulator blocks would spill) x 256 weight rows,
-// eight waves as 2 (M) x 4 (N), operands moved HBM/L2 -> LDS by global_load_lds
-// with load issue spread over the MFMAs.  The K step is 128 E4M3 values (one
+// eight waves as 2 (M) x 4 (N), operands moved HBM/L2 -> LDS by buffer loads to
+// LDS with load issue spread over the MFMAs.  The K step is 128 E4M3 values (one
 // full 128-byte line per row) plus the four E8M0 scale bytes of each row, and
 // the product is v_mfma_scale_f32_32x32x64_f8f6f4: 64 k per instruction with
 // the block scales applied inside the matrix core.
@@ -26,6 +26,13 @@
 // loads has landed.  One barrier per step.  Chunk c of LDS row r sits in slot
 // c ^ ((r >> 1) & 7); wave w's 256-byte scale segment holds the A scales of
 // tile rows 32w .. 32w+31, then the B scales of weight rows 32w .. 32w+31.
+//
+// As in the bf16 kernel the K loop carries no address arithmetic: the code
+// loads are buffer loads (per-lane offsets fixed for the tile, the K advance a
+// scalar offset, the LDS destination scalar), the loop is unrolled over the
+// 6-step period of the two rings so that every fragment and scale read is a
+// precomputed per-lane LDS base plus an immediate; only the per-row scale dword
+// (one per lane and step) is still a vector-addressed load.
 //
 // Gate/up epilogue: h = silu(G) * U in fp32, quantised per row in blocks of 32
 // intermediate columns (a wave's 32 columns are one block) into MXFP8 codes and
@@ -50,7 +57,6 @@ static_assert(LDS_BYTES <= 160 * 1024, "fits the LDS of one CU");
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int lds_off64(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 struct MxParams {
@@ -61,104 +67,139 @@ struct MxParams {
 };
 
 struct Src {
-  uint32_t aoff[3], boff[4];   // byte offsets of this lane's A / B segment chunks at K step 0
-  uint32_t bstep;              // bytes from one K step of the weight codes to the next (row-major or packed)
-  const uint8_t *sptr;         // this lane's scale dword at K step 0: A row (lanes < 32) or B row
+  __amdgpu_buffer_rsrc_t ra, rb;      // activation codes, this expert's weight codes
+  const uint8_t *sptr;                // this lane's scale row: A row (lanes < 32) or B row
+  uint32_t aoff[3], boff[4];          // byte offsets of this lane's A / B segment chunks at K step 0
+  uint32_t bstep;                     // bytes from one K step of the weight codes to the next (row-major or packed)
 };
 
-template <int NMB>
-__device__ __forceinline__ void kloop(const char *abase, const char *bbase, const Src &src, int K, int wave, int lane,
-                                      int arow0, int wn, char *lds, f32x16_t (&acc)[NMB > 0 ? NMB : 1][2]) {
-  const int KT = K / BK;
-  const int h = lane >> 5;
-  // A of step kt: A slot kt % 2; B and the scales of step kt: B slot kt % 3.  Source steps past
-  // the end are clamped to the last one.
-  auto loadA = [&](int kt, int u) __attribute__((always_inline)) {
-    __builtin_amdgcn_global_load_lds((const void *)(abase + (size_t)min(kt, KT - 1) * BK + src.aoff[u]),
-                                     (lds_void *)(lds + (kt & 1) * A_BYTES + (wave + 8 * u) * 1024), 16, 0, 0);
-  };
-  auto loadB = [&](int kt, int u) __attribute__((always_inline)) {
-    __builtin_amdgcn_global_load_lds((const void *)(bbase + (size_t)min(kt, KT - 1) * src.bstep + src.boff[u]),
-                                     (lds_void *)(lds + OFF_B + (kt % 3) * BSLOT + (wave + 8 * u) * 1024), 16, 0, 0);
-  };
-  auto loadS = [&](int kt) __attribute__((always_inline)) {  // four scale bytes per row and K step
-    __builtin_amdgcn_global_load_lds((const void *)(src.sptr + (size_t)min(kt, KT - 1) * 4),
-                                     (lds_void *)(lds + OFF_B + (kt % 3) * BSLOT + BN * BK + wave * 256), 4, 0, 0);
-  };
-  auto step = [&](int kt) __attribute__((always_inline)) {
-    const char *A = lds + (kt & 1) * A_BYTES;
-    const char *B = lds + OFF_B + (kt % 3) * BSLOT;
-    const char *S = B + BN * BK;
-    uint32_t sa[NMB > 0 ? NMB : 1], sb[2];
+constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+// One K step with compile-time ring slots: P = kt % 6 (A slot P % 2, B slot P % 3).  The loads of
+// the next steps are issued past the last step too (their source step clamped to the last one, into
+// slots nobody reads again), so every step issues the same loads and the waits are fixed counts.
+template <int NMB, int P>
+__device__ __forceinline__ void mx_step(int kt, int KT, const Src &src, int wave, const uint32_t (&abase)[4],
+                                        const uint32_t (&bbase)[3][4], uint32_t sabase, const uint32_t (&sbbase)[3],
+                                        int h, char *lds, f32x16_t (&acc)[NMB > 0 ? NMB : 1][2]) {
+  constexpr int NA = NMB > 0 ? NMB : 1;
+  constexpr int SA = P % 2, SB = P % 3, SA1 = (P + 1) % 2, SB2 = (P + 2) % 3;
+  uint32_t sa[NA], sb[2];
+  if constexpr (NMB > 0) {
+#pragma unroll
+    for (int j = 0; j < 2; j++) sb[j] = *(const uint32_t *)(lds + sbbase[SB] + j * 256) >> (8 * h);
+#pragma unroll
+    for (int i = 0; i < NMB; i++) sa[i] = *(const uint32_t *)(lds + sabase + SB * BSLOT + i * 256) >> (8 * h);
+  }
+  const uint32_t soA = (uint32_t)min(kt + 1, KT - 1) * BK, soB = (uint32_t)min(kt + 2, KT - 1) * src.bstep;
+  const int ktS = min(kt + 2, KT - 1);
+  // one 64-k half of the K step; KK is a compile-time constant (the scale byte selector must be)
+  auto half_step = [&](auto KKC) __attribute__((always_inline)) {
+    constexpr int kk = decltype(KKC)::value;
+    v8i_t bf[2], af[NA];
+    if constexpr (NMB > 0) {
+      auto frag = [&](uint32_t lo_off, uint32_t hi_off) __attribute__((always_inline)) {
+        const u32x4_t lo = *(const u32x4_t *)(lds + lo_off);
+        const u32x4_t hi = *(const u32x4_t *)(lds + hi_off);
+        v8i_t v;
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+        return v;
+      };
+#pragma unroll
+      for (int j = 0; j < 2; j++) bf[j] = frag(bbase[SB][2 * kk] + j * 4096, bbase[SB][2 * kk + 1] + j * 4096);
+#pragma unroll
+      for (int i = 0; i < NMB; i++)
+        af[i] = frag(abase[2 * kk] + SA * A_BYTES + i * 4096, abase[2 * kk + 1] + SA * A_BYTES + i * 4096);
+    }
+    if constexpr (kk == 0) {
+#pragma unroll
+      for (int u = 0; u < 3; u++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.ra, (lds_void *)(lds + SA1 * A_BYTES + (wave + 8 * u) * 1024),
+                                                 16, src.aoff[u], soA, 0, 0);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            src.rb, (lds_void *)(lds + OFF_B + SB2 * BSLOT + (wave + 8 * u) * 1024), 16, src.boff[u], soB, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(src.sptr + (size_t)ktS * 4),
+                                       (lds_void *)(lds + OFF_B + SB2 * BSLOT + BN * BK + wave * 256), 4, 0, 0);
+    }
     if constexpr (NMB > 0) {
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
-        const int row = wn * 64 + j * 32 + (lane & 31);
-        sb[j] = *(const uint32_t *)(S + (row >> 5) * 256 + 128 + (row & 31) * 4) >> (8 * h);
-      }
+      for (int i = 0; i < NMB; i++)
 #pragma unroll
-      for (int i = 0; i < NMB; i++) {
-        const int row = arow0 + i * 32 + (lane & 31);
-        sa[i] = *(const uint32_t *)(S + (row >> 5) * 256 + (row & 31) * 4) >> (8 * h);
-      }
+        for (int j = 0; j < 2; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 2 * kk, sa[i],
+                                                                      2 * kk, sb[j]);
     }
-    // one 64-k half of the K step; KK is a compile-time constant (the scale byte selector must be)
-    auto half_step = [&](auto KKC) __attribute__((always_inline)) {
-      constexpr int kk = decltype(KKC)::value;
-      v8i_t bf[2], af[NMB > 0 ? NMB : 1];
-      if constexpr (NMB > 0) {
-        auto frag = [&](const char *base, int row) __attribute__((always_inline)) {
-          const u32x4_t lo = *(const u32x4_t *)(base + lds_off64(row, 4 * kk + h));
-          const u32x4_t hi = *(const u32x4_t *)(base + lds_off64(row, 4 * kk + 2 + h));
-          v8i_t v;
-          v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-          return v;
-        };
-#pragma unroll
-        for (int j = 0; j < 2; j++) bf[j] = frag(B, wn * 64 + j * 32 + (lane & 31));
-#pragma unroll
-        for (int i = 0; i < NMB; i++) af[i] = frag(A, arow0 + i * 32 + (lane & 31));
-      }
-      if constexpr (kk == 0) {
-#pragma unroll
-        for (int u = 0; u < 3; u++) loadA(kt + 1, u);
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; u++) loadB(kt + 2, u);
-        loadS(kt + 2);
-      }
-      if constexpr (NMB > 0) {
-#pragma unroll
-        for (int i = 0; i < NMB; i++)
-#pragma unroll
-          for (int j = 0; j < 2; j++)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 2 * kk, sa[i],
-                                                                        2 * kk, sb[j]);
-      }
-    };
-    half_step(std::integral_constant<int, 0>{});
-    half_step(std::integral_constant<int, 1>{});
   };
+  half_step(std::integral_constant<int, 0>{});
+  half_step(std::integral_constant<int, 1>{});
+}
+
+template <int NMB>
+__device__ __forceinline__ void kloop(const Src &src, int K, int wave, int lane, int arow0, int wn, char *lds,
+                                      f32x16_t (&acc)[NMB > 0 ? NMB : 1][2]) {
+  const int KT = K / BK;
+  const int h = lane >> 5, r = lane & 31;
+  // LDS byte offsets of this lane's fragment chunks: row r (+ multiples of 32, which leave the
+  // swizzle alone), chunks 4 kk + 2 c + h at slot chunk ^ ((r >> 1) & 7), for kk, c in {0, 1}
+  uint32_t abase[4], bbase[3][4], sbbase[3];
+  {
+    const int sw = (r >> 1) & 7;
 #pragma unroll
-  for (int u = 0; u < 4; u++) loadB(0, u);
-  loadS(0);
+    for (int q = 0; q < 4; q++) {  // q = 2 kk + c
+      const uint32_t o = (uint32_t)(((2 * q + h) ^ sw) << 4);
+      abase[q] = (uint32_t)(arow0 + r) * 128u + o;
 #pragma unroll
-  for (int u = 0; u < 3; u++) loadA(0, u);
+      for (int s = 0; s < 3; s++) bbase[s][q] = OFF_B + (uint32_t)s * BSLOT + (uint32_t)(wn * 64 + r) * 128u + o;
+    }
 #pragma unroll
-  for (int u = 0; u < 4; u++) loadB(1, u);
-  loadS(1);
-  for (int kt = 0; kt < KT; kt++) {
-    // this wave's newest five loads are the weights and scales of step kt + 1; all older ones,
-    // among them everything of step kt, have landed once at most five are in flight
-    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    barrier_no_fence();
-    step(kt);
+    for (int s = 0; s < 3; s++)
+      sbbase[s] = OFF_B + (uint32_t)s * BSLOT + BN * BK + (uint32_t)(wn * 2) * 256u + 128u + r * 4u;
+  }
+  // A scales of tile row arow0 + 32 i + r: segment (arow0 >> 5) + i of the slot's scale area
+  const uint32_t sabase = OFF_B + BN * BK + (uint32_t)(arow0 >> 5) * 256u + r * 4u;
+  // prologue: weights and scales of steps 0 and 1, activations of step 0
+#pragma unroll
+  for (int u = 0; u < 4; u++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rb, (lds_void *)(lds + OFF_B + (wave + 8 * u) * 1024), 16,
+                                             src.boff[u], 0, 0, 0);
+  __builtin_amdgcn_global_load_lds((const void *)src.sptr, (lds_void *)(lds + OFF_B + BN * BK + wave * 256), 4, 0, 0);
+#pragma unroll
+  for (int u = 0; u < 3; u++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.ra, (lds_void *)(lds + (wave + 8 * u) * 1024), 16, src.aoff[u], 0, 0,
+                                             0);
+  const uint32_t so1 = (uint32_t)min(1, KT - 1);
+#pragma unroll
+  for (int u = 0; u < 4; u++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rb, (lds_void *)(lds + OFF_B + BSLOT + (wave + 8 * u) * 1024), 16,
+                                             src.boff[u], so1 * src.bstep, 0, 0);
+  __builtin_amdgcn_global_load_lds((const void *)(src.sptr + (size_t)so1 * 4),
+                                   (lds_void *)(lds + OFF_B + BSLOT + BN * BK + wave * 256), 4, 0, 0);
+  // this wave's newest five loads are the weights and scales of step kt + 1; all older ones,
+  // among them everything of step kt, have landed once at most five are in flight
+  auto one = [&](auto PC, int kt) __attribute__((always_inline)) {
+    constexpr int P = decltype(PC)::value;
+    if (kt < KT) {
+      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      barrier_no_fence();
+      mx_step<NMB, P>(kt, KT, src, wave, abase, bbase, sabase, sbbase, h, lds, acc);
+    }
+  };
+  for (int kt = 0; kt < KT; kt += 6) {
+    one(std::integral_constant<int, 0>{}, kt);
+    one(std::integral_constant<int, 1>{}, kt + 1);
+    one(std::integral_constant<int, 2>{}, kt + 2);
+    one(std::integral_constant<int, 3>{}, kt + 3);
+    one(std::integral_constant<int, 4>{}, kt + 4);
+    one(std::integral_constant<int, 5>{}, kt + 5);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int MODE, bool ATOMIC, int NMB>
-__device__ __forceinline__ void body(const MxParams &mp, const char *abase, const char *bbase, const Src &src, int K,
+__device__ __forceinline__ void body(const MxParams &mp, const Src &src, int K,
                                      int nt, int rbase, int mvalid, int wave, int lane, int arow0, int wn, char *lds) {
   const TileParams &p = mp.tp;
   constexpr int NA = NMB > 0 ? NMB : 1;
@@ -169,7 +210,7 @@ __device__ __forceinline__ void body(const MxParams &mp, const char *abase, cons
     for (int j = 0; j < 2; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
-  kloop<NMB>(abase, bbase, src, K, wave, lane, arow0, wn, lds, acc);
+  kloop<NMB>(src, K, wave, lane, arow0, wn, lds, acc);
   if constexpr (NMB > 0) {
     // acc[i][j][r] at lane l is tile row arow0 + i*32 + 8*(r/4) + 4*(l/32) + r%4,
     // weight row wn*64 + j*32 + l%32 of the tile
@@ -223,6 +264,10 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
   const int NT = MODE == 0 ? p.I / 128 : (p.H + BN - 1) / BN;
   int e, nt, mt, mtiles;
   if (!ffn::locate_tile<BM>(p, NT, e, nt, mt, mtiles)) return;
+  e = __builtin_amdgcn_readfirstlane(e);  // the same in every lane: keep it scalar
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  mt = __builtin_amdgcn_readfirstlane(mt);
+  mtiles = __builtin_amdgcn_readfirstlane(mtiles);
   const int beg = p.offsets[e], cnt = p.offsets[e + 1] - beg;
   const int trows = __builtin_amdgcn_readfirstlane(min(BM, (((cnt + mtiles - 1) / mtiles) + 63) & ~63));
   const int r0 = beg + mt * trows;
@@ -230,7 +275,7 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
   if (rows <= 0) return;
   const int half = trows >> 1;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int mvalid = rows - wm * half;
   const int nmb = __builtin_amdgcn_readfirstlane(mvalid <= 0 ? 0 : min(half >> 5, (mvalid + 31) >> 5));
@@ -245,8 +290,10 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
     else return min(nt * BN + row, p.H - 1);
   };
   Src src;
-  const char *abase = (const char *)p.a;
-  const char *bbase = (const char *)p.w + (size_t)e * Nw * K;
+  const int arows = (MODE == 0 && GATHER) ? p.T : p.R_cap;  // rows of the activation tensor
+  src.ra = __builtin_amdgcn_make_buffer_rsrc((void *)p.a, (short)0, (int)((size_t)arows * K), kRsrcWord3);
+  src.rb = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)p.w + (size_t)e * Nw * K), (short)0,
+                                             (int)((size_t)Nw * K), kRsrcWord3);
   const uint8_t *asb = mp.a_scales;
   const uint8_t *bsb = mp.w_scales + (size_t)e * Nw * kb;
 #pragma unroll
@@ -268,7 +315,7 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
   }
   const int arow0 = wm * half;
   const int rbase = r0 + arow0;
-#define MX_BODY(n) body<MODE, ATOMIC, n>(mp, abase, bbase, src, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
+#define MX_BODY(n) body<MODE, ATOMIC, n>(mp, src, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
   switch (nmb) {
     case 0: MX_BODY(0); break;
     case 1: MX_BODY(1); break;
@@ -307,6 +354,7 @@ hipError_t launch_ffn_mx(const FfnMxArgs &a, hipStream_t s) {
   mp.tp.I = a.I;
   mp.tp.R_cap = a.R_cap;
   mp.tp.wpacked = a.wpacked;
+  mp.tp.T = a.T;
   if (a.phase & 1) {
     MxParams m = mp;
     m.tp.a = a.a;
