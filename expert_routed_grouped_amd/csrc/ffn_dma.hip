@@ -191,37 +191,77 @@ __device__ __forceinline__ void dma_body(const TileParams &p, const DmaSrc &src,
     // acc[i][j][r] at lane l is tile row arow0 + i*32 + 8*(r/4) + 4*(l/32) + r%4,
     // weight row wn*128 + j*32 + l%32 of the tile
     if constexpr (MODE == 0) {
-      uint16_t *hout = (uint16_t *)p.out;
+      // h through a buffer resource: a per-lane 32-bit byte offset (row rbase + 4*(l/32), this
+      // lane's column) plus a wave-uniform offset per accumulator row, so no store needs address
+      // arithmetic in vector registers (the whole of h is below 2^31 bytes).  Fully valid row
+      // blocks, the common case, skip the row test.
+      const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+          p.out, (short)0, (int)((size_t)p.R_cap * p.I * 2), kRsrcWord3);
+      const int I2 = __builtin_amdgcn_readfirstlane(p.I * 2);
+      const int voff0 = ((rbase + 4 * (lane >> 5)) * p.I + nt * 128 + wn * NB * 16 + (lane & 31)) * 2;
+      auto put = [&](auto FULL) __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = 0; q < NB / 2; q++) {  // blocks 2q (gate) and 2q+1 (up) of the same 32 columns
-        const int col = nt * 128 + wn * NB * 16 + q * 32 + (lane & 31);  // intermediate index
-        if (col - (lane & 31) >= p.I) continue;
+        for (int q = 0; q < NB / 2; q++) {  // blocks 2q (gate) and 2q+1 (up) of the same 32 columns
+          if (nt * 128 + wn * NB * 16 + q * 32 >= p.I) continue;
 #pragma unroll
-        for (int i = 0; i < NA; i++)
+          for (int i = 0; i < NA; i++)
 #pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (m < mvalid)
-              hout[(size_t)(rbase + m) * p.I + col] = f32_to_bf16(silu_fast(acc[i][2 * q][r]) * acc[i][2 * q + 1][r]);
-          }
-      }
-    } else {
-      float *out = (float *)p.out;
-#pragma unroll
-      for (int j = 0; j < NB; j++) {
-        const int n = nt * BN + wn * NB * 32 + j * 32 + (lane & 31);
-        if (n >= p.H) continue;
-#pragma unroll
-        for (int i = 0; i < NA; i++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (m < mvalid) {
-              const int row = rbase + m;
-              if constexpr (ATOMIC) atomicAdd(out + (size_t)p.row_token[row] * p.H + n, p.row_w[row] * acc[i][j][r]);
-              else out[(size_t)row * p.H + n] = acc[i][j][r];
+            for (int r = 0; r < 16; r += 2) {
+              const int d = i * 32 + 8 * (r >> 2) + (r & 3);  // row offset of acc r; r+1 is one row below
+              const uint32_t hv = pack_bf16x2(silu_fast(acc[i][2 * q][r]) * acc[i][2 * q + 1][r],
+                                              silu_fast(acc[i][2 * q][r + 1]) * acc[i][2 * q + 1][r + 1]);
+              const int m = d + 4 * (lane >> 5);
+              if (decltype(FULL)::value || m < mvalid)
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rh, voff0 + q * 64, d * I2, 0);
+              if (decltype(FULL)::value || m + 1 < mvalid)
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rh, voff0 + q * 64, (d + 1) * I2, 0);
             }
+        }
+      };
+      if (mvalid >= NA * 32) put(std::true_type{});
+      else put(std::false_type{});
+    } else {
+      if constexpr (ATOMIC) {
+        float *out = (float *)p.out;
+#pragma unroll
+        for (int j = 0; j < NB; j++) {
+          const int n = nt * BN + wn * NB * 32 + j * 32 + (lane & 31);
+          if (n >= p.H) continue;
+#pragma unroll
+          for (int i = 0; i < NA; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              if (m < mvalid) {
+                const int row = rbase + m;
+                atomicAdd(out + (size_t)p.row_token[row] * p.H + n, p.row_w[row] * acc[i][j][r]);
+              }
+            }
+        }
+      } else {
+        // y_perm through a buffer resource, as h above: the whole of it is below 2^32 bytes
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+            p.out, (short)0, (int)(uint32_t)((size_t)p.R_cap * p.H * 4), kRsrcWord3);
+        const uint32_t H4 = (uint32_t)__builtin_amdgcn_readfirstlane(p.H * 4);
+        auto put = [&](auto FULL) __attribute__((always_inline)) {
+#pragma unroll
+          for (int j = 0; j < NB; j++) {
+            const int n = nt * BN + wn * NB * 32 + j * 32 + (lane & 31);
+            if (n >= p.H) continue;
+            const uint32_t voff = ((uint32_t)(rbase + 4 * (lane >> 5)) * (uint32_t)p.H + (uint32_t)n) * 4u;
+#pragma unroll
+            for (int i = 0; i < NA; i++)
+#pragma unroll
+              for (int r = 0; r < 16; r++) {
+                const int d = i * 32 + 8 * (r >> 2) + (r & 3);
+                if (decltype(FULL)::value || d + 4 * (lane >> 5) < mvalid)
+                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ry, (int)voff,
+                                                        (int)((uint32_t)d * H4), 0);
+              }
           }
+        };
+        if (mvalid >= NA * 32) put(std::true_type{});
+        else put(std::false_type{});
       }
     }
   }

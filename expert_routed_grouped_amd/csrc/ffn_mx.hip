@@ -215,23 +215,36 @@ __device__ __forceinline__ void body(const MxParams &mp, const Src &src, int K,
     // acc[i][j][r] at lane l is tile row arow0 + i*32 + 8*(r/4) + 4*(l/32) + r%4,
     // weight row wn*64 + j*32 + l%32 of the tile
     if constexpr (MODE == 0) {
+      // h codes and scales through buffer resources: a per-lane 32-bit offset (row rbase + 4*(l/32),
+      // column col) plus a wave-uniform offset per accumulator row, so no store needs address
+      // arithmetic in vector registers; both tensors are below 2^31 bytes.
       const int col = nt * 128 + wn * 32 + (lane & 31);  // intermediate index; I % 128 == 0
-      uint8_t *hq = (uint8_t *)p.out;
       const int ib = p.I / 32;
+      const __amdgpu_buffer_rsrc_t rq =
+          __builtin_amdgcn_make_buffer_rsrc(p.out, (short)0, (int)((size_t)p.R_cap * p.I), kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(mp.out_scales, (short)0, (int)((size_t)p.R_cap * ib), kRsrcWord3);
+      const int Iu = __builtin_amdgcn_readfirstlane(p.I), ibu = __builtin_amdgcn_readfirstlane(ib);
+      const int row0 = rbase + 4 * (lane >> 5);
+      const int voff = row0 * p.I + col, soff = row0 * ib + col / 32;
+      const bool scale_lane = (lane & 31) == 0;
+      auto put = [&](auto FULL) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < NA; i++)
+        for (int i = 0; i < NA; i++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
-          const uint32_t s = mx_scale_of(halfwave_amax(hv));  // every lane joins the shuffles
-          if (m < mvalid) {
-            const size_t row = (size_t)(rbase + m);
-            hq[row * p.I + col] = (uint8_t)e4m3_encode(ldexpf(hv, 127 - (int)s));
-            if ((lane & 31) == 0) mp.out_scales[row * ib + col / 32] = (uint8_t)s;
+          for (int r = 0; r < 16; r++) {
+            const int d = i * 32 + 8 * (r >> 2) + (r & 3);
+            const float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
+            const uint32_t s = mx_scale_of(halfwave_amax(hv));  // every lane joins the shuffles
+            if (decltype(FULL)::value || d + 4 * (lane >> 5) < mvalid) {
+              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e4m3_encode(ldexpf(hv, 127 - (int)s)), rq, voff, d * Iu, 0);
+              if (scale_lane) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)s, rs, soff, d * ibu, 0);
+            }
           }
-        }
-    } else {
+      };
+      if (mvalid >= NA * 32) put(std::true_type{});
+      else put(std::false_type{});
+    } else if constexpr (ATOMIC) {
       float *out = (float *)p.out;
 #pragma unroll
       for (int j = 0; j < 2; j++) {
@@ -244,11 +257,34 @@ __device__ __forceinline__ void body(const MxParams &mp, const Src &src, int K,
             const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             if (m < mvalid) {
               const int row = rbase + m;
-              if constexpr (ATOMIC) atomicAdd(out + (size_t)p.row_token[row] * p.H + n, p.row_w[row] * acc[i][j][r]);
-              else out[(size_t)row * p.H + n] = acc[i][j][r];
+              atomicAdd(out + (size_t)p.row_token[row] * p.H + n, p.row_w[row] * acc[i][j][r]);
             }
           }
       }
+    } else {
+      // y_perm through a buffer resource, as h above: the whole of it is below 2^32 bytes
+      const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+          p.out, (short)0, (int)(uint32_t)((size_t)p.R_cap * p.H * 4), kRsrcWord3);
+      const uint32_t H4 = (uint32_t)__builtin_amdgcn_readfirstlane(p.H * 4);
+      auto put = [&](auto FULL) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+          const int n = nt * BN + wn * 64 + j * 32 + (lane & 31);
+          if (n >= p.H) continue;
+          const uint32_t voff = ((uint32_t)(rbase + 4 * (lane >> 5)) * (uint32_t)p.H + (uint32_t)n) * 4u;
+#pragma unroll
+          for (int i = 0; i < NA; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              const int d = i * 32 + 8 * (r >> 2) + (r & 3);
+              if (decltype(FULL)::value || d + 4 * (lane >> 5) < mvalid)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ry, (int)voff,
+                                                      (int)((uint32_t)d * H4), 0);
+            }
+        }
+      };
+      if (mvalid >= NA * 32) put(std::true_type{});
+      else put(std::false_type{});
     }
   }
 }
