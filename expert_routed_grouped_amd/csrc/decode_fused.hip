@@ -143,11 +143,11 @@ __device__ __noinline__ void route_item(const DecParams &pin, int t, int *smem) 
   if (threadIdx.x == 0) __hip_atomic_store(p.ctl + kDecRouted, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// This lane's weight bytes of row ``row`` (counted over all experts) at k = 0, k offset 32g.
+// This lane's first weight piece of row ``row`` (counted over all experts) at k = 0, k offset 32g.
 template <bool FP8>
 __device__ __forceinline__ const char *weight_lane(const DecParams &p, const void *w, size_t row, int K, int g) {
   constexpr int wesz = FP8 ? 1 : 2;
-  return (const char *)w + ffn::w_row_off(p.wpacked, row, K, wesz) + 32 * g * wesz;
+  return (const char *)w + ffn::w_piece_off(p.wpacked, row, 2 * wesz * g, K, wesz);
 }
 
 template <bool FP8>
@@ -183,7 +183,8 @@ __device__ __noinline__ void gate_up_item(const DecParams &pin, int e, int nb, i
     for (int mb = 0; mb < SMB; mb++) arow[mb] = (const uint16_t *)p.x + (size_t)token(mb * 32 + n) * p.H + 32 * g;
     f32x16_t acc[SMB][2];
     sc::zero_acc(acc);
-    sc::stream_mfma<FP8, SMB, 2>(wrow, ffn::w_chunk_step(p.wpacked, FP8 ? 1 : 2), arow, rows > 32, p.H / 64, acc);
+    sc::stream_mfma<FP8, SMB, 2>(wrow, ffn::w_lane_piece_step(p.wpacked, FP8 ? 1 : 2),
+                                 ffn::w_chunk_step(p.wpacked, FP8 ? 1 : 2), arow, rows > 32, p.H / 64, acc);
     uint16_t *hcol = p.h + (size_t)e * p.T * p.I + col;
 #pragma unroll
     for (int mb = 0; mb < SMB; mb++) {
@@ -245,7 +246,8 @@ __device__ __noinline__ void down_item(const DecParams &pin, int e, int nb, int 
       arow[mb] = p.h + ((size_t)e * p.T + p.row_token[r0 + min(mb * 32 + n, rows - 1)]) * p.I + 32 * g;
     f32x16_t acc[SMB][2];
     sc::zero_acc(acc);
-    sc::stream_mfma<FP8, SMB, 2>(wrow, cstep, arow, rows > 32, p.I / 64, acc);
+    sc::stream_mfma<FP8, SMB, 2>(wrow, ffn::w_lane_piece_step(p.wpacked, FP8 ? 1 : 2), cstep, arow, rows > 32,
+                                 p.I / 64, acc);
 #pragma unroll
     for (int b = 0; b < 2; b++) {
 #pragma unroll

@@ -327,7 +327,7 @@ __global__ void pack_weights_kernel(const char *__restrict__ w, int esz, size_t 
     const int kb = (int)(u - row * per_row) * 16;  // byte offset inside the row-major row
     const int k = kb / esz;
     const size_t dst =
-        ffn::w_row_off(1, row, K, esz) + (size_t)(k >> 6) * ffn::w_chunk_step(1, esz) + (size_t)(kb % (64 * esz));
+        ffn::w_piece_off(1, row, (kb % (64 * esz)) / 16, K, esz) + (size_t)(k >> 6) * ffn::w_chunk_step(1, esz);
     *(u32x4_t *)(out + dst) = *(const u32x4_t *)(w + row * (size_t)K * esz + kb);
   }
 }

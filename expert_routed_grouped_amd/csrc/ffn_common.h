@@ -20,13 +20,30 @@ struct TileParams {
   int T;                  // tokens (rows of x when the gate/up half gathers)
 };
 
-// Byte offset of weight row ``row`` (counted over all experts of the tensor) at k = 0, and the
-// byte step from one 64-wide K chunk to the next, for row-major or packed weights of esz bytes.
-// Packed: every 32 rows form K/64 consecutive blocks of 32 x 64 values, row-major inside.
-__device__ __forceinline__ size_t w_row_off(int packed, size_t row, int K, int esz) {
-  return packed ? ((row >> 5) * 32 * (size_t)K + (row & 31) * 64) * esz : row * (size_t)K * esz;
+// Weight addressing for row-major or packed weights of esz bytes; ``row`` counts over all experts
+// of the tensor.  Packed: every 32 rows form K/64 consecutive blocks of 32 x 64 values (4 KB of
+// bf16, 2 KB of fp8).  Inside an fp8 block the rows follow each other (64 bytes each).  Inside a
+// bf16 block, 16-byte piece c (values 8c .. 8c+7 of the chunk) of block row n sits at byte
+// (c % 4) * 1024 + (n + 32 * (c / 4)) * 16: a wave that streams the block in the operand layout
+// of v_mfma_f32_32x32x16_bf16 (lane n + 32g takes pieces 4g .. 4g+3 of row n) then reads 1 KB
+// contiguously per load, and eight consecutive rows of one piece column are 128 contiguous bytes.
+
+// Byte offset of 16-byte piece c (values 16c/esz .. of the row's first 64-wide K chunk) of ``row``.
+__device__ __forceinline__ size_t w_piece_off(int packed, size_t row, int c, int K, int esz) {
+  if (!packed) return row * (size_t)K * esz + (size_t)c * 16;
+  const size_t blk = (row >> 5) * 32 * (size_t)K * esz;
+  if (esz == 2) return blk + (size_t)(c & 3) * 1024 + ((row & 31) + 32 * (size_t)(c >> 2)) * 16;
+  return blk + (row & 31) * 64 + (size_t)c * 16;
 }
+// Byte offset of ``row`` at k = 0 (its piece 0).
+__device__ __forceinline__ size_t w_row_off(int packed, size_t row, int K, int esz) {
+  return w_piece_off(packed, row, 0, K, esz);
+}
+// Bytes from one 64-wide K chunk of a row to the next.
 __device__ __forceinline__ size_t w_chunk_step(int packed, int esz) { return (size_t)(packed ? 32 * 64 : 64) * esz; }
+// Bytes from piece c to piece c + 1 of one lane's 4 (bf16) or 2 (fp8) pieces of a chunk, whose
+// first piece is a multiple of their count.
+__device__ __forceinline__ size_t w_lane_piece_step(int packed, int esz) { return packed && esz == 2 ? 1024 : 16; }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll

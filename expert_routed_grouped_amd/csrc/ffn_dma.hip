@@ -34,7 +34,11 @@
 // c ^ ((r >> 1) & 7), which keeps the 16 lanes of one LDS cycle on 16 distinct
 // 16-byte bank groups when they read one chunk of 16 consecutive rows.  A load
 // to LDS writes the 16 bytes of lane i to slot i of a 1 KB segment (8 rows), so
-// every lane fetches the global chunk that belongs to its slot.
+// every lane fetches the global chunk that belongs to its slot.  Packed weights
+// are copied into LDS in their own block layout (chunk c of block row r at
+// (c % 4) * 1024 + (r + 32 (c / 4)) * 16 of a 4 KB block): every load then
+// reads 1 KB that is contiguous in memory, and a fragment read is two runs of
+// 512 contiguous bytes, free of bank conflicts without a swizzle.
 //
 // Rows past the expert's count are never multiplied: the K loop is
 // instantiated for 0..4 active 32-row blocks per wave.  The fp32 sums of every
@@ -118,22 +122,27 @@ __device__ __forceinline__ void dma_step(int kt, bool nextA, bool nextB, const D
   }
 }
 
-template <int NMB>
+template <int NMB, bool PB>
 __device__ __forceinline__ void dma_kloop(const DmaSrc &src, int nA, int K, int wave, int lane, int arow0, int wn,
                                           char *lds, f32x16_t (&acc)[NMB > 0 ? NMB : 1][NB]) {
   const int KT = K / BK;
   // LDS byte offsets of this lane's fragments: row r, 16-byte chunk ch = 2 kk + lane / 32 at slot
   // ch ^ ((r >> 1) & 7); rows of one lane differ by multiples of 32, which leave that XOR alone.
+  // Packed weights (PB) keep the global block layout in LDS instead: chunk ch of block row r at
+  // (ch % 4) * 1024 + (r + 32 * (ch / 4)) * 16 of its 4 KB block, where the 32 lanes of one
+  // fragment row read 512 contiguous bytes.
   uint32_t abase[4], bbase[3][4];
   {
     const int r = lane & 31, sw = (r >> 1) & 7, g = lane >> 5;
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) {
       const uint32_t o = (uint32_t)(((2 * kk + g) ^ sw) << 4);
+      const int ch = 2 * kk + g;
+      const uint32_t ob = PB ? (uint32_t)(wn * NB * 4096 + (ch & 3) * 1024 + (r + 32 * (ch >> 2)) * 16)
+                             : (uint32_t)(wn * NB * 32 + r) * 128u + o;
       abase[kk] = (uint32_t)(arow0 + r) * 128u + o;
 #pragma unroll
-      for (int s = 0; s < 3; s++)
-        bbase[s][kk] = 2u * A_BYTES + (uint32_t)s * B_BYTES + (uint32_t)(wn * NB * 32 + r) * 128u + o;
+      for (int s = 0; s < 3; s++) bbase[s][kk] = 2u * A_BYTES + (uint32_t)s * B_BYTES + ob;
     }
   }
   // A of step kt lives in A slot kt % 2, B of step kt in B slot kt % 3.  Within a step every A load
@@ -174,7 +183,7 @@ __device__ __forceinline__ void dma_kloop(const DmaSrc &src, int nA, int K, int 
   }
 }
 
-template <int MODE, bool ATOMIC, int NMB>
+template <int MODE, bool ATOMIC, bool PB, int NMB>
 __device__ __forceinline__ void dma_body(const TileParams &p, const DmaSrc &src,
                                          int nA, int K, int nt, int rbase, int mvalid, int wave, int lane, int arow0,
                                          int wn, char *lds) {
@@ -186,7 +195,7 @@ __device__ __forceinline__ void dma_body(const TileParams &p, const DmaSrc &src,
     for (int j = 0; j < NB; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
-  dma_kloop<NMB>(src, nA, K, wave, lane, arow0, wn, lds, acc);
+  dma_kloop<NMB, PB>(src, nA, K, wave, lane, arow0, wn, lds, acc);
   if constexpr (NMB > 0) {
     // acc[i][j][r] at lane l is tile row arow0 + i*32 + 8*(r/4) + 4*(l/32) + r%4,
     // weight row wn*128 + j*32 + l%32 of the tile
@@ -269,7 +278,7 @@ __device__ __forceinline__ void dma_body(const TileParams &p, const DmaSrc &src,
 
 // MODE 0: gate/up + SwiGLU -> h (bf16).  MODE 1: down + combine epilogue.
 // GATHER (mode 0): A row r is a[row_token[r]].  ATOMIC (mode 1): fused combine.
-template <int MODE, bool GATHER, bool ATOMIC>
+template <int MODE, bool GATHER, bool ATOMIC, bool PB>
 __global__ __launch_bounds__(NTHR, 1) __attribute__((amdgpu_waves_per_eu(NWAVE / 4, NWAVE / 4))) void ffn_dma_kernel(
     TileParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
@@ -296,8 +305,9 @@ __global__ __launch_bounds__(NTHR, 1) __attribute__((amdgpu_waves_per_eu(NWAVE /
   const int mvalid = rows - wm * half;
   const int nmb = __builtin_amdgcn_readfirstlane(mvalid <= 0 ? 0 : min(half >> 5, (mvalid + 31) >> 5));
 
-  // Sources of this lane's slots: segment s (1 KB) holds tile rows 8s .. 8s+7; wave w fills
-  // segments w + 4u.  Slot i of a segment is row 8s + i/8, chunk (i%8) ^ ((row >> 1) & 7).
+  // Sources of this lane's slots: segment s (1 KB) of the activation tile holds tile rows
+  // 8s .. 8s+7 (likewise for row-major weights); wave w fills segments w + NWAVE u.  Slot i of such
+  // a segment is row 8s + i/8, chunk (i%8) ^ ((row >> 1) & 7).
   DmaSrc src;
   {
     const int arows = (MODE == 0 && GATHER) ? p.T : p.R_cap;  // rows of the activation tensor
@@ -306,23 +316,32 @@ __global__ __launch_bounds__(NTHR, 1) __attribute__((amdgpu_waves_per_eu(NWAVE /
                                                (int)((size_t)Nw * K * 2), kRsrcWord3);
   }
 #pragma unroll
-  for (int u = 0; u < B_SEG; u++) {
+  for (int u = 0; u < A_SEG; u++) {
     const int row = (wave + NWAVE * u) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     const int r = r0 + min(row, rows - 1);  // rows past the end repeat the last valid row
     const uint32_t arow = (MODE == 0 && GATHER) ? (uint32_t)p.row_token[r] : (uint32_t)r;
     src.aoff[u] = arow * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
+  }
+#pragma unroll
+  for (int u = 0; u < B_SEG; u++) {
+    // row-major weights: the segment's rows and swizzled chunks as for A.  Packed weights: segment
+    // s is chunk column s % 4 of 32-row block s / 4 (slot i: block row i % 32, chunk s % 4 + 4 (i / 32)),
+    // 1 KB that lie contiguously in the packed tensor too
+    const int sg = wave + NWAVE * u;
+    const int row = PB ? (sg >> 2) * 32 + (lane & 31) : sg * 8 + (lane >> 3);
+    const int chunk = PB ? (sg & 3) + 4 * (lane >> 5) : (lane & 7) ^ ((row >> 1) & 7);
     // gate/up tile row 64g + 32h + c: gate (h = 0) or up (h = 1) row of intermediate column
     // nt*128 + 32g + c; columns past the end (I or H a multiple of 64 only) read a valid row
     int wrow;
     if constexpr (MODE == 0) wrow = ((row >> 5) & 1) * p.I + min(nt * 128 + (row >> 6) * 32 + (row & 31), p.I - 1);
     else wrow = min(nt * BN + row, p.H - 1);
-    src.boff[u] = (uint32_t)ffn::w_row_off(p.wpacked, (size_t)wrow, K, 2) + (uint32_t)chunk * 16u;
+    src.boff[u] = (uint32_t)ffn::w_piece_off(PB, (size_t)wrow, chunk, K, 2);
   }
-  src.bstep = (uint32_t)ffn::w_chunk_step(p.wpacked, 2);
+  src.bstep = (uint32_t)ffn::w_chunk_step(PB, 2);
   const int arow0 = wm * half;
   const int rbase = r0 + arow0;
-#define DMA_BODY(n) dma_body<MODE, ATOMIC, n>(p, src, nA, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
+#define DMA_BODY(n) dma_body<MODE, ATOMIC, PB, n>(p, src, nA, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
   switch (nmb) {
     case 0: DMA_BODY(0); break;
     case 1: DMA_BODY(1); break;
@@ -335,7 +354,8 @@ __global__ __launch_bounds__(NTHR, 1) __attribute__((amdgpu_waves_per_eu(NWAVE /
 
 template <int MODE, bool GATHER, bool ATOMIC>
 hipError_t launch_d(const TileParams &tp, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((ffn_dma_kernel<MODE, GATHER, ATOMIC>), dim3(grid), dim3(NTHR), 0, s, tp);
+  if (tp.wpacked) hipLaunchKernelGGL((ffn_dma_kernel<MODE, GATHER, ATOMIC, true>), dim3(grid), dim3(NTHR), 0, s, tp);
+  else hipLaunchKernelGGL((ffn_dma_kernel<MODE, GATHER, ATOMIC, false>), dim3(grid), dim3(NTHR), 0, s, tp);
   return hipGetLastError();
 }
 

@@ -60,8 +60,8 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
   {
     const size_t r0w = (size_t)e * Nw + c0 + n;                 // this lane's first weight row
     const size_t r1w = MODE == 0 ? r0w + p.I : r0w + 32;        // up row / second down block
-    wrow[0] = (const char *)p.w + ffn::w_row_off(p.wpacked, r0w, K, (int)wesz) + 32 * g * wesz;
-    wrow[1] = (const char *)p.w + ffn::w_row_off(p.wpacked, r1w, K, (int)wesz) + 32 * g * wesz;
+    wrow[0] = (const char *)p.w + ffn::w_piece_off(p.wpacked, r0w, 2 * (int)wesz * g, K, (int)wesz);
+    wrow[1] = (const char *)p.w + ffn::w_piece_off(p.wpacked, r1w, 2 * (int)wesz * g, K, (int)wesz);
   }
   // activation rows (two 32-row blocks; rows past the end repeat the last valid row)
   const uint16_t *arow[SMB];
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64 * SWAVES) void ffn_stream_kernel(TileParams p) {
   for (int b = 0; b < NB; b++) wrow[b] += (size_t)kb * cstep;
 #pragma unroll
   for (int mb = 0; mb < SMB; mb++) arow[mb] += (size_t)kb * 64;
-  sc::stream_mfma<FP8, SMB, NB>(wrow, cstep, arow, two_m, KC, acc);
+  sc::stream_mfma<FP8, SMB, NB>(wrow, ffn::w_lane_piece_step(p.wpacked, (int)wesz), cstep, arow, two_m, KC, acc);
 
   // ---- epilogue: acc[mb][b][r] at lane l is row mb*32 + 8*(r/4) + 4*(l/32) + r%4, column c0 + l%32
   const int col = c0 + n;

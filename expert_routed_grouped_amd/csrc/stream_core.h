@@ -5,7 +5,8 @@
 // v_mfma_f32_32x32x16_bf16: the contraction index may be permuted freely as long as both operands
 // use the same permutation, so in every 64-wide k chunk lane (n, g) reads 64 contiguous bytes of
 // row n at k offset 32g (bf16; 32 bytes for e4m3) and feeds them to four MFMAs; the two lanes of
-// a row cover one whole 128-byte line.  The activations are read with the same layout.  Two
+// a row cover one whole 128-byte line (in the packed bf16 layout the wave reads 1 KB contiguously
+// per load instead).  The activations are read with the same layout.  Two
 // chunks are in flight per wave (register double buffering).
 #pragma once
 #include "common.h"
@@ -27,13 +28,14 @@ __device__ __forceinline__ bf16x8_t as_operand(const u32x4_t *q, int s) {
   }
 }
 
-// acc[mb][b] += A_mb . W_b^T over KC consecutive 64-wide k chunks.  wrow[b]: this lane's weight
-// bytes at the first chunk (row n = lane % 32 of block b, k offset 32 (lane / 32) elements);
-// cstep: bytes from one chunk of a row to the next (row-major or packed layout).  arow[mb]: this
+// acc[mb][b] += A_mb . W_b^T over KC consecutive 64-wide k chunks.  wrow[b]: this lane's first
+// 16-byte weight piece at the first chunk (row n = lane % 32 of block b, k offset 32 (lane / 32)
+// elements); pstep: bytes from one of the lane's pieces of a chunk to the next; cstep: bytes from
+// one chunk of a row to the next (row-major or packed layout).  arow[mb]: this
 // lane's bf16 activation row of block mb at the first chunk, k offset 32 (lane / 32); chunks are
 // 64 elements apart.  two_m (wave-uniform): the second activation block is used.
 template <bool FP8, int SMB, int NB>
-__device__ __forceinline__ void stream_mfma(const char *const (&wrow)[NB], size_t cstep,
+__device__ __forceinline__ void stream_mfma(const char *const (&wrow)[NB], size_t pstep, size_t cstep,
                                             const uint16_t *const (&arow)[SMB], bool two_m, int KC,
                                             f32x16_t (&acc)[SMB][NB]) {
   constexpr int WQ = FP8 ? 2 : 4;  // 16-byte weight loads per lane per 64-wide k chunk
@@ -42,7 +44,7 @@ __device__ __forceinline__ void stream_mfma(const char *const (&wrow)[NB], size_
 #pragma unroll
     for (int b = 0; b < NB; b++)
 #pragma unroll
-      for (int q = 0; q < WQ; q++) wq[buf][b][q] = *(const u32x4_t *)(wrow[b] + (size_t)(k0 >> 6) * cstep + 16 * q);
+      for (int q = 0; q < WQ; q++) wq[buf][b][q] = *(const u32x4_t *)(wrow[b] + (size_t)(k0 >> 6) * cstep + pstep * q);
 #pragma unroll
     for (int q = 0; q < 4; q++) aq[buf][0][q] = *(const u32x4_t *)(arow[0] + k0 + 8 * q);
     if constexpr (SMB > 1) {

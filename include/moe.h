@@ -272,9 +272,15 @@ int moe_grouped_ffn_noalloc(const void *a, int a_dtype, const int32_t *offsets, 
  * w: [E, N, K] row-major, MOE_BF16 or MOE_FP8_E4M3 (w_dtype); packed: the same
  * number of bytes, written as, for every group of 32 rows (row = e*N + n over
  * all experts) and every 64-wide K chunk c, the 32 x 64 block of those rows and
- * columns [64c, 64c+64), row-major, with the blocks of a row group in order of
- * c and the row groups in order.  Element (row, k) is at
- *   ((row / 32) * 32 * K + (row % 32) * 64 + (k / 64) * 2048 + k % 64).
+ * columns [64c, 64c+64), with the blocks of a row group in order of c and the
+ * row groups in order.  fp8 blocks are row-major: element (row, k) is at byte
+ *   (row / 32) * 32 * K + (row % 32) * 64 + (k / 64) * 2048 + k % 64.
+ * bf16 blocks hold 16-byte pieces (8 values k = 8p .. 8p+7 of the chunk, p = (k % 64) / 8)
+ * ordered by p % 4, then p / 4, then block row: element (row, k) is at byte
+ *   (row / 32) * 64 * K + (k / 64) * 4096 + (p % 4) * 1024
+ *     + ((row % 32) + 32 * (p / 4)) * 16 + (k % 8) * 2,
+ * the order in which a wave that streams a block into matrix-core operands
+ * reads it, 1 KB contiguously per load.
  * Pass the packed w_gate_up ([E_loc, 2I, H]: N = 2I, K = H) and w_down
  * ([E_loc, H, I]: N = H, K = I) to moe_grouped_ffn or moe_shared_expert (E = 1)
  * with MOE_FFN_PACKED_WEIGHTS; fp8 scales stay as they are.  N a multiple of 32,

@@ -917,9 +917,13 @@ def test_full_workload_layer_mx(name, fused, packed):
 # packed weight layout: the reorder itself, and bit-identical FFN outputs
 # ----------------------------------------------------------------------------
 def np_packed(w):
-    """The packed block layout written with numpy: 32-row groups, 64-wide K chunks, row-major blocks."""
+    """The packed block layout written with numpy: 32-row groups, 64-wide K chunks; fp8 blocks
+    row-major, bf16 blocks ordered (piece q of 4 within a 32-value half g, half g, row n, 8 values)."""
     E, N, K = w.shape
-    return np.ascontiguousarray(w.reshape(E * N // 32, 32, K // 64, 64).transpose(0, 2, 1, 3)).reshape(E, N, K)
+    b = w.reshape(E * N // 32, 32, K // 64, 64).transpose(0, 2, 1, 3)  # [group, chunk, row, value]
+    if w.dtype == np.uint16:
+        b = b.reshape(b.shape[0], b.shape[1], 32, 2, 4, 8).transpose(0, 1, 4, 3, 2, 5)
+    return np.ascontiguousarray(b).reshape(E, N, K)
 
 
 @pytest.mark.parametrize("dt,shape", [("bf16", (3, 96, 192)), ("fp8", (2, 64, 320)), ("bf16", (64, 128)),
