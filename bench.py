@@ -408,7 +408,7 @@ def measure(wl: Workload, args):
         streaming = bufs.R_cap <= 48 * cfg.E_loc
         kernel = (("ffn_mx_stream_kernel" if streaming else "ffn_mx_kernel") if mx else
                   ("ffn_stream_kernel" if streaming else
-                   ("ffn_dma_kernel" if cfg.wdt == "bf16" else "ffn_big_kernel")))
+                   "ffn_dma_kernel"))
         roof["traffic"] = measured_traffic(kernel, wl.name, weights)
         # rows the grouped GEMM actually multiplies, by the tiling of the kernel in use
         padded = (A.padded_rows(counts, 64) if kernel == "ffn_stream_kernel" else

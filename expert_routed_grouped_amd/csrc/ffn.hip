@@ -16,252 +16,19 @@
 // weight tile those M tiles share is fetched from HBM about once and served
 // from that XCD's L2 afterwards.
 //
-// Three tile kernels, chosen by batch shape and weight type:
+// Two tile kernels, chosen by batch shape:
 //  - few rows per expert (decode): the weight-streaming kernel of
 //    ffn_stream.hip, bound by HBM bandwidth;
-//  - bf16 weights, many rows: the direct-to-LDS pipelined kernel of
-//    ffn_dma.hip;
-//  - fp8 e4m3 weights, many rows: the kernel below, which stages operands
-//    through registers so that the e4m3 codes are converted to bf16 (exactly)
-//    on their way into LDS; the MFMA loop is then the same as for bf16 and the
-//    per-output-channel scale is applied in the epilogue.
+//  - many rows: the direct-to-LDS pipelined kernel of ffn_dma.hip, for bf16
+//    weights and for e4m3 weights (codes copied into LDS, converted to bf16
+//    exactly after the fragment reads, the per-output-channel scale applied in
+//    the epilogue).
 // fp32 weights take plain fp32 FMA loops (no matrix cores).
 #include "ffn_common.h"
 
 namespace {
 
 using ffn::TileParams;
-
-// An LDS row holds 64 bf16 (128 bytes) as eight 16-byte chunks; chunk c of row r
-// sits in slot c ^ ((r >> 1) & 7).  With 64 four-byte banks one LDS cycle serves
-// 16 lanes x 16 bytes, and both access shapes used here stay conflict-free:
-// 16 lanes reading one chunk of 16 consecutive rows (MFMA operands), and 16
-// lanes writing the 8 chunks of 2 consecutive rows (staging).
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
-
-// ---------------------------------------------------------------------------
-// Tiles of 256 rows x 256 weight rows, 8 waves (2 along M x 4 along N); each
-// wave owns 128 rows x 64 weight rows as 4 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16.  Global loads run two K steps ahead of the MFMAs
-// through two register sets (a uniform base pointer per step plus a fixed
-// 32-bit offset per thread), LDS holds two stages of both operands (128 KB, one
-// workgroup per CU).  Rows past the expert's count are never multiplied: the
-// K loop is instantiated for 0..4 active 32-row blocks and each wave runs the
-// one that matches its rows, so a partly filled M tile costs what its rows cost.
-// ---------------------------------------------------------------------------
-namespace big {
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 512;
-constexpr int STAGE = BM * BK * 2;  // bytes of one operand stage (bf16)
-}  // namespace big
-
-template <bool FP8>
-struct BigLoads {
-  static constexpr int BQ = FP8 ? 2 : 4;  // 16-byte weight pieces per thread per K step
-  const char *abase;                      // uniform
-  const char *bbase[BQ];                  // uniform per piece (bf16) / this expert's weights (fp8)
-  uint32_t aoff[4];                       // per thread
-  uint32_t boff[FP8 ? BQ : 1];            // per thread (bf16: one offset shared by every piece)
-  uint32_t bstep;                         // weight bytes from one K step to the next (row-major or packed)
-};
-
-template <bool FP8>
-__device__ __forceinline__ void big_kloop(const BigLoads<FP8> &ld, int K, int tid, int lane, int wm, int wn, int nmb,
-                                          char (*lds)[2][big::STAGE], f32x16_t (&acc)[4][2]) {
-  constexpr int BQ = BigLoads<FP8>::BQ;
-  constexpr int BK = big::BK;
-  const int ach = tid & 7;
-  u32x4_t ra0[4], rb0[BQ], ra1[4], rb1[BQ];
-  auto gload = [&](u32x4_t(&ra)[4], u32x4_t(&rb)[BQ], int k0) __attribute__((always_inline)) {
-    const char *a = ld.abase + (size_t)k0 * 2;
-#pragma unroll
-    for (int q = 0; q < 4; q++) ra[q] = *(const u32x4_t *)(a + ld.aoff[q]);
-#pragma unroll
-    for (int q = 0; q < BQ; q++) {
-      const char *b = ld.bbase[q] + (size_t)(k0 / BK) * ld.bstep;
-      rb[q] = *(const u32x4_t *)(b + ld.boff[FP8 ? q : 0]);
-    }
-  };
-  auto lstore = [&](const u32x4_t(&ra)[4], const u32x4_t(&rb)[BQ], int st) __attribute__((always_inline)) {
-    char *A = lds[st][0], *B = lds[st][1];
-#pragma unroll
-    for (int q = 0; q < 4; q++) *(u32x4_t *)(A + lds_off((tid >> 3) + 64 * q, ach)) = ra[q];
-#pragma unroll
-    for (int q = 0; q < BQ; q++) {
-      if constexpr (FP8) {
-        const int rho = (tid >> 2) + 128 * q, ch = tid & 3;
-        const uint2 c0 = e4m3x4_to_bf16x4(rb[q].x), c1 = e4m3x4_to_bf16x4(rb[q].y);
-        const uint2 c2 = e4m3x4_to_bf16x4(rb[q].z), c3 = e4m3x4_to_bf16x4(rb[q].w);
-        const u32x4_t v0 = {c0.x, c0.y, c1.x, c1.y}, v1 = {c2.x, c2.y, c3.x, c3.y};
-        *(u32x4_t *)(B + lds_off(rho, 2 * ch)) = v0;
-        *(u32x4_t *)(B + lds_off(rho, 2 * ch + 1)) = v1;
-      } else {
-        *(u32x4_t *)(B + lds_off((tid >> 3) + 64 * q, tid & 7)) = rb[q];
-      }
-    }
-  };
-  // nmb is wave-uniform (scalar branches); operands are read unconditionally so the
-  // LDS reads of a K step can all be in flight before its MFMAs
-  auto compute = [&](int st) __attribute__((always_inline)) {
-    const char *A = lds[st][0], *B = lds[st][1];
-#pragma unroll
-    for (int kk = 0; kk < 4; kk++) {
-      const int ch = kk * 2 + (lane >> 5);
-      bf16x8_t bf[2], af[4];
-#pragma unroll
-      for (int j = 0; j < 2; j++) bf[j] = *(const bf16x8_t *)(B + lds_off(wn * 64 + j * 32 + (lane & 31), ch));
-#pragma unroll
-      for (int i = 0; i < 4; i++) af[i] = *(const bf16x8_t *)(A + lds_off(wm * 128 + i * 32 + (lane & 31), ch));
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (i < nmb) {
-#pragma unroll
-          for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-  };
-  const int KT = K / BK;
-  gload(ra0, rb0, 0);
-  if (KT > 1) gload(ra1, rb1, BK);
-  lstore(ra0, rb0, 0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; kt += 2) {
-    // even step kt: LDS stage 0; set 1 holds step kt+1; set 0 takes step kt+2
-    if (kt + 2 < KT) gload(ra0, rb0, (kt + 2) * BK);
-    compute(0);
-    if (kt + 1 < KT) lstore(ra1, rb1, 1);
-    __syncthreads();
-    if (kt + 1 >= KT) break;
-    // odd step kt+1: LDS stage 1; set 0 holds step kt+2; set 1 takes step kt+3
-    if (kt + 3 < KT) gload(ra1, rb1, (kt + 3) * BK);
-    compute(1);
-    if (kt + 2 < KT) lstore(ra0, rb0, 0);
-    __syncthreads();
-  }
-}
-
-// MODE 0: gate/up + SwiGLU -> h (bf16).  MODE 1: down + combine epilogue.
-// FP8: weights are e4m3 codes.  GATHER (mode 0): A row r is a[row_token[r]].
-// ATOMIC (mode 1): y[row_token[r]] += row_w[r] * o, else y_perm[r] = o.
-template <int MODE, bool FP8, bool GATHER, bool ATOMIC>
-__global__ __launch_bounds__(big::NTHR, 1) void ffn_big_kernel(TileParams p) {
-  constexpr int BM = big::BM, BN = big::BN;
-  __shared__ __attribute__((aligned(16))) char lds[2][2][big::STAGE];  // [stage][A/B]
-  const int K = MODE == 0 ? p.H : p.I;
-  const int Nw = MODE == 0 ? 2 * p.I : p.H;
-  const int NT = MODE == 0 ? (p.I + 127) / 128 : (p.H + BN - 1) / BN;
-  int e, nt, r0, rows;
-  if (!ffn::find_tile<BM>(p, NT, e, nt, r0, rows)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int mvalid = rows - wm * 128;  // rows of this wave's 128-row half (may be <= 0)
-  const int nmb = __builtin_amdgcn_readfirstlane(mvalid <= 0 ? 0 : min(4, (mvalid + 31) >> 5));
-
-  BigLoads<FP8> ld;
-  ld.abase = (const char *)p.a;
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const int m = (tid >> 3) + 64 * q;
-    const int r = r0 + min(m, rows - 1);
-    const uint32_t src_row = (MODE == 0 && GATHER) ? (uint32_t)p.row_token[r] : (uint32_t)r;
-    ld.aoff[q] = src_row * (uint32_t)K * 2u + (uint32_t)(tid & 7) * 16u;
-  }
-  const char *wexp = (const char *)p.w + (size_t)e * Nw * K * (FP8 ? 1 : 2);  // this expert's weights
-  if constexpr (FP8) {
-    // fp8 rows are 64 bytes = 4 pieces: piece q of thread tid is row (tid >> 2) + 128q, chunk tid & 3
-#pragma unroll
-    for (int q = 0; q < 2; q++) {
-      const int rho = (tid >> 2) + 128 * q;
-      // columns past the end (I or H a multiple of 64 but not of the tile) read a valid row; never stored
-      int wrow;
-      if constexpr (MODE == 0) wrow = ((rho >> 5) & 1) * p.I + min(nt * 128 + (rho >> 6) * 32 + (rho & 31), p.I - 1);
-      else wrow = min(nt * BN + rho, p.H - 1);
-      ld.bbase[q] = wexp;
-      ld.boff[q] = (uint32_t)ffn::w_row_off(p.wpacked, (size_t)wrow, K, 1) + (uint32_t)(tid & 3) * 16u;
-    }
-    ld.bstep = (uint32_t)ffn::w_chunk_step(p.wpacked, 1);
-  } else {
-    // piece q of thread tid is tile row (tid >> 3) + 64q, chunk tid & 7.  Gate/up: tile rows
-    // [64q, 64q+64) are the gate then up rows of intermediate columns nt*128 + 32q + [0, 32);
-    // down: weight rows nt*256 + 64q + [0, 64).  A piece group past the end re-reads group 0.
-    const int t8 = tid >> 3;
-    ld.bstep = big::BK * 2;  // row-major only (bf16 weights take the direct-to-LDS kernel)
-    if constexpr (MODE == 0) {
-      ld.boff[0] = (uint32_t)((((t8 >> 5) & 1) * p.I + (t8 & 31)) * K) * 2u + (uint32_t)(tid & 7) * 16u;
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int c = nt * 128 + 32 * q < p.I ? nt * 128 + 32 * q : nt * 128;
-        ld.bbase[q] = wexp + (size_t)c * K * 2;
-      }
-    } else {
-      ld.boff[0] = (uint32_t)(t8 * K) * 2u + (uint32_t)(tid & 7) * 16u;
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int n0 = nt * BN + 64 * q < p.H ? nt * BN + 64 * q : nt * BN;
-        ld.bbase[q] = wexp + (size_t)n0 * K * 2;
-      }
-    }
-  }
-
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 2; j++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
-  big_kloop<FP8>(ld, K, tid, lane, wm, wn, nmb, lds, acc);
-
-  // ---- epilogue.  acc[i][j][r] at lane l is row wm*128 + i*32 + 8*(r/4) + 4*(l/32) + r%4,
-  // weight row wn*64 + j*32 + l%32 of the tile.
-  if (nmb == 0) return;
-  if constexpr (MODE == 0) {
-    if (nt * 128 + wn * 32 >= p.I) return;
-    const int col = nt * 128 + wn * 32 + (lane & 31);  // intermediate index
-    float sg = 1.0f, su = 1.0f;
-    if constexpr (FP8) {
-      sg = p.scale[(size_t)e * Nw + col];
-      su = p.scale[(size_t)e * Nw + p.I + col];
-    }
-    uint16_t *hout = (uint16_t *)p.out;
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < mvalid) {
-          const float g = acc[i][0][r] * sg, u = acc[i][1][r] * su;
-          hout[(size_t)(r0 + wm * 128 + m) * p.I + col] = f32_to_bf16(silu_fast(g) * u);
-        }
-      }
-  } else {
-    float *out = (float *)p.out;
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int n = nt * BN + wn * 64 + j * 32 + (lane & 31);
-      if (n >= p.H) continue;
-      const float sc = FP8 ? p.scale[(size_t)e * Nw + n] : 1.0f;
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (m < mvalid) {
-            const int row = r0 + wm * 128 + m;
-            const float o = acc[i][j][r] * sc;
-            if constexpr (ATOMIC) atomicAdd(out + (size_t)p.row_token[row] * p.H + n, p.row_w[row] * o);
-            else out[(size_t)row * p.H + n] = o;
-          }
-        }
-    }
-  }
-}
-
-template <int MODE, bool FP8, bool GATHER, bool ATOMIC>
-hipError_t launch_big(const TileParams &tp, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((ffn_big_kernel<MODE, FP8, GATHER, ATOMIC>), dim3(grid), dim3(big::NTHR), 0, s, tp);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // fp32 path: plain fp32 FMA loops (small fp32 models; no matrix cores).
@@ -364,50 +131,15 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
   }
   // Few rows per expert on average: stream the weights (HBM bound); else tiles (matrix-core bound).
   const bool stream = a.kernel == 1 || (a.kernel == 0 && (long long)a.R_cap <= 48LL * a.El);
-  if (stream || a.w_dt == 1) {
-    TileParams base{};
-    base.offsets = a.offsets;
-    base.row_token = a.row_token;
-    base.row_w = a.row_w;
-    base.El = a.El;
-    base.H = a.H;
-    base.I = a.I;
-    base.R_cap = a.R_cap;
-    base.wpacked = a.wpacked;
-    return stream ? launch_ffn_stream(base, a, s) : launch_ffn_dma(base, a, s);
-  }
-  // worst-case M-tiles: sum_e ceil(c_e/BM) <= (R + El*(BM-1))/BM and <= El*ceil(T/BM)
-  constexpr int TBM = big::BM;
-  const long long mt1 = ((long long)a.R_cap + (long long)a.El * (TBM - 1)) / TBM;
-  const long long mt2 = (long long)a.El * ceil_div_i(a.T, TBM);
-  const long long max_mt = mt1 < mt2 ? mt1 : mt2;
-  // only fp8 weights get here (bf16 weights take the direct-to-LDS kernel above)
-  if (a.w_dt != 2) return hipErrorInvalidValue;
-  TileParams tp{};
-  tp.offsets = a.offsets;
-  tp.row_token = a.row_token;
-  tp.row_w = a.row_w;
-  tp.El = a.El;
-  tp.H = a.H;
-  tp.I = a.I;
-  tp.R_cap = a.R_cap;
-  tp.wpacked = a.wpacked;
-  if (first) {
-    tp.a = a.a;
-    tp.w = a.w_gu;
-    tp.scale = a.s_gu;
-    tp.out = a.h;
-    const int grid = (int)(max_mt * ceil_div_i(a.I, 128));
-    err = a.gather ? launch_big<0, true, true, false>(tp, grid, s) : launch_big<0, true, false, false>(tp, grid, s);
-    if (err != hipSuccess) return err;
-  }
-  if (!second) return hipSuccess;
-  tp.a = a.h;
-  tp.w = a.w_d;
-  tp.scale = a.s_d;
-  const bool atomic = a.y != nullptr;
-  tp.out = atomic ? (void *)a.y : (void *)a.y_perm;
-  const int grid = (int)(max_mt * ceil_div_i(a.H, big::BN));
-  return atomic ? launch_big<1, true, false, true>(tp, grid, s) : launch_big<1, true, false, false>(tp, grid, s);
+  TileParams base{};
+  base.offsets = a.offsets;
+  base.row_token = a.row_token;
+  base.row_w = a.row_w;
+  base.El = a.El;
+  base.H = a.H;
+  base.I = a.I;
+  base.R_cap = a.R_cap;
+  base.wpacked = a.wpacked;
+  return stream ? launch_ffn_stream(base, a, s) : launch_ffn_dma(base, a, s);
 }
 

@@ -606,7 +606,7 @@ def test_route_dispatch_empty_batch_zeroes_counts():
 # shared expert: standalone against the oracle, and added to the routed layer
 # ----------------------------------------------------------------------------
 SHARED_CASES = [
-    # T <= 128: weight-streaming kernel; larger T: tile kernels (bf16 DMA, fp8 register-staged); fp32 model
+    # T <= 128: weight-streaming kernel; larger T: the direct-to-LDS tile kernel (bf16 and fp8 weights); fp32 model
     LayerConfig("sh_decode", T=64, H=256, E=4, k=2, I=64, seed=401, w_std=0.05, I_s=384),
     LayerConfig("sh_tail", T=129, H=384, E=4, k=2, I=64, seed=402, w_std=0.05, I_s=320),
     LayerConfig("sh_prefill", T=700, H=384, E=4, k=2, I=64, seed=403, w_std=0.05, I_s=448),
@@ -961,7 +961,7 @@ PACKED_CASES = ["stream_bf16", "stream_fp8_local", "stream_hot", "ffn_bf16", "ff
 
 @pytest.mark.parametrize("name", PACKED_CASES)
 def test_ffn_packed_weights_bit_identical(name):
-    """Weight streaming (bf16, fp8), direct-to-LDS tiles (bf16) and register-staged tiles (fp8)
+    """Weight streaming (bf16, fp8) and direct-to-LDS tiles (bf16, fp8)
     read packed weights to the same bits as row-major ones; the fused combine matches the oracle."""
     if name == "tiles_fp8":
         cfg = LayerConfig("tiles_fp8", T=1000, H=320, E=len(TILE_COUNTS), k=5, I=192, wdt="fp8", seed=210,
