@@ -19,11 +19,16 @@
 // LDS: the activation operand of a K step (192 x 128 B) sits in a two-slot ring
 // and is fetched one step ahead; the weight operand (256 x 128 B) together with
 // the scale dwords of both operands sits in a three-slot ring and is fetched two
-// steps ahead (2 x 24 KB + 3 x 34 KB = 150 KB, one workgroup per CU).  Every
+// steps ahead (2 x 24 KB + 3 x 34 KB = 150 KB, one workgroup per CU).  When K is
+// a multiple of 512 the scales instead move four K steps at a time, 16 bytes per
+// lane, into a two-group ring of their own (2 x 24 KB + 3 x 32 KB + 2 x 8 KB =
+// 160 KB): a scale load touches one line per lane whatever its size, so this
+// cuts the L2 requests of the scales by four.  Every
 // wave issues the same loads every step (past the last K step they refetch it
 // into slots nobody reads again), so the loop has no branches and the wait at
-// the top of a step is a fixed count: everything but this wave's five newest
-// loads has landed.  One barrier per step.  Chunk c of LDS row r sits in slot
+// the top of a step is a fixed count: everything but this wave's newest loads
+// (the weights of the next step, with their scale dwords or a scale group) has
+// landed.  One barrier per step.  Chunk c of LDS row r sits in slot
 // c ^ ((r >> 1) & 7); wave w's 256-byte scale segment holds the A scales of
 // tile rows 32w .. 32w+31, then the B scales of weight rows 32w .. 32w+31.
 //
@@ -48,11 +53,22 @@ using ffn::TileParams;
 constexpr int BM = 192, BN = 256, BK = 128, NTHR = 512;
 constexpr int A_BYTES = BM * BK;                 // 24 KB: one activation slot
 constexpr int S_BYTES = NTHR / 64 * 256;         // 2 KB: scale dwords of 8 x 32 A rows and 8 x 32 B rows
-constexpr int BSLOT = BN * BK + S_BYTES;         // 34 KB: one weight + scales slot
 constexpr int OFF_B = 2 * A_BYTES;
-constexpr int LDS_BYTES = OFF_B + 3 * BSLOT;     // 150 KB
+constexpr int SGRP = NTHR / 64 * 64 * 16;        // 8 KB: the scales of four K steps, 16 bytes per lane
+// Two scale schemes (template argument S4):
+//   per step: each lane's row scale dword of the step rides in the weight slot (three-slot ring);
+//   S4 (K a multiple of 512, scale rows 16-byte aligned): each lane loads its row's scales of four
+//      K steps (16 bytes) every four steps into a two-group ring of its own, a quarter of the
+//      scale requests (every lane's row is a different line, so each scale load costs 64 L2
+//      requests however few bytes it moves).
+template <bool S4>
+struct Lay {
+  static constexpr int BSLOT = BN * BK + (S4 ? 0 : S_BYTES);  // one weight (+ scales) slot: 32 or 34 KB
+  static constexpr int OFF_S = OFF_B + 3 * BSLOT;               // S4: the scale groups
+  static constexpr int BYTES = OFF_S + (S4 ? 2 * SGRP : 0);     // 160 or 150 KB
+  static_assert(BYTES <= 160 * 1024, "fits the LDS of one CU");
+};
 static_assert(NTHR / 64 * 32 >= BM && NTHR / 64 * 32 >= BN, "scale segments cover every tile row");
-static_assert(LDS_BYTES <= 160 * 1024, "fits the LDS of one CU");
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -78,18 +94,27 @@ constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (
 // One K step with compile-time ring slots: P = kt % 6 (A slot P % 2, B slot P % 3).  The loads of
 // the next steps are issued past the last step too (their source step clamped to the last one, into
 // slots nobody reads again), so every step issues the same loads and the waits are fixed counts.
-template <int NMB, int P>
+template <int NMB, int P, bool S4>
 __device__ __forceinline__ void mx_step(int kt, int KT, const Src &src, int wave, const uint32_t (&abase)[4],
                                         const uint32_t (&bbase)[3][4], uint32_t sabase, const uint32_t (&sbbase)[3],
                                         int h, char *lds, f32x16_t (&acc)[NMB > 0 ? NMB : 1][2]) {
   constexpr int NA = NMB > 0 ? NMB : 1;
   constexpr int SA = P % 2, SB = P % 3, SA1 = (P + 1) % 2, SB2 = (P + 2) % 3;
+  constexpr int BS = Lay<S4>::BSLOT;
   uint32_t sa[NA], sb[2];
   if constexpr (NMB > 0) {
+    if constexpr (S4) {  // group kt / 4 in ring entry (kt / 4) % 2, dword kt % 4 of each lane's 16 bytes
+      const uint32_t so = (uint32_t)(((kt >> 2) & 1) * SGRP + (kt & 3) * 4);
 #pragma unroll
-    for (int j = 0; j < 2; j++) sb[j] = *(const uint32_t *)(lds + sbbase[SB] + j * 256) >> (8 * h);
+      for (int j = 0; j < 2; j++) sb[j] = *(const uint32_t *)(lds + sbbase[0] + so + j * 1024) >> (8 * h);
 #pragma unroll
-    for (int i = 0; i < NMB; i++) sa[i] = *(const uint32_t *)(lds + sabase + SB * BSLOT + i * 256) >> (8 * h);
+      for (int i = 0; i < NMB; i++) sa[i] = *(const uint32_t *)(lds + sabase + so + i * 1024) >> (8 * h);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; j++) sb[j] = *(const uint32_t *)(lds + sbbase[SB] + j * 256) >> (8 * h);
+#pragma unroll
+      for (int i = 0; i < NMB; i++) sa[i] = *(const uint32_t *)(lds + sabase + SB * BS + i * 256) >> (8 * h);
+    }
   }
   const uint32_t soA = (uint32_t)min(kt + 1, KT - 1) * BK, soB = (uint32_t)min(kt + 2, KT - 1) * src.bstep;
   const int ktS = min(kt + 2, KT - 1);
@@ -120,9 +145,18 @@ __device__ __forceinline__ void mx_step(int kt, int KT, const Src &src, int wave
 #pragma unroll
       for (int u = 0; u < 4; u++)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            src.rb, (lds_void *)(lds + OFF_B + SB2 * BSLOT + (wave + 8 * u) * 1024), 16, src.boff[u], soB, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(src.sptr + (size_t)ktS * 4),
-                                       (lds_void *)(lds + OFF_B + SB2 * BSLOT + BN * BK + wave * 256), 4, 0, 0);
+            src.rb, (lds_void *)(lds + OFF_B + SB2 * BS + (wave + 8 * u) * 1024), 16, src.boff[u], soB, 0, 0);
+      if constexpr (S4) {
+        if ((kt & 3) == 2) {  // the scales of steps kt+2 .. kt+5 (the last group again past the end)
+          const int g = min((kt + 2) >> 2, (KT >> 2) - 1);
+          __builtin_amdgcn_global_load_lds((const void *)(src.sptr + (size_t)g * 16),
+                                           (lds_void *)(lds + Lay<S4>::OFF_S + (((kt + 2) >> 2) & 1) * SGRP + wave * 1024),
+                                           16, 0, 0);
+        }
+      } else {
+        __builtin_amdgcn_global_load_lds((const void *)(src.sptr + (size_t)ktS * 4),
+                                         (lds_void *)(lds + OFF_B + SB2 * BS + BN * BK + wave * 256), 4, 0, 0);
+      }
     }
     if constexpr (NMB > 0) {
 #pragma unroll
@@ -137,10 +171,11 @@ __device__ __forceinline__ void mx_step(int kt, int KT, const Src &src, int wave
   half_step(std::integral_constant<int, 1>{});
 }
 
-template <int NMB>
+template <int NMB, bool S4>
 __device__ __forceinline__ void kloop(const Src &src, int K, int wave, int lane, int arow0, int wn, char *lds,
                                       f32x16_t (&acc)[NMB > 0 ? NMB : 1][2]) {
   const int KT = K / BK;
+  constexpr int BSLOT = Lay<S4>::BSLOT;
   const int h = lane >> 5, r = lane & 31;
   // LDS byte offsets of this lane's fragment chunks: row r (+ multiples of 32, which leave the
   // swizzle alone), chunks 4 kk + 2 c + h at slot chunk ^ ((r >> 1) & 7), for kk, c in {0, 1}
@@ -156,16 +191,22 @@ __device__ __forceinline__ void kloop(const Src &src, int K, int wave, int lane,
     }
 #pragma unroll
     for (int s = 0; s < 3; s++)
-      sbbase[s] = OFF_B + (uint32_t)s * BSLOT + BN * BK + (uint32_t)(wn * 2) * 256u + 128u + r * 4u;
+      sbbase[s] = S4 ? Lay<S4>::OFF_S + (uint32_t)(wn * 2) * 1024u + (32u + r) * 16u
+                     : OFF_B + (uint32_t)s * BSLOT + BN * BK + (uint32_t)(wn * 2) * 256u + 128u + r * 4u;
   }
-  // A scales of tile row arow0 + 32 i + r: segment (arow0 >> 5) + i of the slot's scale area
-  const uint32_t sabase = OFF_B + BN * BK + (uint32_t)(arow0 >> 5) * 256u + r * 4u;
-  // prologue: weights and scales of steps 0 and 1, activations of step 0
+  // A scales of tile row arow0 + 32 i + r: segment (arow0 >> 5) + i of the slot's scale area (S4: of
+  // the scale group, 16 bytes per lane)
+  const uint32_t sabase = S4 ? Lay<S4>::OFF_S + (uint32_t)(arow0 >> 5) * 1024u + r * 16u
+                             : OFF_B + BN * BK + (uint32_t)(arow0 >> 5) * 256u + r * 4u;
+  // prologue: weights and scales of steps 0 and 1 (S4: the scales of steps 0 .. 3), activations of step 0
 #pragma unroll
   for (int u = 0; u < 4; u++)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rb, (lds_void *)(lds + OFF_B + (wave + 8 * u) * 1024), 16,
                                              src.boff[u], 0, 0, 0);
-  __builtin_amdgcn_global_load_lds((const void *)src.sptr, (lds_void *)(lds + OFF_B + BN * BK + wave * 256), 4, 0, 0);
+  if constexpr (S4)
+    __builtin_amdgcn_global_load_lds((const void *)src.sptr, (lds_void *)(lds + Lay<S4>::OFF_S + wave * 1024), 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((const void *)src.sptr, (lds_void *)(lds + OFF_B + BN * BK + wave * 256), 4, 0, 0);
 #pragma unroll
   for (int u = 0; u < 3; u++)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.ra, (lds_void *)(lds + (wave + 8 * u) * 1024), 16, src.aoff[u], 0, 0,
@@ -175,16 +216,24 @@ __device__ __forceinline__ void kloop(const Src &src, int K, int wave, int lane,
   for (int u = 0; u < 4; u++)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rb, (lds_void *)(lds + OFF_B + BSLOT + (wave + 8 * u) * 1024), 16,
                                              src.boff[u], so1 * src.bstep, 0, 0);
-  __builtin_amdgcn_global_load_lds((const void *)(src.sptr + (size_t)so1 * 4),
-                                   (lds_void *)(lds + OFF_B + BSLOT + BN * BK + wave * 256), 4, 0, 0);
-  // this wave's newest five loads are the weights and scales of step kt + 1; all older ones,
-  // among them everything of step kt, have landed once at most five are in flight
+  if constexpr (!S4)
+    __builtin_amdgcn_global_load_lds((const void *)(src.sptr + (size_t)so1 * 4),
+                                     (lds_void *)(lds + OFF_B + BSLOT + BN * BK + wave * 256), 4, 0, 0);
+  // this wave's newest loads are the weights of step kt + 1 with their scale dwords (five loads),
+  // or with S4 the weights of step kt + 1 (four loads) and, at kt % 4 == 3, the scale group issued
+  // after them; all older ones, among them everything step kt reads, have landed once no more than
+  // those are in flight
   auto one = [&](auto PC, int kt) __attribute__((always_inline)) {
     constexpr int P = decltype(PC)::value;
     if (kt < KT) {
-      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      if constexpr (S4) {
+        if ((kt & 3) == 3) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      }
       barrier_no_fence();
-      mx_step<NMB, P>(kt, KT, src, wave, abase, bbase, sabase, sbbase, h, lds, acc);
+      mx_step<NMB, P, S4>(kt, KT, src, wave, abase, bbase, sabase, sbbase, h, lds, acc);
     }
   };
   for (int kt = 0; kt < KT; kt += 6) {
@@ -198,7 +247,7 @@ __device__ __forceinline__ void kloop(const Src &src, int K, int wave, int lane,
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int MODE, bool ATOMIC, int NMB>
+template <int MODE, bool ATOMIC, bool S4, int NMB>
 __device__ __forceinline__ void body(const MxParams &mp, const Src &src, int K,
                                      int nt, int rbase, int mvalid, int wave, int lane, int arow0, int wn, char *lds) {
   const TileParams &p = mp.tp;
@@ -210,7 +259,7 @@ __device__ __forceinline__ void body(const MxParams &mp, const Src &src, int K,
     for (int j = 0; j < 2; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
-  kloop<NMB>(src, K, wave, lane, arow0, wn, lds, acc);
+  kloop<NMB, S4>(src, K, wave, lane, arow0, wn, lds, acc);
   if constexpr (NMB > 0) {
     // acc[i][j][r] at lane l is tile row arow0 + i*32 + 8*(r/4) + 4*(l/32) + r%4,
     // weight row wn*64 + j*32 + l%32 of the tile
@@ -291,9 +340,9 @@ __device__ __forceinline__ void body(const MxParams &mp, const Src &src, int K,
 
 // MODE 0: gate/up + SwiGLU -> h (MXFP8).  MODE 1: down + combine epilogue.
 // GATHER (mode 0): A row r is a[row_token[r]].  ATOMIC (mode 1): fused combine.
-template <int MODE, bool GATHER, bool ATOMIC>
+template <int MODE, bool GATHER, bool ATOMIC, bool S4>
 __global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[Lay<S4>::BYTES];
   const TileParams &p = mp.tp;
   const int K = MODE == 0 ? p.H : p.I;
   const int Nw = MODE == 0 ? 2 * p.I : p.H;
@@ -351,7 +400,7 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
   }
   const int arow0 = wm * half;
   const int rbase = r0 + arow0;
-#define MX_BODY(n) body<MODE, ATOMIC, n>(mp, src, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
+#define MX_BODY(n) body<MODE, ATOMIC, S4, n>(mp, src, K, nt, rbase, mvalid, wave, lane, arow0, wn, lds)
   switch (nmb) {
     case 0: MX_BODY(0); break;
     case 1: MX_BODY(1); break;
@@ -363,7 +412,11 @@ __global__ __launch_bounds__(NTHR, 1) void ffn_mx_kernel(MxParams mp) {
 
 template <int MODE, bool GATHER, bool ATOMIC>
 hipError_t launch_m(const MxParams &mp, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((ffn_mx_kernel<MODE, GATHER, ATOMIC>), dim3(grid), dim3(NTHR), 0, s, mp);
+  // S4: K a multiple of 512 (whole four-step scale groups) and every scale row 16-byte aligned
+  const int K = MODE == 0 ? mp.tp.H : mp.tp.I;
+  const bool s4 = K % 512 == 0 && ((uintptr_t)mp.a_scales & 15) == 0 && ((uintptr_t)mp.w_scales & 15) == 0;
+  if (s4) hipLaunchKernelGGL((ffn_mx_kernel<MODE, GATHER, ATOMIC, true>), dim3(grid), dim3(NTHR), 0, s, mp);
+  else hipLaunchKernelGGL((ffn_mx_kernel<MODE, GATHER, ATOMIC, false>), dim3(grid), dim3(NTHR), 0, s, mp);
   return hipGetLastError();
 }
 
