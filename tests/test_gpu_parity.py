@@ -846,6 +846,9 @@ MX_CASES = [
     # K a multiple of 512 in both halves: scales read four K steps at a time
     LayerConfig("mx_stream_s4", T=64, H=512, E=16, k=4, I=512, wdt="mxfp8", seed=309, w_std=0.05),
     LayerConfig("mx_stream_hot", T=120, H=256, E=16, k=2, I=256, wdt="mxfp8", bias="zipf", seed=308, w_std=0.05),
+    # tile kernel with K a multiple of 512 in both halves: scales moved four K steps at a time (two
+    # groups per gate/up tile, one per down tile, whose second load is the clamped refetch)
+    LayerConfig("mx_tiles_s4", T=800, H=1024, E=6, k=3, I=512, wdt="mxfp8", seed=310, w_std=0.05),
 ]
 
 
