@@ -10,12 +10,12 @@
 //   [0, T)                    route token t; the last routing item to finish (ticket counter)
 //                             groups all assignments by expert and raises the ``routed`` flag;
 //   [T, T + El*NBg)           gate/up item (expert e, 128 intermediate columns), h into a dense
-//                             [El, T, I] buffer (row = token).  Claimed before the flag is up, it
-//                             computes every token of the batch (T <= 64: the one 64-row tile the
-//                             weight-streaming kernel pads to anyway) and never waits for the
-//                             router, whose dependent loads slow down a lot once they compete with
-//                             the weight stream; claimed after, only the expert's rows, and nothing
-//                             for an expert without rows;
+//                             [El, T, I] buffer (row = token), after the flag: only the expert's
+//                             rows, and nothing for an expert without rows.  (Starting these items
+//                             before the routing is known, over every token of the batch so that
+//                             the weights stream while the router runs, measured slower: the
+//                             router's dependent loads slow down once they compete with the weight
+//                             stream, and every wave then reads twice the activations);
 //   [.., + El*NBd)            down item (expert e, 256 output columns) over the expert's rows, whose
 //                             h rows it gathers by token, after the flag and the NBg gate/up items
 //                             of e (per-expert completion counter).
@@ -154,19 +154,17 @@ template <bool FP8>
 __device__ __noinline__ void gate_up_item(const DecParams &pin, int e, int nb, int *s) {
   const DecParams p = global_params(pin);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 31, g = lane >> 5;
-  if (threadIdx.x == 0) {  // the routing, if already known (agent-scope loads only)
-    const bool routed = ld_agent(p.ctl + kDecRouted) != 0;
+  if (threadIdx.x == 0) {  // the grouping (agent-scope loads only); a wait that gives up leaves no rows
+    const bool routed = wait_at_least(p, p.ctl + kDecRouted, 1u, 16u, false);
     const int beg = routed ? ld_agent(p.offsets + e) : 0;
-    s[0] = routed;
     s[1] = beg;
-    s[2] = routed ? ld_agent(p.offsets + e + 1) - beg : p.T;
+    s[2] = routed ? ld_agent(p.offsets + e + 1) - beg : 0;
   }
   __syncthreads();
   // wave-uniform (the same LDS words in every lane)
-  const bool routed = __builtin_amdgcn_readfirstlane(s[0]) != 0;
   const int beg = __builtin_amdgcn_readfirstlane(s[1]), rows = __builtin_amdgcn_readfirstlane(s[2]);
   const int c0 = nb * GU_COLS + wave * 32;
-  // known routing: only the expert's rows (none: skip, no weight read); otherwise every token
+  // only the expert's rows (none: skip, no weight read)
   if (rows > 0 && c0 < p.I) {  // I is a multiple of 32: a wave's columns are all valid or all past the end
     const int col = c0 + n;
     const char *wrow[2] = {weight_lane<FP8>(p, p.wgu, (size_t)e * 2 * p.I + col, p.H, g),
@@ -177,7 +175,7 @@ __device__ __noinline__ void gate_up_item(const DecParams &pin, int e, int nb, i
       su = p.sgu[(size_t)e * 2 * p.I + p.I + col];
     }
     // token of tile row m (rows past the end repeat the last one)
-    auto token = [&](int m) { return routed ? ld_agent(p.row_token + beg + min(m, rows - 1)) : min(m, rows - 1); };
+    auto token = [&](int m) { return ld_agent(p.row_token + beg + min(m, rows - 1)); };
     const uint16_t *arow[SMB];
 #pragma unroll
     for (int mb = 0; mb < SMB; mb++) arow[mb] = (const uint16_t *)p.x + (size_t)token(mb * 32 + n) * p.H + 32 * g;

@@ -427,10 +427,10 @@ size_t moe_decode_layer_workspace_size(int T, int k, int E_loc, int I);
  * with the FFN of moe_grouped_ffn (h rounded to bf16; fp32 atomic accumulation, so the order of a
  * token's additions is not fixed).  One persistent launch: routing items, then gate/up items, then
  * down items, taken from a work queue by at most as many workgroups as the device holds at once.
- * The gate/up items compute h for every token of the batch (the one 64-row tile the weight stream
- * pads to anyway) and do not wait for the routing, so the expert weights stream while the router
- * runs; h [E_loc, T, I] is left in the workspace after the control words, and its rows of the
- * routed (token, expert) pairs are bit-identical to moe_grouped_ffn's h with few rows per expert.
+ * The gate/up items wait for the grouping and compute h for the routed rows only; h [E_loc, T, I]
+ * (row = token) is left in the workspace after the control words, and its rows of the routed
+ * (token, expert) pairs are bit-identical to moe_grouped_ffn's h with few rows per expert (the
+ * other rows are not written).
  *
  * x [T,H] MOE_BF16; w_router [E,H] MOE_BF16 or MOE_F32, or MOE_F32_ROUTER_PACKED (moe_pack_router);
  * bias [E] or NULL; expert weights and scales as moe_grouped_ffn (MOE_BF16 or MOE_FP8_E4M3; flag
