@@ -1,5 +1,7 @@
-// Grouped FFN tiles for large batches with bf16 weights: operands move from
-// HBM/L2 straight into LDS (buffer_load ... lds, no register staging).
+// Grouped FFN tiles for large batches with bf16 or e4m3 (per-output-channel
+// scale) weights: operands move from HBM/L2 straight into LDS (buffer_load ...
+// lds, no register staging); e4m3 codes are converted to bf16 exactly after
+// each fragment read, and their scales multiply the fp32 sums in the epilogue.
 //
 // Tile: up to 256 rows of one expert x 256 weight rows, K step 64 (one full
 // 128-byte line per row and step).  An expert with c rows is cut into
@@ -14,7 +16,7 @@
 // Pipeline: the weight operand, whose first touch comes from HBM, is fetched
 // two K steps ahead through a three-slot ring; the activation rows, mostly L2
 // hits, one step ahead through a two-slot ring (2 x 32 KB + 3 x 32 KB = 160 KB
-// of LDS, one workgroup per CU).  The loads of the next steps are issued
+// of LDS, or 2 x 32 KB + 3 x 16 KB of e4m3 codes; one workgroup per CU).  The loads of the next steps are issued
 // between the MFMAs of the current step, and the fragments of the next 16-wide
 // K slice are read while the MFMAs of the current one run.  Per K step: wait
 // until this wave's loads of the step have landed (vmcnt; loads retire in
