@@ -274,6 +274,10 @@ FFN_CASES = [
     # several 128-row tiles per expert with ragged tails; 64-col ragged N tail in the down projection
     LayerConfig("ffn_bf16", T=700, H=320, E=4, k=2, I=192, seed=201, w_std=0.05),
     LayerConfig("ffn_fp8_local", T=700, H=320, E=6, k=3, I=192, wdt="fp8", e_begin=1, e_end=4, seed=202, w_std=0.05),
+    # e4m3 tiles with one K step in both halves (H = I = 64: the shortest pipeline, a 64-wide N tail),
+    # and one expert of 300 rows over three K steps (two unequal M tiles)
+    LayerConfig("ffn_fp8_k64", T=600, H=64, E=4, k=2, I=64, wdt="fp8", seed=211, w_std=0.05),
+    LayerConfig("ffn_fp8_single", T=300, H=192, E=1, k=1, I=128, wdt="fp8", seed=212, w_std=0.05),
     LayerConfig("ffn_skew_empty", T=500, H=256, E=32, k=4, I=128, bias="zipf", seed=203, w_std=0.05),
     LayerConfig("ffn_k_eq_E", T=130, H=128, E=4, k=4, I=64, seed=204, w_std=0.05),
     LayerConfig("ffn_single_expert", T=257, H=192, E=1, k=1, I=128, seed=205, w_std=0.05),
