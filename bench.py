@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--weights", default="packed", choices=["packed", "row-major"],
                     help="layout of the resident bf16/fp8 expert weights (packed once with moe_pack_weights "
                          "before timing)")
+    ap.add_argument("--shared-after", action="store_true",
+                    help="decode with a shared expert: run it after the routed FFN on the same stream instead of "
+                         "on a second stream beside the router")
     ap.add_argument("--one-launch", action="store_true",
                     help="decode batches: the whole layer as one launch (moe_decode_layer) instead of route + "
                          "dispatch, gate/up, down (three launches)")
@@ -203,7 +206,8 @@ class Workload:
         if args.weights == "packed":
             L.pack_weights(dev)  # one-time layout change of the resident weights, like loading them
         self.packed = bool(dev.get("packed", False))
-        bufs = self.bufs = L.LayerBuffers(cfg, use_decode_layer=args.one_launch)
+        bufs = self.bufs = L.LayerBuffers(cfg, use_decode_layer=args.one_launch,
+                                          shared_beside_router=not args.shared_after)
         self.one_launch = bufs.dec_ws is not None
         decode_router = bufs.rd_ws is not None or self.one_launch
         if decode_router and args.router == "packed":
@@ -234,11 +238,18 @@ class Workload:
 
     def route(self):
         moe, cfg, bufs, dev, p, s = self.moe, self.cfg, self.bufs, self.dev, self.bufs.perm, self.stream
+        if bufs.side is not None:  # decode with a shared expert: it zeroes y and runs beside the router
+            side_stream, side_done = bufs.side
+            side_stream.wait_stream(s)
+            self.moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], bufs.y, dev.get("ss_gate_up"),
+                                       dev.get("ss_down"), workspace=bufs.shared_ws, zero_y=True,
+                                       packed=self.packed, stream=side_stream)
+            side_done.record(side_stream)
         if bufs.rd_ws is not None:  # decode: route + dispatch (+ zeroing of y) in one launch
             moe.moe_route_dispatch(dev["x"], dev["w_router"] if self.wrp is None else self.wrp, dev["bias"], cfg.k,
                                    cfg.E, cfg.lo, cfg.hi, bufs.rd_ws, bufs.topk_ids, bufs.topk_w, p,
-                                   y_zero=bufs.y if bufs.fused else None, router_packed=self.wrp is not None,
-                                   stream=s)
+                                   y_zero=bufs.y if (bufs.fused and bufs.side is None) else None,
+                                   router_packed=self.wrp is not None, stream=s)
         else:
             moe.moe_route(dev["x"], dev["w_router"], dev["bias"], cfg.k, bufs.topk_ids, bufs.topk_w, stream=s)
             moe.moe_permute(bufs.topk_ids, bufs.topk_w, cfg.E, cfg.lo, cfg.hi, out=p, stream=s)
@@ -257,11 +268,13 @@ class Workload:
                                 dev["w_gate_up"], dev["w_down"], dev["s_gate_up"], dev["s_down"], **outs, **common)
 
     def down(self):
+        if self.bufs.side is not None:  # the shared expert on the side stream zeroed y and added to it
+            self.stream.wait_event(self.bufs.side[1])
         self.ffn_half("down")
         if not self.bufs.fused:
             self.moe.moe_combine(self.bufs.y_perm, self.bufs.perm["token_row"], self.bufs.topk_w, y=self.bufs.y,
                                  stream=self.stream)
-        if self.bufs.shared_ws is not None:
+        if self.bufs.shared_ws is not None and self.bufs.side is None:
             self.shared()
 
     def shared(self):

@@ -1,4 +1,5 @@
-"""One MoE FFN layer call = the four library calls in order, on one stream.
+"""One MoE FFN layer call = the four library calls in order, on one stream (a decode-sized
+batch with a shared expert runs the shared expert on a second stream beside the router).
 
 Host logic only: buffer allocation, choosing between the fused (atomic) combine
 and the per-row outputs + ``moe_combine`` path, and moving synthetic numpy
@@ -83,7 +84,7 @@ class LayerBuffers:
     """Device buffers of one layer shape, reused across calls."""
 
     def __init__(self, cfg, device="cuda", fused: Optional[bool] = None, use_route_dispatch: bool = True,
-                 use_decode_layer: bool = False):
+                 use_decode_layer: bool = False, shared_beside_router: bool = True):
         T, k, El, H, I = cfg.T, cfg.k, cfg.E_loc, cfg.H, cfg.I
         self.cfg = cfg
         self.R_cap = T * min(k, El)
@@ -115,6 +116,12 @@ class LayerBuffers:
         fits = 1 <= T <= 512 and T * k <= 8192 and cfg.E <= 256 and H % 8 == 0 and H <= 16384
         self.rd_ws = (moe.moe_route_dispatch_workspace(device) if (fits and use_route_dispatch and not dec)
                       else None)
+        # a decode-sized batch with a shared expert: the shared expert (which zeroes y, then adds to it)
+        # runs on a second stream while the latency-bound router leaves HBM idle; the routed down
+        # projection waits for it before its own fp32 adds into y
+        self.side = None
+        if shared_beside_router and self.rd_ws is not None and self.fused and self.shared_ws is not None:
+            self.side = (torch.cuda.Stream(device=device), torch.cuda.Event())
 
 
 def run_layer(dev: dict, bufs: LayerBuffers, stream=None) -> torch.Tensor:
@@ -134,6 +141,26 @@ def run_layer(dev: dict, bufs: LayerBuffers, stream=None) -> torch.Tensor:
         if bufs.shared_ws is not None:
             moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], bufs.y, dev.get("ss_gate_up"),
                                   dev.get("ss_down"), workspace=bufs.shared_ws, packed=packed, stream=stream)
+        return bufs.y
+    if bufs.side is not None:  # shared expert beside the router, routed halves after it
+        main = stream if stream is not None else torch.cuda.current_stream()
+        side_stream, side_done = bufs.side
+        side_stream.wait_stream(main)
+        moe.moe_shared_expert(dev["x"], dev["ws_gate_up"], dev["ws_down"], bufs.y, dev.get("ss_gate_up"),
+                              dev.get("ss_down"), workspace=bufs.shared_ws, zero_y=True, packed=packed,
+                              stream=side_stream)
+        side_done.record(side_stream)
+        moe.moe_route_dispatch(dev["x"], dev["w_router"] if wp is None else wp, dev["bias"], cfg.k, cfg.E, cfg.lo,
+                               cfg.hi, bufs.rd_ws, bufs.topk_ids, bufs.topk_w, p, y_zero=None,
+                               router_packed=wp is not None, stream=main)
+        ffn = dict(workspace=bufs.workspace, gather=True, packed=packed, stream=main)
+        moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
+                            dev["w_gate_up"], dev["w_down"], dev.get("s_gate_up"), dev.get("s_down"),
+                            y=bufs.y, zero_y=False, phase="gate_up", **ffn)
+        main.wait_event(side_done)
+        moe.moe_grouped_ffn(dev["x"], p["offsets"], p["row_token"], p["row_w"], cfg.T, bufs.R_cap,
+                            dev["w_gate_up"], dev["w_down"], dev.get("s_gate_up"), dev.get("s_down"),
+                            y=bufs.y, zero_y=False, phase="down", **ffn)
         return bufs.y
     if bufs.rd_ws is not None:  # one launch: route, dispatch and (fused combine) the zeroing of y
         moe.moe_route_dispatch(dev["x"], dev["w_router"] if wp is None else wp, dev["bias"], cfg.k, cfg.E, cfg.lo,

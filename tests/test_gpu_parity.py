@@ -428,6 +428,43 @@ def test_layer_graph_replay_matches_oracle(fused, packed):
         del junk
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["stored", "packed"])
+def test_layer_graph_replay_shared_beside_router(packed):
+    """A decode batch with a shared expert: the shared expert (which zeroes y) runs on a second stream
+    beside the router and the routed down projection waits for it.  Eager, and captured in one graph
+    (the second stream forks from and joins the capturing stream), every replay against the oracle."""
+    cfg = LayerConfig("graph_shared", T=64, H=512, E=32, k=4, I=256, seed=602, w_std=0.05, I_s=256)
+    inp = host_inputs(cfg)
+    dev = L.to_device(inp)
+    if packed:
+        L.pack_weights(dev)
+        L.pack_router(dev)
+    bufs = L.LayerBuffers(cfg, fused=True)
+    assert bufs.side is not None, "a decode batch with a shared expert runs it beside the router"
+    r = O.layer(inp)
+    r["y"] = r["y"].astype(np.float64) + O.shared_tokens(np.arange(cfg.T), inp["x"], inp["ws_gate_up"],
+                                                         inp["ws_down"], inp["ss_gate_up"], inp["ss_down"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        L.run_layer(dev, bufs, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    check_y(bufs.y.cpu().numpy(), r["y"], f"eager, shared beside the router, packed={packed}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        L.run_layer(dev, bufs, stream=s)
+    for rep in range(4):
+        bufs.y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bufs.topk_ids.cpu().numpy(), r["topk_ids"]), f"replay {rep}"
+        check_y(bufs.y.cpu().numpy(), r["y"], f"graph replay {rep}, shared beside the router, packed={packed}")
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between the replays
+        torch.cuda.synchronize()
+        del junk
+
+
 # ----------------------------------------------------------------------------
 # full workload shapes, benchmark launch configuration, every output row
 # ----------------------------------------------------------------------------
