@@ -260,39 +260,62 @@ __device__ __forceinline__ void body(const MxParams &mp, const Src &src, int K,
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
   kloop<NMB, S4>(src, K, wave, lane, arow0, wn, lds, acc);
+  // gate/up: the epilogue stages h in LDS once every wave is past its last operand read (every
+  // wave runs the same K steps, so every wave reaches this barrier)
+  if constexpr (MODE == 0) __syncthreads();
   if constexpr (NMB > 0) {
     // acc[i][j][r] at lane l is tile row arow0 + i*32 + 8*(r/4) + 4*(l/32) + r%4,
     // weight row wn*64 + j*32 + l%32 of the tile
     if constexpr (MODE == 0) {
-      // h codes and scales through buffer resources: a per-lane 32-bit offset (row rbase + 4*(l/32),
-      // column col) plus a wave-uniform offset per accumulator row, so no store needs address
-      // arithmetic in vector registers; both tensors are below 2^31 bytes.
-      const int col = nt * 128 + wn * 32 + (lane & 31);  // intermediate index; I % 128 == 0
+      // h = silu(G) U (fp32) goes through this wave's part of the LDS, transposed so that a lane owns
+      // whole rows of the wave's 32 intermediate columns, which are exactly one MX block: the lane
+      // takes the block maximum over its own 32 values, encodes them four to a dword and stores its
+      // 32 codes and the scale byte (no cross-lane reduction, no byte stores).  Staged rows are 36
+      // floats apart: 16-byte aligned, and 16 lanes reading the same 16 bytes of 16 rows hit 16
+      // distinct groups of banks.
+      constexpr int LS = 36;
+      float *st = (float *)(lds + wave * (BM / 2) * LS * 4);
+#pragma unroll
+      for (int i = 0; i < NA; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          st[m * LS + (lane & 31)] = silu_fast(acc[i][0][r]) * acc[i][1][r];
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows are staged (LDS is in order per wave)
+      const int colbase = nt * 128 + wn * 32;  // first intermediate column of the block; I % 128 == 0
       const int ib = p.I / 32;
-      const __amdgpu_buffer_rsrc_t rq =
-          __builtin_amdgcn_make_buffer_rsrc(p.out, (short)0, (int)((size_t)p.R_cap * p.I), kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(mp.out_scales, (short)0, (int)((size_t)p.R_cap * ib), kRsrcWord3);
-      const int Iu = __builtin_amdgcn_readfirstlane(p.I), ibu = __builtin_amdgcn_readfirstlane(ib);
-      const int row0 = rbase + 4 * (lane >> 5);
-      const int voff = row0 * p.I + col, soff = row0 * ib + col / 32;
-      const bool scale_lane = (lane & 31) == 0;
-      auto put = [&](auto FULL) __attribute__((always_inline)) {
+      uint8_t *hq = (uint8_t *)p.out;
 #pragma unroll
-        for (int i = 0; i < NA; i++)
+      for (int m0 = 0; m0 < NA * 32; m0 += 64) {
+        const int m = m0 + lane;
+        if (m < NA * 32 && m < mvalid) {
+          f32x4_t v[8];
 #pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int d = i * 32 + 8 * (r >> 2) + (r & 3);
-            const float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
-            const uint32_t s = mx_scale_of(halfwave_amax(hv));  // every lane joins the shuffles
-            if (decltype(FULL)::value || d + 4 * (lane >> 5) < mvalid) {
-              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e4m3_encode(ldexpf(hv, 127 - (int)s)), rq, voff, d * Iu, 0);
-              if (scale_lane) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)s, rs, soff, d * ibu, 0);
-            }
+          for (int q = 0; q < 8; q++) v[q] = *(const f32x4_t *)(st + m * LS + 4 * q);
+          float amax = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; q++)
+#pragma unroll
+            for (int c = 0; c < 4; c++) amax = fmaxf(amax, fabsf(v[q][c]));
+          const uint32_t sc = mx_scale_of(amax);
+          const int ex = 127 - (int)sc;
+          u32x4_t w[2];
+#pragma unroll
+          for (int q = 0; q < 8; q++) {
+            const float c0 = fminf(fmaxf(ldexpf(v[q][0], ex), -448.0f), 448.0f);
+            const float c1 = fminf(fmaxf(ldexpf(v[q][1], ex), -448.0f), 448.0f);
+            const float c2 = fminf(fmaxf(ldexpf(v[q][2], ex), -448.0f), 448.0f);
+            const float c3 = fminf(fmaxf(ldexpf(v[q][3], ex), -448.0f), 448.0f);
+            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+            w[q >> 2][q & 3] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, lo, true);
           }
-      };
-      if (mvalid >= NA * 32) put(std::true_type{});
-      else put(std::false_type{});
+          const size_t row = (size_t)(rbase + m);
+          *(u32x4_t *)(hq + row * p.I + colbase) = w[0];
+          *(u32x4_t *)(hq + row * p.I + colbase + 16) = w[1];
+          mp.out_scales[row * ib + colbase / 32] = (uint8_t)sc;
+        }
+      }
     } else if constexpr (ATOMIC) {
       float *out = (float *)p.out;
 #pragma unroll
