@@ -43,8 +43,10 @@
 // 512 contiguous bytes, free of bank conflicts without a swizzle.
 //
 // Rows past the expert's count are never multiplied: the K loop is
-// instantiated for 0..4 active 32-row blocks per wave.  The fp32 sums of every
-// output run over K in the same order as in a plain 16-wide-slice MFMA chain.
+// instantiated for 0..4 active 32-row blocks per wave.  With bf16 weights the
+// fp32 sums of every output run over K in the same order as in a plain
+// 16-wide-slice MFMA chain; e4m3 weights use a fixed permutation of each
+// 64-wide K step (see dma_kloop).
 #include "ffn_common.h"
 
 #include <type_traits>
