@@ -89,6 +89,7 @@ def ffn(**kw):
     (dict(y=None), -1), (dict(yp=FAKE), -1), (dict(wdt=2), -1), (dict(rt=None), -1), (dict(rw=None), -1),
     (dict(ws=None), -4), (dict(wsb=10), -4), (dict(a=FAKE_ODD), -6), (dict(ws=P(0x1010)), -6),
     (dict(T=1 << 20, R=1 << 20, H=1024), -2), (dict(flags=3 | 32), -2), (dict(ad=0, wdt=0, flags=3 | 16), -3),
+    (dict(T=32768, R=262144, H=4096, I=1536), -2),  # R_cap * H = 2^30: one row past the limit
 ])
 def test_ffn_validation(kw, code):
     assert ffn(**kw) == code
@@ -107,7 +108,7 @@ def ffn_mx(**kw):
     (dict(H=192), -2), (dict(I=64), -2), (dict(El=0), -2), (dict(R=16 * 8 + 1), -2), (dict(T=1 << 20, R=1 << 20, H=1024), -2),
     (dict(y=None), -1), (dict(yp=FAKE), -1), (dict(as_=None), -1), (dict(wds=None), -1), (dict(rt=None), -1),
     (dict(ws=None), -4), (dict(wsb=10), -4), (dict(a=FAKE_ODD), -6), (dict(as_=P(0x1002)), -6),
-    (dict(ws=P(0x1010)), -6), (dict(flags=3 | 4 | 8), -2),
+    (dict(ws=P(0x1010)), -6), (dict(flags=3 | 4 | 8), -2), (dict(T=32768, R=262144, H=4096, I=1536), -2),
 ])
 def test_ffn_mx_validation(kw, code):
     assert ffn_mx(**kw) == code

@@ -527,6 +527,50 @@ def test_full_workload_layer(name, packed, one_launch):
 
 
 # ----------------------------------------------------------------------------
+# the largest batch the grouped FFN accepts at the workload's H and I
+# ----------------------------------------------------------------------------
+# R_cap * H = 262136 * 4096 is 32768 elements short of 2^30, the grouped FFN's limit: the per-row
+# fp32 outputs end 128 KiB below 4 GiB, h takes 805 MB, so the tile kernels' 32-bit buffer offsets
+# and the combine's reads run at the top of their range.
+MAX_CFG = LayerConfig("max_rows", T=32767, H=4096, E=128, k=8, I=1536, seed=10)
+
+
+@pytest.mark.timeout(900)
+def test_layer_at_the_size_limit():
+    """The layer at the largest T the grouped FFN takes (packed weights, per-row outputs + combine,
+    as at prefill): routing and the permutation in full, y on every token that owns one of the
+    highest 256 rows of the per-row outputs, the first and last 16 tokens and 64 others."""
+    cfg = MAX_CFG
+    assert cfg.R_cap * cfg.H < (1 << 30) <= (cfg.T + 1) * cfg.k * cfg.H
+    say(f"size limit: generating T={cfg.T} (R_cap={cfg.R_cap})")
+    inp = synth.make_inputs(cfg)
+    dev = L.to_device(inp)
+    L.pack_weights(dev)
+    bufs = L.LayerBuffers(cfg)
+    assert not bufs.fused, "a batch this size writes per-row outputs and combines them"
+    say(f"size limit: run_layer R_cap={bufs.R_cap}, per-row outputs {bufs.R_cap * cfg.H * 4} bytes")
+    y = L.run_layer(dev, bufs)
+    torch.cuda.synchronize()
+    ids, w, _ = O.route(inp["x"], inp["w_router"], inp["bias"], cfg.k)
+    assert np.array_equal(bufs.topk_ids.cpu().numpy(), ids)
+    assert np.max(np.abs(bufs.topk_w.cpu().numpy() - w)) <= GATE_TOL
+    p_or = O.permute(ids, w, cfg.lo, cfg.hi)
+    check_permutation(bufs.perm, p_or, cfg.T, cfg.k, same_gates=False)
+    R = p_or["R"]
+    assert R == cfg.R_cap
+    rng = np.random.default_rng(10)
+    toks = set(p_or["row_token"][R - 256:].tolist()) | set(range(16)) | set(range(cfg.T - 16, cfg.T))
+    toks |= set(rng.choice(cfg.T, 64, replace=False).tolist())
+    toks = np.array(sorted(toks), dtype=np.int32)
+    say(f"size limit: oracle on {toks.size} tokens")
+    y_o = O.layer_tokens(toks, inp["x"], ids, w, cfg.lo, cfg.hi, inp["w_gate_up"], inp["w_down"], inp["s_gate_up"],
+                         inp["s_down"])
+    check_y(y.cpu().numpy()[toks], y_o, f"size limit, {toks.size} tokens")
+    del dev, bufs, y, inp
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
 # decode route + dispatch in one launch: bit-identical to moe_route + moe_permute
 # ----------------------------------------------------------------------------
 RD_CASES = [
