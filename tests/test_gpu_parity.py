@@ -1001,6 +1001,32 @@ def test_full_workload_layer_mx(name, fused, packed):
     check_mx_layer(cfg, inp, ids, w, y, h)
 
 
+@pytest.mark.timeout(900)
+def test_layer_mx_at_the_size_limit():
+    """The W8A8 layer at the largest T its grouped FFN takes (R_cap * H = 2^30 - 32768, per-row
+    outputs + combine, packed codes): the MX intermediate rows and y of every token that owns one of
+    the highest 256 output rows, the first and last 16 tokens and 64 others."""
+    cfg = MAX_CFG.replace(name="max_rows_mx", wdt="mxfp8", seed=11)
+    say(f"MX size limit: generating T={cfg.T} (R_cap={cfg.R_cap})")
+    inp = synth.make_inputs(cfg)
+    dev = mx_dev(inp)
+    ids, w, _ = O.route(inp["x"], inp["w_router"], inp["bias"], cfg.k)
+    ids_d, w_d = to_dev_routing(ids, w)
+    say(f"MX size limit: layer, per-row outputs {cfg.R_cap * cfg.H * 4} bytes")
+    y, p, h = mx_layer(dev, cfg, ids_d, w_d, fused=False, packed=True)
+    del dev
+    torch.cuda.empty_cache()
+    p_or = O.permute(ids, w, cfg.lo, cfg.hi)
+    check_permutation(p, p_or, cfg.T, cfg.k)
+    R = p_or["R"]
+    rng = np.random.default_rng(11)
+    toks = set(p_or["row_token"][R - 256:].tolist()) | set(range(16)) | set(range(cfg.T - 16, cfg.T))
+    toks |= set(rng.choice(cfg.T, 64, replace=False).tolist())
+    toks = np.array(sorted(toks), dtype=np.int32)
+    say(f"MX size limit: oracle on {toks.size} tokens")
+    check_mx_layer(cfg, inp, ids, w, y, h, tokens=toks)
+
+
 # ----------------------------------------------------------------------------
 # packed weight layout: the reorder itself, and bit-identical FFN outputs
 # ----------------------------------------------------------------------------
