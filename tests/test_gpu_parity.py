@@ -292,6 +292,9 @@ FFN_CASES = [
     LayerConfig("stream_hot", T=120, H=256, E=16, k=2, I=128, bias="zipf", seed=209, w_std=0.05),
     # many experts: 1000 routed, 600 of them local (mostly empty experts, a few rows each)
     LayerConfig("many_experts", T=300, H=128, E=1000, k=8, I=64, e_begin=200, e_end=800, seed=210, w_std=0.05),
+    # one token; two tokens whose only local assignment is expert 2 (the other slots dropped)
+    LayerConfig("ffn_t1", T=1, H=128, E=8, k=3, I=64, seed=213, w_std=0.05),
+    LayerConfig("ffn_t2_local", T=2, H=128, E=8, k=2, I=64, e_begin=2, e_end=3, seed=214, w_std=0.05),
 ]
 
 
